@@ -1,0 +1,173 @@
+"""Seeded synthetic workloads for one Tiled Data Parallelism (TDP) upscale step.
+
+This module is shared by the CPU oracle, the tests, the smoke check and the
+benchmark.  It holds no arithmetic of the method itself: it only names the five
+workloads and draws their random inputs.  Nothing here tiles, normalizes, keeps,
+attends or blends.
+
+The workloads stand in for the shapes that the TDP design page ("Tiled Data
+Parallelism (TDP)", sections "What it is" and "Usage") describes: a patchified
+(frames, height, width) latent, counts of tiles per dimension with an overlap in
+latent units, conditioning tokens with [start, end) intervals of which some sit
+at negative time, and an untiled audio stream.  The pages measure no public
+dataset; these synthetic arrays replace real latents and trained weights.
+
+Draw order per workload (``numpy.random.default_rng(seed)``):
+  1. ``x_global [B][N+M][C]``  ~ N(0, 1)
+  2. ``cond_pos [M][3][2]``    (see ``draw_cond_pos``)
+  3. ``wq, wk, wv [C][hidden]`` ~ N(0, 1/sqrt(C))
+  4. ``wo [hidden][C]``         ~ N(0, 1/sqrt(hidden))
+  5. ``x_aud [B][A][C]``        ~ N(0, 1)
+Arrays of a bf16 workload are rounded once to bf16 values (round to nearest,
+ties to even) and kept as float32 arrays holding those values.  The weights
+are always rounded to bf16: the attention consumes bf16 weights.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "workload", "Inputs", "make_inputs",
+           "round_to_bf16", "draw_cond_pos"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic TDP step: geometry, tiling, denoiser shape and dtype."""
+    name: str
+    grid: tuple            # (F, H, W) patchified latent grid
+    tiling: tuple          # ((n_f, o_f), (n_h, o_h), (n_w, o_w)) tile counts and overlaps
+    batch: int
+    channels: int          # C, channels per latent token
+    heads: int
+    head_dim: int
+    n_cond: int            # M conditioning tokens appended after the N generated ones
+    n_cond_neg: int        # how many of them (the last ones) sit at negative time
+    n_audio: int           # A untiled audio tokens attended on every tile forward
+    latent_dtype: str      # "f32" or "bf16"
+    identity: bool         # identity denoiser (blend stress) instead of attention
+    seed: int
+
+    @property
+    def n_gen(self) -> int:
+        f, h, w = self.grid
+        return f * h * w
+
+    @property
+    def hidden(self) -> int:
+        return self.heads * self.head_dim
+
+    @property
+    def n_tiles(self) -> int:
+        n = 1
+        for c, _ in self.tiling:
+            n *= c
+        return n
+
+
+# The five workloads.  Sizes follow the TDP page's examples: 16 tiles (as in the
+# "16 tiles on 4 GPUs" example), 2D H x W grids with an overlap in latent units,
+# negative-time reference tokens, and an untiled audio stream.
+WORKLOADS = {
+    "tiny_2x16x16": Workload(
+        "tiny_2x16x16", grid=(2, 16, 16), tiling=((1, 0), (2, 4), (2, 4)), batch=1,
+        channels=128, heads=2, head_dim=64, n_cond=8, n_cond_neg=2, n_audio=0,
+        latent_dtype="f32", identity=False, seed=0),
+    "d64_8x32x32": Workload(
+        "d64_8x32x32", grid=(8, 32, 32), tiling=((1, 0), (2, 8), (2, 8)), batch=1,
+        channels=128, heads=32, head_dim=64, n_cond=16, n_cond_neg=4, n_audio=0,
+        latent_dtype="bf16", identity=False, seed=1),
+    "t16_16x64x64": Workload(
+        "t16_16x64x64", grid=(16, 64, 64), tiling=((1, 0), (4, 8), (4, 8)), batch=1,
+        channels=128, heads=32, head_dim=128, n_cond=0, n_cond_neg=0, n_audio=0,
+        latent_dtype="bf16", identity=False, seed=2),
+    "audio_32x48x80": Workload(
+        "audio_32x48x80", grid=(32, 48, 80), tiling=((2, 4), (3, 8), (4, 8)), batch=2,
+        channels=128, heads=16, head_dim=128, n_cond=64, n_cond_neg=16, n_audio=256,
+        latent_dtype="bf16", identity=False, seed=3),
+    "blend_32x96x160": Workload(
+        "blend_32x96x160", grid=(32, 96, 160), tiling=((1, 0), (6, 16), (10, 16)), batch=1,
+        channels=128, heads=0, head_dim=0, n_cond=0, n_cond_neg=0, n_audio=0,
+        latent_dtype="f32", identity=True, seed=4),
+}
+
+
+def workload(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def round_to_bf16(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest bf16 value (ties to even).
+
+    Returns float32 values that are exactly representable in bf16.  NaN/Inf do
+    not occur in these synthetic inputs.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    u = (u + 0x7FFF + lsb) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def draw_cond_pos(rng: np.random.Generator, grid, n_cond: int, n_neg: int) -> np.ndarray:
+    """Conditioning token intervals ``[M][3][2]`` (start, end) in latent units.
+
+    Non-negative tokens: per dim, start ~ U{0..L-1}, width ~ U{1..4} (time:
+    U{1..2}), end = min(start + width, L).  The last ``n_neg`` tokens are
+    negative-time reference tokens: time start ~ U{-4..-1}, end = start + 1,
+    spatial dims drawn as above.
+    """
+    pos = np.zeros((n_cond, 3, 2), dtype=np.float32)
+    for j in range(n_cond):
+        for d in range(3):
+            L = grid[d]
+            s = int(rng.integers(0, L))
+            wmax = 2 if d == 0 else 4
+            width = int(rng.integers(1, wmax + 1))
+            e = min(s + width, L)
+            pos[j, d] = (s, e)
+        if j >= n_cond - n_neg:
+            s = int(rng.integers(-4, 0))
+            pos[j, 0] = (s, s + 1)
+    return pos
+
+
+@dataclasses.dataclass
+class Inputs:
+    workload: Workload
+    x_global: np.ndarray              # [B][N+M][C] float32 (bf16 values for bf16 workloads)
+    cond_pos: np.ndarray              # [M][3][2] float32
+    wq: Optional[np.ndarray]          # [C][hidden] float32 holding bf16 values
+    wk: Optional[np.ndarray]
+    wv: Optional[np.ndarray]
+    wo: Optional[np.ndarray]          # [hidden][C]
+    x_aud: Optional[np.ndarray]       # [B][A][C] or None
+
+
+def make_inputs(wl: Workload | str, seed: Optional[int] = None) -> Inputs:
+    """Draw the seeded inputs of a workload (seed defaults to the workload's)."""
+    if isinstance(wl, str):
+        wl = WORKLOADS[wl]
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    B, C = wl.batch, wl.channels
+    n_rows = wl.n_gen + wl.n_cond
+    x = rng.standard_normal((B, n_rows, C), dtype=np.float32)
+    if wl.latent_dtype == "bf16":
+        x = round_to_bf16(x)
+    cond = draw_cond_pos(rng, wl.grid, wl.n_cond, wl.n_cond_neg)
+    wq = wk = wv = wo = xa = None
+    if not wl.identity:
+        hid = wl.hidden
+        s_in = np.float32(1.0 / np.sqrt(C))
+        s_out = np.float32(1.0 / np.sqrt(hid))
+        wq = round_to_bf16(rng.standard_normal((C, hid), dtype=np.float32) * s_in)
+        wk = round_to_bf16(rng.standard_normal((C, hid), dtype=np.float32) * s_in)
+        wv = round_to_bf16(rng.standard_normal((C, hid), dtype=np.float32) * s_in)
+        wo = round_to_bf16(rng.standard_normal((hid, C), dtype=np.float32) * s_out)
+        if wl.n_audio > 0:
+            xa = rng.standard_normal((B, wl.n_audio, C), dtype=np.float32)
+            if wl.latent_dtype == "bf16":
+                xa = round_to_bf16(xa)
+    return Inputs(wl, x, cond, wq, wk, wv, wo, xa)

@@ -1,0 +1,146 @@
+"""Planted mistakes in the oracle must make a pin fail (CPU only).
+
+Each test patches one plausible error into the oracle (a wrong ramp, a
+non-strict overlap test, offsets taken over the wrong rows, a RoPE sign, a
+wrong softmax scale, a dropped 1/k weight, a swapped projection) and runs the
+pin that should catch it, expecting that pin to fail.  The oracle's own code is
+untouched outside each test.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.blend as oblend
+import oracle.denoise as oden
+import oracle.tile_plan as oplan
+import tests.test_oracle_attention as tatt
+import tests.test_oracle_blend as tblend
+import tests.test_oracle_plan as tplan
+
+
+def _wrong_ramp(L, n, o, i):
+    w = _ORIG_DIM_WEIGHTS(L, n, o, i)
+    if n > 1 and o > 0:
+        w = w.copy()
+        a, _ = oplan.dim_boxes(L, n, o)[i]
+        if i > 0:      # ramp up with (k+1)/(2o) instead of (2k+1)/(2o)
+            s = oplan._cores(L, n)[i] - o // 2
+            for k in range(o):
+                w[s + k - a] = np.float32(k + 1) / np.float32(2 * o)
+    return w
+
+
+_ORIG_DIM_WEIGHTS = oplan.dim_weights
+
+
+def test_wrong_ramp_is_caught(monkeypatch):
+    monkeypatch.setattr(oplan, "dim_weights", _wrong_ramp)
+    with pytest.raises(AssertionError):
+        tplan.test_masks_sum_to_one_exactly("tiny_2x16x16")
+
+
+def test_non_strict_overlap_is_caught(monkeypatch):
+    def keeps(cond_pos, j, ext_s, ext_e):
+        s, e = cond_pos[j, :, 0], cond_pos[j, :, 1]
+        return bool(s[0] < 0 or all(s[d] <= ext_e[d] and e[d] >= ext_s[d] for d in range(3)))
+    monkeypatch.setattr(oplan, "_keeps", keeps)
+    with pytest.raises(AssertionError):
+        for name in ["tiny_2x16x16", "d64_8x32x32", "audio_32x48x80"]:
+            tplan.test_keep_rule_brute_force(name)
+
+
+def test_missing_negative_time_rule_is_caught(monkeypatch):
+    def keeps(cond_pos, j, ext_s, ext_e):
+        s, e = cond_pos[j, :, 0], cond_pos[j, :, 1]
+        return bool(all(s[d] < ext_e[d] and e[d] > ext_s[d] for d in range(3)))
+    monkeypatch.setattr(oplan, "_keeps", keeps)
+    with pytest.raises(AssertionError):
+        tplan.test_keep_rule_brute_force("tiny_2x16x16")
+
+
+def test_offset_over_all_rows_is_caught(monkeypatch):
+    orig = oplan.plan
+
+    def plan(grid, tiling, cond_pos=None, normalize_positions=True, world_size=1, rank=0):
+        p = orig(grid, tiling, cond_pos, normalize_positions, world_size, rank)
+        if normalize_positions:   # re-base every tile on the min start over ALL its rows
+            for t in range(p.tile_id.size):
+                r0, r1 = p.tile_row_begin[t], p.tile_row_begin[t + 1]
+                raw = p.row_pos[r0:r1] + p.tile_offset[t][None, :, None]
+                off = raw[:, :, 0].min(axis=0)
+                p.row_pos[r0:r1] = raw - off[None, :, None]
+                p.tile_offset[t] = off
+        return p
+    monkeypatch.setattr(oplan, "plan", plan)
+    monkeypatch.setattr(oracle, "plan", plan)
+    with pytest.raises(AssertionError):
+        tplan.test_normalization_invariants("audio_32x48x80")
+
+
+def test_rope_sign_error_is_caught(monkeypatch):
+    def bad_rope(x, angles):
+        x = np.asarray(x, dtype=np.float64)
+        c, s = np.cos(angles), np.sin(angles)
+        out = np.empty_like(x)
+        out[:, 0::2] = x[:, 0::2] * c + x[:, 1::2] * s      # sign flipped here only
+        out[:, 1::2] = x[:, 0::2] * s + x[:, 1::2] * c
+        return out
+    monkeypatch.setattr(oden, "apply_rope", bad_rope)
+    monkeypatch.setattr(oracle, "apply_rope", bad_rope)
+    with pytest.raises(AssertionError):
+        tatt.test_rope_matches_complex_rotation_and_keeps_norms(64)
+    with pytest.raises(AssertionError):
+        tatt.test_attention_brute_force(False, 12)
+
+
+def test_rope_axis_mixup_is_caught(monkeypatch):
+    orig = oden.rope_angles
+
+    def bad_angles(pos, head_dim, base=10000.0):
+        pos = np.asarray(pos)[:, [1, 0, 2], :]              # time and height swapped
+        return orig(pos, head_dim, base)
+    monkeypatch.setattr(oden, "rope_angles", bad_angles)
+    with pytest.raises(AssertionError):
+        tatt.test_attention_brute_force(False, 12)
+
+
+def test_softmax_scale_error_is_caught(monkeypatch):
+    orig = oden._softmax_rows
+    monkeypatch.setattr(oden, "_softmax_rows", lambda z: orig(z * np.sqrt(2.0)))
+    with pytest.raises(AssertionError):
+        tatt.test_equal_positions_reduce_to_textbook_attention()
+
+
+def test_swapped_projection_is_caught(monkeypatch):
+    orig = oden.tile_forward
+
+    def bad(x, pos, xa, wq, wk, wv, wo, *a, **k):
+        return orig(x, pos, xa, wq, wv, wk, wo, *a, **k)     # K and V weights swapped
+    monkeypatch.setattr(oracle, "tile_forward", bad)
+    with pytest.raises(AssertionError):
+        tatt.test_attention_brute_force(True, 6)
+
+
+def test_dropped_inverse_k_weight_is_caught(monkeypatch):
+    orig = oplan.plan
+
+    def plan(*a, **k):
+        p = orig(*a, **k)
+        n_gen = p.grid[0] * p.grid[1] * p.grid[2]
+        p.row_weight[p.row_src >= n_gen] = 1.0
+        return p
+    monkeypatch.setattr(oracle, "plan", plan)
+    with pytest.raises(AssertionError):
+        tblend.test_identity_reconstructs_latent("d64_8x32x32")
+
+
+def test_blend_row_mixup_is_caught(monkeypatch):
+    orig = oblend.blend_tiles
+
+    def bad(y_tiles, p, n_dst=None, y_global=None):
+        y = np.array(y_tiles, copy=True)
+        y[:, :-1] = y[:, 1:]                                  # off-by-one row
+        return orig(y, p, n_dst, y_global)
+    monkeypatch.setattr(oracle, "blend_tiles", bad)
+    with pytest.raises(AssertionError):
+        tblend.test_identity_reconstructs_latent("tiny_2x16x16")
