@@ -1,0 +1,274 @@
+/*
+ * tdp.h - C ABI of libtdp.so: one Tiled Data Parallelism (TDP) upscale step on
+ * one MI355X (gfx950), the GPU holding every tile.
+ *
+ * The method is the one on the "Tiled Data Parallelism (TDP)" design page:
+ * split the patchified (frames, height, width) latent into overlapping tiles
+ * ("What it is"), shift each tile's positions so its generated tokens start at
+ * zero ("Position normalization"), keep the conditioning tokens that overlap a
+ * tile plus every negative-time reference token ("Shared negative (reference)
+ * positions"), run the denoiser on every tile, and sum the mask-weighted tile
+ * outputs into the global latent.  On one GPU that sum replaces the page's
+ * single all_reduce.
+ *
+ * Conventions for every call:
+ *  - Every call returns a tdp_status; nothing throws, nothing aborts.
+ *  - The library never allocates memory.  Host arrays, device buffers, the
+ *    workspace and the stream are the caller's.
+ *  - Pointers marked "host" are read or written before the call returns.
+ *    Pointers marked "device" are HBM addresses (hipMalloc'd, e.g. the
+ *    data_ptr() of a torch tensor on cuda:0) and must be 16-byte aligned.
+ *  - Device work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ *    default stream) and runs asynchronously.  Arguments are validated on the
+ *    host before anything is launched: an invalid call launches nothing.  A
+ *    launch failure returns TDP_ERR_HIP; faults show at the caller's sync.
+ *  - Calls hold no global state and may be made from several threads; calls
+ *    whose device buffers overlap must be ordered by the caller (one stream).
+ *  - Layouts are row-major, innermost index last.  "bf16" is IEEE binary32
+ *    truncated to its upper 16 bits in storage (round to nearest even when
+ *    the library produces it).
+ */
+#ifndef TDP_H
+#define TDP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TDP_OK = 0,
+  TDP_ERR_NULL = -1,        /* a required pointer is NULL                          */
+  TDP_ERR_ARG = -2,         /* a count, size or tiling is out of range             */
+  TDP_ERR_SHAPE = -3,       /* sizes disagree with each other (e.g. plan vs desc)  */
+  TDP_ERR_UNSUPPORTED = -4, /* a valid but unsupported shape or dtype              */
+  TDP_ERR_BUFFER = -5,      /* a caller buffer or the workspace is too small       */
+  TDP_ERR_HIP = -6,         /* a HIP launch or runtime call failed                 */
+  TDP_ERR_ALIGN = -7        /* a device pointer is not 16-byte aligned             */
+} tdp_status;
+
+typedef enum { TDP_F32 = 0, TDP_BF16 = 1 } tdp_dtype;
+
+/* Static string naming a status (never NULL). */
+const char *tdp_status_string(int32_t status);
+
+/* ------------------------------------------------------------------------ */
+/* Plan (host only)                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* One dimension's tiling: a tile COUNT and an overlap in latent grid units
+ * ("API / Tiling config": counts, not sizes).  Boxes: the dimension [0, L) is
+ * split into num_tiles cores [c_i, c_{i+1}), c_i = floor(i L / num_tiles); core
+ * i is widened by floor(overlap/2) on the left and ceil(overlap/2) on the
+ * right, clipped to [0, L), so neighbours overlap by exactly `overlap`.
+ * Requires 1 <= num_tiles <= L and, for num_tiles > 1,
+ * 0 <= overlap <= smallest core length; num_tiles == 1 ignores overlap. */
+typedef struct {
+  int32_t num_tiles;
+  int32_t overlap;
+} tdp_dim_tiling;
+
+typedef struct {
+  int32_t grid[3];            /* (F, H, W) patchified latent grid, each >= 1        */
+  tdp_dim_tiling tiling[3];   /* frames, height, width                              */
+  int32_t n_cond;             /* M >= 0 conditioning tokens, appended after the
+                                 N = F*H*W generated tokens                         */
+  const float *cond_pos;      /* host [M][3][2]: (start, end) per dim (t, h, w), in
+                                 latent units; NULL iff M == 0; finite values       */
+  int32_t normalize_positions;/* 1 (default) or 0 ("Position normalization")        */
+  int32_t world_size, rank;   /* round-robin share: tile t belongs to rank
+                                 t mod world_size ("What it is"); (1, 0) = all     */
+} tdp_plan_desc;
+
+typedef struct {
+  int32_t n_tiles_total;      /* T = product of the tile counts                    */
+  int32_t n_tiles_local;      /* tiles of this rank                                */
+  int32_t max_tile_rows;      /* largest local tile (generated + kept cond rows)   */
+  int32_t n_gen_total;        /* N                                                 */
+  int64_t n_rows;             /* sum of local tile rows                            */
+  int64_t n_dst_rows;         /* N + M                                             */
+} tdp_plan_sizes;
+
+/* Caller-owned host arrays, sized from tdp_plan_sizes.  Tile order: global
+ * tile index t = (i_f * n_h + i_h) * n_w + i_w, local tiles ascending.  A
+ * tile's rows are its generated tokens, row-major over its box (w fastest),
+ * then its kept conditioning tokens in ascending j. */
+typedef struct {
+  int32_t *tile_id;           /* [n_tiles_local] global tile index                 */
+  int32_t *tile_box;          /* [n_tiles_local][3][2] box [a, b) per dim          */
+  float *tile_offset;         /* [n_tiles_local][3] subtracted positions (0 if off)*/
+  int64_t *tile_row_begin;    /* [n_tiles_local + 1] CSR of rows over tiles        */
+  int32_t *tile_n_gen;        /* [n_tiles_local] generated rows of each tile       */
+  int32_t *row_src;           /* [n_rows] global token: (f*H + h)*W + w, or N + j  */
+  float *row_weight;          /* [n_rows] trapezoid mask product, or 1/k_j         */
+  float *row_pos;             /* [n_rows][3][2] normalized (start, end)            */
+  int32_t *cond_keep_count;   /* [M] k_j = tiles (of all ranks) keeping token j    */
+  int64_t *dst_row_begin;     /* [n_dst_rows + 1] inverse CSR over global tokens   */
+  int32_t *dst_rows;          /* [n_rows] rows feeding each token, ascending       */
+} tdp_plan_out;
+
+/* Sizes of a rank's plan.  Errors: TDP_ERR_NULL, TDP_ERR_ARG (bad grid,
+ * tiling, M < 0, world_size < 1, rank outside [0, world_size)). */
+tdp_status tdp_plan_query(const tdp_plan_desc *desc, tdp_plan_sizes *sizes);
+
+/* Fill a rank's plan.
+ *  Masks ("What it is": trapezoidal masks summing to one): along a dimension,
+ *  at the k-th position (k = 0..o-1) of the overlap between tiles i-1 and i,
+ *  tile i weighs (2k+1)/(2o) and tile i-1 weighs (2o-2k-1)/(2o), each a
+ *  float32 quotient; 1 elsewhere, grid edges included.  A generated row's
+ *  weight is the float32 product (w_f * w_h) * w_w.
+ *  Positions ("Position normalization"): generated token (f, h, w) has the
+ *  intervals [f, f+1), [h, h+1), [w, w+1).  A tile's offset per dim is the
+ *  smallest start of its generated tokens (0 when normalize_positions == 0)
+ *  and is subtracted from both ends of all its rows.
+ *  Keep rule ("Shared negative (reference) positions"): token j is kept by a
+ *  tile when its time start is < 0, or when in all three dims
+ *  start < tile_end and end > tile_start (the tile's generated extent, in
+ *  global units).  Its weight is 1.0f / k_j; a token no tile keeps gets no
+ *  row.  `sizes` must be the values tdp_plan_query returned for `desc`
+ *  (TDP_ERR_SHAPE otherwise).  All out arrays are required (TDP_ERR_NULL). */
+tdp_status tdp_plan(const tdp_plan_desc *desc, const tdp_plan_sizes *sizes,
+                    tdp_plan_out *out);
+
+/* ------------------------------------------------------------------------ */
+/* Gather (device)                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* x_tiles[b][r][:] = x_global[b][row_src[r]][:] ("What it is": each tile is a
+ * piece of the latent; kept conditioning rows follow the generated ones).
+ *  x_global: device [batch][n_src_rows][C], dtype `dtype`.
+ *  row_src:  device [n_rows] int32, each in [0, n_src_rows) (rows outside are
+ *            written as zeros, never read out of bounds).
+ *  x_tiles:  device [batch][n_rows][C], same dtype.
+ * C must be a positive multiple of 8.  n_rows == 0 is a no-op. */
+tdp_status tdp_gather_tiles(const void *x_global, int32_t dtype, int32_t batch,
+                            int64_t n_src_rows, int32_t C, const int32_t *row_src,
+                            int64_t n_rows, void *x_tiles, void *hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Per-tile attention (device)                                               */
+/* ------------------------------------------------------------------------ */
+
+/* The denoiser run on every tile ("What it is": every rank runs the full
+ * transformer on its tiles; "When to use it": attention is quadratic in a
+ * tile's token count).  It is one multi-head self-attention layer, no bias,
+ * no norm, no residual:  per tile t and batch b, with S = [tile rows ; audio
+ * rows] (audio untiled, attended on every tile forward),
+ *   Q = S Wq, K = S Wk, V = S Wv          (bf16 operands, fp32 accumulation)
+ *   3D RoPE on the Q and K of tile rows at their normalized positions
+ *     ("Position normalization"): head_dim/2 interleaved pairs (2i, 2i+1),
+ *     p = head_dim/6 pairs per axis: pairs [0,p) time, [p,2p) height,
+ *     [2p,3p) width, the rest unrotated; pair j of an axis turns by
+ *     m * rope_base^(-j/p), m = (start + end)/2 of the row's interval.
+ *     Audio rows are not rotated.
+ *   O_h = softmax(Q_h K_h^T / sqrt(head_dim)) V_h, bidirectional, no mask
+ *   Y = [O_1 .. O_heads] Wo
+ * Tile rows of Y go to y_tiles, audio rows to y_audio_tiles[t]. */
+typedef struct {
+  int32_t batch;              /* B >= 1                                           */
+  int32_t C;                  /* channels; must be 128                            */
+  int32_t heads;              /* >= 1                                             */
+  int32_t head_dim;           /* 64 or 128                                        */
+  int32_t n_audio;            /* A >= 0 audio tokens                              */
+  int32_t x_dtype;            /* dtype of x_tiles and x_audio (TDP_F32/TDP_BF16)  */
+  int32_t y_dtype;            /* dtype of y_tiles                                 */
+  float rope_base;            /* > 0; 10000 in the workloads                      */
+} tdp_attn_desc;
+
+/* Workspace bytes tdp_tile_attention needs for these sizes.  Errors as
+ * tdp_tile_attention's shape checks. */
+tdp_status tdp_tile_attention_workspace(const tdp_attn_desc *desc, int32_t n_tiles,
+                                        int64_t n_rows, size_t *bytes);
+
+/*  tile_row_begin: device [n_tiles + 1] int64 CSR (from tdp_plan): non-
+ *                  decreasing, [0] = 0, [n_tiles] = n_rows, every tile at most
+ *                  max_tile_rows rows.  (A violation gives wrong results but
+ *                  every access stays inside the caller's buffers and the
+ *                  workspace.)
+ *  x_tiles:   device [B][n_rows][C] (x_dtype), e.g. from tdp_gather_tiles.
+ *  row_pos:   device [n_rows][3][2] float32 normalized positions (tdp_plan).
+ *  wq, wk, wv: device [C][heads*head_dim] bf16;  wo: device [heads*head_dim][C]
+ *             bf16 (row-major [in][out]).
+ *  x_audio:   device [B][A][C] (x_dtype), NULL iff A == 0.
+ *  y_tiles:   device [B][n_rows][C] (y_dtype), overwritten.
+ *  y_audio_tiles: device [n_tiles][B][A][C] float32, NULL iff A == 0.
+ *  workspace: device, >= tdp_tile_attention_workspace bytes; scratch, its
+ *             contents are overwritten. */
+tdp_status tdp_tile_attention(const tdp_attn_desc *desc, int32_t n_tiles,
+                              const int64_t *tile_row_begin, int32_t max_tile_rows,
+                              int64_t n_rows, const void *x_tiles, const float *row_pos,
+                              const void *wq, const void *wk, const void *wv,
+                              const void *wo, const void *x_audio, void *y_tiles,
+                              float *y_audio_tiles, void *workspace,
+                              size_t workspace_bytes, void *hip_stream);
+
+/* The same step split into its three stages, for callers that time or
+ * schedule them separately.  tdp_tile_attention == prepare; qkv_rope;
+ * core; out_proj, on one stream with the same arguments and workspace.
+ *  prepare:  transposed weights and the tile -> 128-row block table.
+ *  qkv_rope: the Q/K/V projection with RoPE, into the workspace.
+ *  core:     softmax(QK^T/sqrt(d))V per tile, head and batch, into the
+ *            workspace (bf16 O).
+ *  out_proj: Y = O Wo into y_tiles and y_audio_tiles. */
+tdp_status tdp_attn_prepare(const tdp_attn_desc *desc, int32_t n_tiles,
+                            const int64_t *tile_row_begin, int32_t max_tile_rows,
+                            int64_t n_rows, const void *wq, const void *wk,
+                            const void *wv, const void *wo, void *workspace,
+                            size_t workspace_bytes, void *hip_stream);
+tdp_status tdp_attn_qkv_rope(const tdp_attn_desc *desc, int32_t n_tiles,
+                             const int64_t *tile_row_begin, int32_t max_tile_rows,
+                             int64_t n_rows, const void *x_tiles, const float *row_pos,
+                             const void *x_audio, void *workspace,
+                             size_t workspace_bytes, void *hip_stream);
+tdp_status tdp_attn_core(const tdp_attn_desc *desc, int32_t n_tiles,
+                         const int64_t *tile_row_begin, int32_t max_tile_rows,
+                         int64_t n_rows, void *workspace, size_t workspace_bytes,
+                         void *hip_stream);
+tdp_status tdp_attn_out_proj(const tdp_attn_desc *desc, int32_t n_tiles,
+                             const int64_t *tile_row_begin, int32_t max_tile_rows,
+                             int64_t n_rows, void *y_tiles, float *y_audio_tiles,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Blend (device) - the on-device stand-in for the multi-GPU all_reduce      */
+/* ------------------------------------------------------------------------ */
+
+/* y_global[b][n][:] (+)= sum over k in [dst_row_begin[n], dst_row_begin[n+1])
+ *                         of row_weight[r] * y_tiles[b][r][:],  r = dst_rows[k]
+ * ("What it is": masked tiles summed into the result; "Shared negative
+ * (reference) positions": conditioning rows weigh 1/k).  Rows are summed in
+ * the order dst_rows lists them (ascending tile), in float32.  One thread
+ * writes each output element: deterministic, no atomics.
+ *  y_tiles:       device [batch][n_rows][C] (dtype `dtype`).
+ *  dst_row_begin: device [n_dst_rows + 1] int64 (tdp_plan), non-decreasing,
+ *                 last entry <= n_rows.
+ *  dst_rows:      device int32 row ids in [0, n_rows) (others are skipped).
+ *  row_weight:    device [n_rows] float32.
+ *  y_global:      device [batch][n_dst_rows][C] float32; overwritten when
+ *                 accumulate == 0, added to when accumulate == 1 (the sum over
+ *                 ranks of a multi-rank plan).
+ * C must be a positive multiple of 8. */
+tdp_status tdp_blend_accumulate(const void *y_tiles, int32_t dtype, int32_t batch,
+                                int64_t n_rows, int32_t C, const int64_t *dst_row_begin,
+                                const int32_t *dst_rows, const float *row_weight,
+                                int64_t n_dst_rows, float *y_global, int32_t accumulate,
+                                void *hip_stream);
+
+/* Audio average ("What it is": audio is processed untiled on every tile
+ * forward and averaged across tiles):
+ *   y_audio[b][a][:] (+)= sum_t (1 / n_tiles_total) * y_audio_tiles[t][b][a][:]
+ * over the n_tiles_local tiles given, in ascending t, float32.
+ *  y_audio_tiles: device [n_tiles_local][batch][A][C] float32.
+ *  y_audio:       device [batch][A][C] float32. */
+tdp_status tdp_audio_accumulate(const float *y_audio_tiles, int32_t n_tiles_local,
+                                int32_t n_tiles_total, int32_t batch, int32_t n_audio,
+                                int32_t C, float *y_audio, int32_t accumulate,
+                                void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDP_H */

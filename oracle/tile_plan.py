@@ -177,7 +177,9 @@ def plan(grid, tiling, cond_pos=None, normalize_positions: bool = True,
         raise PlanError(f"rank {rank} not in [0, {world_size})")
     if cond_pos is None:
         cond_pos = np.zeros((0, 3, 2), dtype=F32)
-    cond_pos = np.asarray(cond_pos, dtype=F32)
+    cond_pos = np.asarray(cond_pos, dtype=F32).reshape(-1, 3, 2)
+    if not np.all(np.isfinite(cond_pos)) or np.any(cond_pos[..., 1] < cond_pos[..., 0]):
+        raise PlanError("conditioning intervals must be finite with end >= start")
     M = int(cond_pos.shape[0])
     N = F * H * W
     dims = (F, H, W)

@@ -1,0 +1,210 @@
+"""The C ABI on the CPU: exported symbols, host plan bit-parity with the oracle,
+status codes for invalid arguments.  No GPU work is launched: device entry
+points are only called with arguments that fail validation on the host.
+"""
+import ctypes
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import tdp_inputs as ti
+from tiled_video_diffusion_amd import tdp
+
+PLAN_FIELDS = ["tile_id", "tile_box", "tile_offset", "tile_row_begin", "tile_n_gen", "row_src",
+               "row_weight", "row_pos", "cond_keep_count", "dst_row_begin", "dst_rows"]
+
+
+def test_library_exports_every_declared_symbol():
+    names = tdp.declared_symbols()
+    assert len(names) >= 12
+    L = tdp.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tdp._SIGS)
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        assert tdp.status_string(code) and tdp.status_string(code) != "unknown status"
+    assert tdp.status_string(-99) == "unknown status"
+
+
+def _assert_same_plan(pc, po):
+    for f in PLAN_FIELDS:
+        a, b = getattr(pc, f), getattr(po, f)
+        assert a.dtype == b.dtype, f
+        assert a.shape == b.shape, (f, a.shape, b.shape)
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f   # bit-exact
+    assert pc.n_rows == po.n_rows and pc.max_tile_rows == po.max_tile_rows
+
+
+@pytest.mark.parametrize("name", [n for n in ti.WORKLOADS if n != "blend_32x96x160"])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_plan_bit_exact_vs_oracle(name, normalize):
+    inp = ti.make_inputs(name)
+    wl = inp.workload
+    pc = tdp.tdp_plan(wl.grid, wl.tiling, inp.cond_pos, normalize)
+    po = oracle.plan(wl.grid, wl.tiling, inp.cond_pos, normalize)
+    _assert_same_plan(pc, po)
+    assert pc.n_tiles_total == po.n_tiles_total
+
+
+def test_plan_bit_exact_blend_workload():
+    wl = ti.workload("blend_32x96x160")
+    wl = dataclasses.replace(wl, grid=(4,) + wl.grid[1:])       # same tiling, fewer frames
+    pc = tdp.tdp_plan(wl.grid, wl.tiling)
+    po = oracle.plan(wl.grid, wl.tiling)
+    _assert_same_plan(pc, po)
+
+
+@pytest.mark.parametrize("W", [2, 3, 4, 7])
+def test_plan_bit_exact_multi_rank(W):
+    inp = ti.make_inputs("audio_32x48x80")
+    wl = dataclasses.replace(inp.workload, grid=(8, 48, 80))
+    for r in range(W):
+        pc = tdp.tdp_plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r)
+        po = oracle.plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r)
+        _assert_same_plan(pc, po)
+
+
+def _random_case(rng):
+    grid = [int(rng.integers(1, 13)) for _ in range(3)]
+    tiling = []
+    for L in grid:
+        n = int(rng.integers(1, min(L, 4) + 1))
+        core = L // n
+        o = int(rng.integers(0, core + 1)) if n > 1 else int(rng.integers(0, 3))
+        tiling.append((n, o))
+    M = int(rng.integers(0, 7))
+    cond = np.zeros((M, 3, 2), np.float32)
+    for j in range(M):
+        for d in range(3):
+            s = float(rng.integers(-3, grid[d] + 2))
+            cond[j, d] = (s, s + float(rng.integers(0, 4)))
+    return grid, tiling, cond
+
+
+def test_plan_bit_exact_random_descriptors():
+    rng = np.random.default_rng(77)
+    for _ in range(150):
+        grid, tiling, cond = _random_case(rng)
+        W = int(rng.integers(1, 4))
+        r = int(rng.integers(0, W))
+        norm = bool(rng.integers(0, 2))
+        pc = tdp.tdp_plan(grid, tiling, cond, norm, W, r)
+        po = oracle.plan(grid, tiling, cond, norm, W, r)
+        _assert_same_plan(pc, po)
+
+
+def test_plan_fractional_cond_positions():
+    cond = np.array([[[0.5, 1.25], [3.5, 7.75], [-0.5, 2.0]],
+                     [[-0.25, 0.5], [10.0, 10.0], [0.0, 0.5]]], np.float32)
+    grid, tiling = (3, 12, 10), ((1, 0), (2, 3), (2, 5))
+    _assert_same_plan(tdp.tdp_plan(grid, tiling, cond), oracle.plan(grid, tiling, cond))
+
+
+@pytest.mark.parametrize("grid,tiling,cond,world,rank,code", [
+    ((0, 4, 4), ((1, 0), (1, 0), (1, 0)), None, 1, 0, -2),
+    ((2, 4, 4), ((1, 0), (5, 0), (1, 0)), None, 1, 0, -2),
+    ((2, 4, 4), ((1, 0), (0, 0), (1, 0)), None, 1, 0, -2),
+    ((2, 8, 8), ((1, 0), (2, 5), (1, 0)), None, 1, 0, -2),
+    ((2, 8, 8), ((1, 0), (2, -1), (1, 0)), None, 1, 0, -2),
+    ((2, 8, 8), ((1, 0), (2, 2), (1, 0)), None, 0, 0, -2),
+    ((2, 8, 8), ((1, 0), (2, 2), (1, 0)), None, 2, 2, -2),
+    ((2, 8, 8), ((1, 0), (2, 2), (1, 0)), [[[0, np.nan], [0, 1], [0, 1]]], 1, 0, -2),
+    ((2, 8, 8), ((1, 0), (2, 2), (1, 0)), [[[2, 1], [0, 1], [0, 1]]], 1, 0, -2),
+])
+def test_plan_rejects_invalid(grid, tiling, cond, world, rank, code):
+    cond = None if cond is None else np.array(cond, np.float32)
+    with pytest.raises(tdp.TdpError) as e:
+        tdp.tdp_plan_query(grid, tiling, cond, True, world, rank)
+    assert e.value.status == code
+    with pytest.raises(oracle.PlanError):
+        oracle.plan(grid, tiling, cond, True, world, rank)
+
+
+def test_plan_null_and_shape_errors():
+    L = tdp.lib()
+    s = tdp.PlanSizes()
+    assert L.tdp_plan_query(None, ctypes.byref(s)) == -1
+    d, _ = tdp._desc((2, 8, 8), ((1, 0), (2, 2), (1, 0)), None, True, 1, 0)
+    assert L.tdp_plan_query(ctypes.byref(d), None) == -1
+    d.n_cond = 3                                          # M > 0 with NULL positions
+    assert L.tdp_plan_query(ctypes.byref(d), ctypes.byref(s)) == -1
+    d.n_cond = 0
+    assert L.tdp_plan_query(ctypes.byref(d), ctypes.byref(s)) == 0
+    out = tdp.PlanOut()
+    assert L.tdp_plan(ctypes.byref(d), ctypes.byref(s), ctypes.byref(out)) == -1
+    s.n_rows += 1                                         # sizes that disagree with desc
+    assert L.tdp_plan(ctypes.byref(d), ctypes.byref(s), ctypes.byref(out)) == -3
+
+
+# --- device entry points: host-side validation only (nothing is launched) ---
+
+FAKE = 1 << 20          # a non-null, 16-byte aligned value that is never dereferenced
+
+
+def test_gather_validation():
+    L = tdp.lib()
+    assert L.tdp_gather_tiles(FAKE, 5, 1, 10, 128, FAKE, 4, FAKE, None) == -4   # dtype
+    assert L.tdp_gather_tiles(FAKE, 0, 0, 10, 128, FAKE, 4, FAKE, None) == -2   # batch
+    assert L.tdp_gather_tiles(FAKE, 0, 1, 10, 12, FAKE, 4, FAKE, None) == -2    # C % 8
+    assert L.tdp_gather_tiles(None, 0, 1, 10, 128, FAKE, 4, FAKE, None) == -1
+    assert L.tdp_gather_tiles(FAKE + 4, 0, 1, 10, 128, FAKE, 4, FAKE, None) == -7
+    assert L.tdp_gather_tiles(None, 0, 1, 10, 128, None, 0, None, None) == 0     # empty: no-op
+
+
+def test_blend_validation():
+    L = tdp.lib()
+    assert L.tdp_blend_accumulate(FAKE, 0, 1, 4, 128, FAKE, FAKE, FAKE, 4, FAKE, 2, None) == -2
+    assert L.tdp_blend_accumulate(FAKE, 3, 1, 4, 128, FAKE, FAKE, FAKE, 4, FAKE, 0, None) == -4
+    assert L.tdp_blend_accumulate(FAKE, 0, 1, 4, 128, None, FAKE, FAKE, 4, FAKE, 0, None) == -1
+    assert L.tdp_blend_accumulate(FAKE, 0, 1, 4, 128, FAKE, FAKE, FAKE, 4, FAKE + 8, 0, None) == -7
+    assert L.tdp_blend_accumulate(None, 0, 1, 0, 128, None, None, None, 0, None, 0, None) == 0
+    assert L.tdp_audio_accumulate(FAKE, 3, 2, 1, 4, 128, FAKE, 0, None) == -2   # local > total
+    assert L.tdp_audio_accumulate(None, 2, 2, 1, 4, 128, FAKE, 0, None) == -1
+    assert L.tdp_audio_accumulate(None, 0, 2, 1, 0, 128, None, 0, None) == 0
+
+
+def test_attention_validation():
+    L = tdp.lib()
+    good = tdp.attn_desc(1, 128, 2, 64, 0, 0, 0)
+    n = ctypes.c_size_t()
+    assert L.tdp_tile_attention_workspace(ctypes.byref(good), 4, 800, ctypes.byref(n)) == 0
+    ws = n.value
+    assert ws > 0
+    for field, val, code in [("C", 64, -4), ("head_dim", 96, -4), ("heads", 0, -2),
+                             ("batch", 0, -2), ("x_dtype", 7, -4), ("n_audio", -1, -2),
+                             ("rope_base", 0.0, -2)]:
+        d = tdp.attn_desc(1, 128, 2, 64, 0, 0, 0)
+        setattr(d, field, val)
+        assert L.tdp_tile_attention_workspace(ctypes.byref(d), 4, 800, ctypes.byref(n)) == code
+    args = lambda **k: dict(dict(desc=ctypes.byref(good), T=4, trb=FAKE, maxr=200, rows=800,  # noqa
+                                 x=FAKE, pos=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, wo=FAKE, xa=None,
+                                 y=FAKE, ya=None, ws=FAKE, wsb=ws, s=None), **k)
+
+    def call(**k):
+        a = args(**k)
+        return L.tdp_tile_attention(*a.values())
+    assert call(wsb=ws - 1) == -5
+    assert call(wq=None) == -1
+    assert call(trb=None) == -1
+    assert call(maxr=0) == -2
+    assert call(maxr=801) == -2
+    assert call(ws=FAKE + 2) == -7
+    assert call(T=0) == -2
+    audio = tdp.attn_desc(1, 128, 2, 64, 16, 0, 0)
+    assert L.tdp_tile_attention_workspace(ctypes.byref(audio), 4, 800, ctypes.byref(n)) == 0
+    assert call(desc=ctypes.byref(audio), wsb=n.value) == -1       # audio without buffers
+    assert L.tdp_attn_core(ctypes.byref(good), 4, FAKE, 200, 800, None, ws, None) == -1
+    assert L.tdp_attn_out_proj(ctypes.byref(good), 4, FAKE, 200, 800, None, None, FAKE, ws,
+                               None) == -1
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(tdp, "_lib", None)
+    monkeypatch.setattr(tdp, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError):
+        tdp.tdp_plan_query((2, 4, 4), ((1, 0), (1, 0), (1, 0)))

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: gather bit-exact; fp32 blend within 1e-5 (max abs error / max abs
+reference, fed the GPU's own tile outputs); attention outputs within 2e-2 of
+the float64 oracle by the same measure (bf16 operands on the GPU).  Full-size
+workloads the oracle cannot finish quickly are checked on sampled query rows,
+which the oracle evaluates one by one against all keys of their tile.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import tdp_inputs as ti
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = 2e-2
+BLEND_TOL = 1e-5
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return float(np.abs(got - want).max() / max(np.abs(want).max(), 1e-30))
+
+
+def _step(inp, **kw):
+    from tiled_video_diffusion_amd.step import TdpStep
+    return TdpStep(inp, **kw)
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+# --------------------------------------------------------------------------
+# gather / blend / identity
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_2x16x16", "d64_8x32x32", "audio_32x48x80",
+                                  "blend_32x96x160"])
+def test_gather_bit_exact(name):
+    say("gather", name)
+    inp = ti.make_inputs(name)
+    s = _step(inp, identity=True)
+    s.gather()
+    torch.cuda.synchronize()
+    want = inp.x_global[:, s.plan.row_src, :]
+    got = s.x_tiles.float().cpu().numpy()
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", ["tiny_2x16x16", "d64_8x32x32", "audio_32x48x80",
+                                  "blend_32x96x160"])
+def test_identity_step_reconstructs(name):
+    """Identity denoiser: the blend gives back the latent (every kept row)."""
+    say("identity", name)
+    inp = ti.make_inputs(name)
+    s = _step(inp, identity=True)
+    s.run()
+    torch.cuda.synchronize()
+    y = _np(s.y_global)
+    kept = np.concatenate([np.ones(inp.workload.n_gen, bool), s.plan.cond_keep_count > 0])
+    assert rel_err(y[:, kept], inp.x_global[:, kept]) <= BLEND_TOL
+    assert np.all(y[:, ~kept] == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny_2x16x16", "d64_8x32x32", "audio_32x48x80"])
+def test_blend_matches_oracle_on_random_tile_outputs(name):
+    """Blend of arbitrary tile outputs, overwrite then accumulate."""
+    say("blend random", name)
+    inp = ti.make_inputs(name)
+    s = _step(inp, identity=True)
+    rng = np.random.default_rng(11)
+    y = rng.standard_normal(tuple(s.x_tiles.shape)).astype(np.float32)
+    s.x_tiles.copy_(torch.from_numpy(y).to(s.x_tiles.dtype))
+    yt = _np(s.x_tiles)
+    s.blend(accumulate=False)
+    torch.cuda.synchronize()
+    p = oracle.plan(inp.workload.grid, inp.workload.tiling, inp.cond_pos)
+    want = oracle.blend_tiles(yt, p)
+    assert rel_err(_np(s.y_global), want) <= BLEND_TOL
+    s.blend(accumulate=True)
+    torch.cuda.synchronize()
+    assert rel_err(_np(s.y_global), 2 * want) <= BLEND_TOL
+
+
+# --------------------------------------------------------------------------
+# attention end to end
+# --------------------------------------------------------------------------
+
+def _check_full(inp, s, normalize=True):
+    """Whole-step parity against the oracle (all rows)."""
+    r = oracle.step(inp, normalize_positions=normalize, p=None)
+    torch.cuda.synchronize()
+    yt = _np(s.y_tiles)
+    e_tiles = rel_err(yt, r.y_tiles)
+    e_glob = rel_err(_np(s.y_global), r.y_global)
+    # blend bar: the oracle blend of the GPU's own tile outputs
+    e_blend = rel_err(_np(s.y_global), oracle.blend_tiles(yt, r.plan))
+    say(f"  y_tiles {e_tiles:.2e}  y_global {e_glob:.2e}  blend {e_blend:.2e}")
+    assert e_tiles <= ATTN_TOL and e_glob <= ATTN_TOL and e_blend <= BLEND_TOL
+    if r.y_aud is not None:
+        e_at = rel_err(_np(s.y_audio_tiles), r.y_aud_tiles)
+        e_a = rel_err(_np(s.y_audio), r.y_aud)
+        say(f"  y_audio_tiles {e_at:.2e}  y_audio {e_a:.2e}")
+        assert e_at <= ATTN_TOL and e_a <= ATTN_TOL
+        e_am = rel_err(_np(s.y_audio), oracle.audio_mean(_np(s.y_audio_tiles), r.plan.n_tiles_total))
+        assert e_am <= BLEND_TOL
+
+
+@pytest.mark.parametrize("name", ["tiny_2x16x16", "d64_8x32x32"])
+def test_attention_step_full(name):
+    say("attention full", name)
+    inp = ti.make_inputs(name)
+    s = _step(inp)
+    s.run()
+    _check_full(inp, s)
+
+
+def _variant(base, **kw):
+    wl = dataclasses.replace(ti.workload(base), **kw)
+    return ti.make_inputs(wl)
+
+
+EDGE_CASES = {
+    # odd overlaps, tiles not multiples of 64/128, audio not a multiple of 64, batch 2
+    "odd_ragged_audio_d128": dict(base="tiny_2x16x16", grid=(3, 17, 23),
+                                  tiling=((1, 0), (3, 5), (4, 5)), heads=2, head_dim=128,
+                                  n_cond=12, n_cond_neg=3, n_audio=37, batch=2,
+                                  latent_dtype="bf16"),
+    # a single tile shorter than one key block, fp32 latent
+    "one_small_tile": dict(base="tiny_2x16x16", grid=(1, 5, 7), tiling=((1, 0), (1, 0), (1, 0)),
+                           n_cond=3, n_cond_neg=1),
+    # tiles in all three dims, d=64, many heads, ragged rows
+    "3d_tiles_d64": dict(base="d64_8x32x32", grid=(6, 13, 11), tiling=((2, 2), (2, 3), (3, 1)),
+                         heads=6, n_cond=9, n_cond_neg=2, n_audio=65, batch=2),
+    # a tile of more than one 128-row block plus a 1-row remainder
+    "remainder_rows": dict(base="tiny_2x16x16", grid=(1, 129, 1), tiling=((1, 0), (1, 0), (1, 0)),
+                           n_cond=0, n_cond_neg=0),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE_CASES))
+def test_attention_edge_cases(case):
+    kw = dict(EDGE_CASES[case])
+    base = kw.pop("base")
+    say("edge case", case)
+    inp = _variant(base, **kw)
+    s = _step(inp)
+    s.run()
+    _check_full(inp, s)
+
+
+def test_normalize_off_matches_oracle():
+    say("normalize off tiny")
+    inp = ti.make_inputs("tiny_2x16x16")
+    s = _step(inp, normalize_positions=False)
+    s.run()
+    _check_full(inp, s, normalize=False)
+
+
+def test_stage_split_equals_fused_call():
+    say("stage split d64")
+    inp = ti.make_inputs("d64_8x32x32")
+    s = _step(inp)
+    s.gather()
+    s.attention()
+    torch.cuda.synchronize()
+    fused = s.y_tiles.clone()
+    s.y_tiles.zero_()
+    s.attn_prepare()
+    s.attn_qkv()
+    s.attn_core()
+    s.attn_out()
+    torch.cuda.synchronize()
+    assert torch.equal(fused, s.y_tiles)
+
+
+def _sample_rows(p, t, rng, k):
+    r0, r1 = int(p.tile_row_begin[t]), int(p.tile_row_begin[t + 1])
+    n = r1 - r0
+    picks = {0, n - 1, int(p.tile_n_gen[t]) - 1, min(n - 1, 127), min(n - 1, 128)}
+    picks |= set(rng.integers(0, n, size=k).tolist())
+    return np.array(sorted(picks)), r0, r1
+
+
+@pytest.mark.parametrize("name", ["t16_16x64x64", "audio_32x48x80"])
+def test_attention_full_size_sampled(name):
+    """Full-size workloads in the benchmark's launch configuration, sampled rows."""
+    say("attention sampled", name)
+    inp = ti.make_inputs(name)
+    wl = inp.workload
+    s = _step(inp)
+    s.run()
+    torch.cuda.synchronize()
+    p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    yt = _np(s.y_tiles)
+    # blend bar on every row: the oracle blend of the GPU's own tile outputs
+    e_blend = rel_err(_np(s.y_global), oracle.blend_tiles(yt, p))
+    say(f"  blend {e_blend:.2e}")
+    assert e_blend <= BLEND_TOL
+    rng = np.random.default_rng(3)
+    tiles = sorted({0, p.tile_id.size - 1, int(np.argmax(np.diff(p.tile_row_begin)))} |
+                   set(rng.integers(0, p.tile_id.size, size=1).tolist()))
+    x_tiles = oracle.gather_tiles(inp.x_global, p)
+    for t in tiles:
+        rows, r0, r1 = _sample_rows(p, t, rng, 24)
+        for b in range(wl.batch):
+            xa = None if inp.x_aud is None else inp.x_aud[b]
+            aq = None if xa is None else np.array([0, 5, xa.shape[0] - 1])
+            y, ya = oracle.tile_forward(x_tiles[b, r0:r1], p.row_pos[r0:r1], xa, inp.wq, inp.wk,
+                                        inp.wv, inp.wo, wl.heads, wl.head_dim,
+                                        query_rows=rows, audio_query_rows=aq)
+            e = rel_err(yt[b, r0 + rows], y)
+            say(f"  tile {t} batch {b} rows {rows.size}: {e:.2e}")
+            assert e <= ATTN_TOL
+            if ya is not None:
+                ea = rel_err(_np(s.y_audio_tiles)[t, b, aq], ya)
+                say(f"  tile {t} batch {b} audio rows: {ea:.2e}")
+                assert ea <= ATTN_TOL
+    if s.y_audio is not None:
+        e_am = rel_err(_np(s.y_audio), oracle.audio_mean(_np(s.y_audio_tiles), p.n_tiles_total))
+        assert e_am <= BLEND_TOL
+
+
+@pytest.mark.parametrize("W", [2, 4])
+def test_multi_rank_sum_equals_single_rank(W):
+    """The page's single all_reduce: summing the W ranks' blends equals one rank's."""
+    say("multi-rank", W)
+    inp = _variant("audio_32x48x80", grid=(8, 48, 80), heads=4)
+    full = _step(inp)
+    full.run()
+    acc_g = torch.zeros_like(full.y_global)
+    acc_a = torch.zeros_like(full.y_audio)
+    for r in range(W):
+        s = _step(inp, world_size=W, rank=r)
+        s.y_global = acc_g
+        s.y_audio = acc_a
+        s.run(accumulate=True)
+    torch.cuda.synchronize()
+    assert rel_err(_np(acc_g), _np(full.y_global)) <= BLEND_TOL
+    assert rel_err(_np(acc_a), _np(full.y_audio)) <= BLEND_TOL
+
+
+def test_repeat_runs_are_deterministic():
+    say("determinism d64")
+    inp = ti.make_inputs("d64_8x32x32")
+    s = _step(inp)
+    s.run()
+    torch.cuda.synchronize()
+    a = s.y_global.clone()
+    s.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a, s.y_global)

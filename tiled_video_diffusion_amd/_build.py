@@ -1,0 +1,76 @@
+"""Build libtdp.so in-tree: host plan with g++, gfx950 kernels with hipcc.
+
+Every HIP source is compiled with packed-fp32 instructions disabled
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host plan is
+compiled with ``-ffp-contract=off`` so its float32 outputs are single IEEE
+operations.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libtdp.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-I", INCLUDE, "-I", CSRC]
+CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-ffp-contract=off",
+             "-I", INCLUDE]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    err = "\n".join(line for line in r.stderr.splitlines() if noise not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{err}")
+    return err
+
+
+def sources():
+    hip = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
+    cpp = sorted(f for f in os.listdir(CSRC) if f.endswith(".cpp"))
+    return hip, cpp
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``libtdp.so`` next to this file; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    hip, cpp = sources()
+    hipcc = _hipcc()
+    jobs = []
+    for f in hip:
+        obj = os.path.join(BUILD, f + ".o")
+        jobs.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, f), "-o", obj])
+    for f in cpp:
+        obj = os.path.join(BUILD, f + ".o")
+        jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, f), "-o", obj])
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        for cmd, err in zip(jobs, ex.map(_run, jobs)):
+            if verbose and err.strip():
+                print(err)
+    objs = [j[-1] for j in jobs]
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,871 @@
+// Per-tile multi-head self-attention with 3D RoPE on gfx950 (MI355X).
+//
+// "Tiled Data Parallelism (TDP)" page: "What it is" - every tile runs the
+// denoiser with only its own rows (plus the untiled audio tokens); "When to
+// use it" - attention is quadratic in a tile's token count, which is where the
+// time goes; "Position normalization" - RoPE sees each tile's normalized
+// positions.  The denoiser is one attention layer (see tdp.h).
+//
+// Stages (one stream):
+//   prepare   W^T copies of the weights; a table mapping every 128-row block
+//             of the padded row space to (tile, first row).
+//   qkv_rope  Q, K (row-major per token) and V^T (keys contiguous) in bf16,
+//             RoPE applied to the fp32 accumulator; tiles padded to 128 rows
+//             with zero rows so every K/V block load is aligned and finite.
+//   core      flash attention per (batch, head, 128-query block): S^T = K Q^T
+//             and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16.  With keys on
+//             the MFMA rows, a lane holds one query's scores, so the online
+//             softmax needs one cross-half exchange per 64-key block, and P
+//             stays in registers as the B operand of the second MFMA.
+//   out_proj  Y = O Wo on MFMA, into y_tiles / y_audio_tiles.
+#include <cmath>
+
+#include "tdp_common.h"
+
+namespace tdp {
+namespace {
+
+constexpr int kC = 128;       // channels per token row
+constexpr int kBM = 128;      // query rows per attention block (4 waves x 32)
+constexpr int kBN = 64;       // keys per attention iteration
+constexpr int kRowPad = 128;  // tile rows are padded to a multiple of this
+constexpr int kThreads = 256;
+static_assert(kBM == kRowPad && kBM == 4 * 32, "a query block is one padded row block, 32 rows per wave");
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace layout (byte offsets, each 256-aligned).
+struct Layout {
+  int64_t npb = 0;    // 128-row blocks of the padded tile row space (upper bound)
+  int64_t n_pad = 0;  // npb * 128 rows per (batch, head) slab
+  int64_t a_pad = 0;  // audio rows padded to 128
+  int32_t n_aqb = 0;  // 128-query audio blocks per tile
+  int32_t hidden = 0;
+  size_t off_wt = 0, off_wot = 0, off_pad_begin = 0, off_blk_tile = 0, off_blk_q0 = 0;
+  size_t off_q = 0, off_k = 0, off_vt = 0, off_qa = 0, off_ka = 0, off_vta = 0;
+  size_t off_o = 0, off_oa = 0, total = 0;
+};
+
+tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, Layout *L) {
+  if (!d) return TDP_ERR_NULL;
+  if (d->batch < 1 || d->batch > 65535 || d->heads < 1 || d->n_audio < 0 || n_tiles < 1 ||
+      n_tiles > (1 << 20) || n_rows < 1 || n_rows > INT32_MAX || !(d->rope_base > 0.0f) ||
+      !std::isfinite(d->rope_base))
+    return TDP_ERR_ARG;
+  if (d->C != kC || (d->head_dim != 64 && d->head_dim != 128)) return TDP_ERR_UNSUPPORTED;
+  if ((d->x_dtype != TDP_F32 && d->x_dtype != TDP_BF16) ||
+      (d->y_dtype != TDP_F32 && d->y_dtype != TDP_BF16))
+    return TDP_ERR_UNSUPPORTED;
+  const int64_t hidden = static_cast<int64_t>(d->heads) * d->head_dim;
+  if (hidden > (1 << 16)) return TDP_ERR_UNSUPPORTED;
+  L->hidden = static_cast<int32_t>(hidden);
+  L->npb = (n_rows + static_cast<int64_t>(kRowPad - 1) * n_tiles) / kRowPad;
+  L->n_pad = L->npb * kRowPad;
+  L->a_pad = ceil_div(d->n_audio, kRowPad) * kRowPad;
+  L->n_aqb = static_cast<int32_t>(L->a_pad / kRowPad);
+  const size_t B = d->batch, H = d->heads, D = d->head_dim, T = n_tiles, A = d->n_audio;
+  size_t off = 0;
+  auto take = [&off](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+  L->off_wt = take(3 * hidden * kC * 2);
+  L->off_wot = take(kC * hidden * 2);
+  L->off_pad_begin = take((T + 1) * 4);
+  L->off_blk_tile = take(L->npb * 4);
+  L->off_blk_q0 = take(L->npb * 4);
+  L->off_q = take(B * H * L->n_pad * D * 2);
+  L->off_k = take(B * H * L->n_pad * D * 2);
+  L->off_vt = take(B * H * L->n_pad * D * 2);
+  L->off_qa = take(B * H * L->a_pad * D * 2);
+  L->off_ka = take(B * H * L->a_pad * D * 2);
+  L->off_vta = take(B * H * L->a_pad * D * 2);
+  L->off_o = take(B * static_cast<size_t>(n_rows) * hidden * 2);
+  L->off_oa = take(T * B * A * hidden * 2);
+  L->total = off;
+  return TDP_OK;
+}
+
+template <typename T>
+T *ws_at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+// ---------------------------------------------------------------------------
+// prepare
+// ---------------------------------------------------------------------------
+
+// dst[m][f][c] = src_m[c][f] for the three [C][hidden] input projections, and
+// wot[c][f] = wo[f][c].  One thread per element (a few MB, once per call).
+__global__ void transpose_weights_kernel(const bf16 *__restrict__ wq, const bf16 *__restrict__ wk,
+                                         const bf16 *__restrict__ wv, const bf16 *__restrict__ wo,
+                                         int32_t hidden, bf16 *__restrict__ wt,
+                                         bf16 *__restrict__ wot) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per = static_cast<int64_t>(hidden) * kC;
+  if (i < 3 * per) {
+    const int64_t m = i / per, rem = i - m * per;
+    const int64_t f = rem / kC, c = rem - f * kC;
+    const bf16 *src = m == 0 ? wq : (m == 1 ? wk : wv);
+    wt[i] = src[c * hidden + f];
+  } else if (i < 4 * per) {
+    const int64_t j = i - 3 * per;
+    const int64_t c = j / hidden, f = j - c * hidden;
+    wot[j] = wo[f * kC + c];
+  }
+}
+
+// Rows of tile t, clamped into [0, n_rows] and to max_rows.
+__device__ inline void tile_rows(const int64_t *trb, int32_t t, int64_t n_rows, int32_t max_rows,
+                                 int64_t *r0, int32_t *len) {
+  int64_t a = trb[t], b = trb[t + 1];
+  a = a < 0 ? 0 : (a > n_rows ? n_rows : a);
+  b = b < a ? a : (b > n_rows ? n_rows : b);
+  *r0 = a;
+  *len = static_cast<int32_t>(min(b - a, static_cast<int64_t>(max_rows)));
+}
+
+// pad_begin[t] = first 128-row block of tile t in the padded row space (clamped
+// to npb); blk_tile/blk_q0 map each block to its tile and first tile row (-1
+// for blocks past the last tile).  One workgroup.
+__global__ __launch_bounds__(1024) void block_table_kernel(const int64_t *__restrict__ trb,
+                                                           int32_t T, int64_t n_rows,
+                                                           int32_t max_rows, int64_t npb,
+                                                           int32_t *__restrict__ pad_begin,
+                                                           int32_t *__restrict__ blk_tile,
+                                                           int32_t *__restrict__ blk_q0) {
+  for (int32_t t = threadIdx.x; t < T; t += blockDim.x) {
+    int64_t r0;
+    int32_t len;
+    tile_rows(trb, t, n_rows, max_rows, &r0, &len);
+    pad_begin[t + 1] = static_cast<int32_t>(ceil_div(len, kRowPad));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    pad_begin[0] = 0;
+    int64_t acc = 0;
+    for (int32_t t = 0; t < T; ++t) {
+      acc = min(acc + pad_begin[t + 1], npb);
+      pad_begin[t + 1] = static_cast<int32_t>(acc);
+    }
+  }
+  __syncthreads();
+  const int32_t used = pad_begin[T];
+  for (int64_t pb = threadIdx.x; pb < npb; pb += blockDim.x) {
+    int32_t tile = -1, q0 = 0;
+    if (pb < used) {
+      int32_t lo = 0, hi = T - 1;  // last t with pad_begin[t] <= pb
+      while (lo < hi) {
+        const int32_t mid = (lo + hi + 1) >> 1;
+        if (pad_begin[mid] <= pb) lo = mid; else hi = mid - 1;
+      }
+      tile = lo;
+      q0 = static_cast<int32_t>((pb - pad_begin[lo]) * kRowPad);
+    }
+    blk_tile[pb] = tile;
+    blk_q0[pb] = q0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// qkv_rope
+// ---------------------------------------------------------------------------
+
+template <typename TX>
+__device__ inline bf16x8 load_x8(const TX *p);
+template <>
+__device__ inline bf16x8 load_x8<bf16>(const bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+template <>
+__device__ inline bf16x8 load_x8<float>(const float *p) {
+  const f32x4 a = *reinterpret_cast<const f32x4 *>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
+  bf16x8 r;
+  r[0] = static_cast<bf16>(a[0]); r[1] = static_cast<bf16>(a[1]);
+  r[2] = static_cast<bf16>(a[2]); r[3] = static_cast<bf16>(a[3]);
+  r[4] = static_cast<bf16>(b[0]); r[5] = static_cast<bf16>(b[1]);
+  r[6] = static_cast<bf16>(b[2]); r[7] = static_cast<bf16>(b[3]);
+  return r;
+}
+
+struct QkvArgs {
+  const void *x;              // tile rows [B][x_rows][C] or audio [B][A][C]
+  int64_t x_rows;
+  const int32_t *blk_tile, *blk_q0, *pad_begin;
+  const int64_t *trb;
+  int64_t n_rows;
+  int32_t max_rows;
+  const float *row_pos;       // [n_rows][3][2]
+  const bf16 *wt;             // [3][hidden][C]
+  int32_t heads, hidden;
+  int64_t n_pad;              // padded rows per (batch, head) slab of the outputs
+  float log2_theta_step;      // -log2(rope_base) / p
+  bf16 *q, *k, *vt;
+};
+
+// One workgroup = 128 token rows (4 waves x 32) of one batch entry, all
+// 3*heads output chunks of head_dim features.  D[feature][token] = W^T X^T on
+// MFMA, so a lane owns one token and groups of 4 consecutive features: RoPE
+// pairs (2i, 2i+1) sit in one lane and cos/sin depend on that lane's token,
+// computed once and reused by every Q and K head.
+template <typename TX, int D, bool AUDIO>
+__global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
+  constexpr int kFT = D / 32;            // 32-feature MFMA tiles per head
+  constexpr int kPairs = D / 4;          // rotation pairs held per lane
+  constexpr int kLdsRow = kC + 8;        // bf16 elements per staged W^T row
+  __shared__ __attribute__((aligned(16))) bf16 sW[D * kLdsRow];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int64_t b = blockIdx.y;
+  const int64_t pb = blockIdx.x;
+
+  int64_t src0 = 0, pad_row0 = 0;
+  int32_t nvalid = 0, tile = 0;
+  if (AUDIO) {
+    src0 = pb * kRowPad;
+    pad_row0 = pb * kRowPad;
+    nvalid = static_cast<int32_t>(min(static_cast<int64_t>(kRowPad), a.x_rows - src0));
+  } else {
+    tile = a.blk_tile[pb];
+    if (tile < 0) return;
+    const int32_t q0 = a.blk_q0[pb];
+    int64_t r0;
+    int32_t len;
+    tile_rows(a.trb, tile, a.n_rows, a.max_rows, &r0, &len);
+    src0 = r0 + q0;
+    pad_row0 = static_cast<int64_t>(a.pad_begin[tile]) * kRowPad + q0;
+    nvalid = len - q0;
+  }
+  const int my = wave * 32 + l32;
+  const bool valid = my < nvalid;
+
+  // X^T fragments (B operand): token `my`, channels 16s + 8hh + 0..7.
+  bf16x8 xf[kC / 16];
+  const TX *xrow = static_cast<const TX *>(a.x) + (b * a.x_rows + src0 + (valid ? my : 0)) * kC;
+#pragma unroll
+  for (int s = 0; s < kC / 16; ++s) {
+    xf[s] = valid ? load_x8<TX>(xrow + 16 * s + 8 * hh) : bf16x8{};
+  }
+
+  // cos/sin of the lane's rotation pairs: pair j = 16 ft + 4 g + 2 hh + e.
+  float rc[kPairs], rs[kPairs];
+  if (!AUDIO) {
+    constexpr int p = D / 6;
+    float mid[3] = {0.f, 0.f, 0.f};
+    if (valid) {
+      const float *pp = a.row_pos + (src0 + my) * 6;
+#pragma unroll
+      for (int ax = 0; ax < 3; ++ax) mid[ax] = 0.5f * (pp[2 * ax] + pp[2 * ax + 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int ft = i / 8, g = (i / 2) % 4, e = i % 2;
+      const int j = 16 * ft + 4 * g + 2 * hh + e;
+      const int ax = j / p;
+      float c = 1.f, s = 0.f;
+      if (ax < 3) {
+        const float theta = exp2f(static_cast<float>(j - ax * p) * a.log2_theta_step);
+        sincosf(mid[ax] * theta, &s, &c);
+      }
+      rc[i] = c;
+      rs[i] = s;
+    }
+  }
+
+  for (int chunk = 0; chunk < 3 * a.heads; ++chunk) {
+    const int m = chunk / a.heads, h = chunk - m * a.heads;
+    __syncthreads();
+    {  // stage W^T rows [m][h*D, h*D + D) into LDS
+      const bf16 *src = a.wt + (static_cast<int64_t>(m) * a.hidden + static_cast<int64_t>(h) * D) * kC;
+#pragma unroll
+      for (int i = 0; i < D * kC / 8 / kThreads; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        const int row = c / (kC / 8), col = (c % (kC / 8)) * 8;
+        *reinterpret_cast<bf16x8 *>(&sW[row * kLdsRow + col]) =
+            *reinterpret_cast<const bf16x8 *>(src + row * kC + col);
+      }
+    }
+    __syncthreads();
+    const int64_t slab = b * a.heads + h;
+#pragma unroll
+    for (int ft = 0; ft < kFT; ++ft) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int s = 0; s < kC / 16; ++s) {
+        const bf16x8 w = *reinterpret_cast<const bf16x8 *>(&sW[(32 * ft + l32) * kLdsRow + 16 * s + 8 * hh]);
+        acc = mfma32(w, xf[s], acc);
+      }
+      // acc[v]: feature 32 ft + 8 (v/4) + 4 hh + v%4 of token `my`
+      if (!AUDIO && m < 2) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = ft * 8 + g * 2 + e, v = 4 * g + 2 * e;
+            const float x0 = acc[v], x1 = acc[v + 1];
+            acc[v] = x0 * rc[i] - x1 * rs[i];
+            acc[v + 1] = x0 * rs[i] + x1 * rc[i];
+          }
+        }
+      }
+      if (m < 2) {
+        bf16 *dst = (m == 0 ? a.q : a.k) + (slab * a.n_pad + pad_row0 + my) * D + 32 * ft + 4 * hh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v4;
+          v4[0] = static_cast<bf16>(acc[4 * g + 0]);
+          v4[1] = static_cast<bf16>(acc[4 * g + 1]);
+          v4[2] = static_cast<bf16>(acc[4 * g + 2]);
+          v4[3] = static_cast<bf16>(acc[4 * g + 3]);
+          *reinterpret_cast<bf16x4 *>(dst + 8 * g) = v4;
+        }
+      } else {
+        bf16 *dst = a.vt + (slab * D + 32 * ft + 4 * hh) * a.n_pad + pad_row0 + my;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          dst[static_cast<int64_t>(8 * (v / 4) + (v % 4)) * a.n_pad] = static_cast<bf16>(acc[v]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// core
+// ---------------------------------------------------------------------------
+
+struct CoreArgs {
+  const bf16 *q, *k, *vt, *qa, *ka, *vta;
+  bf16 *o, *oa;
+  const int32_t *blk_tile, *blk_q0, *pad_begin;
+  const int64_t *trb;
+  int64_t npb, n_pad, a_pad, n_rows, units_per_bh, total_units;
+  int32_t T, heads, batch, A, n_aqb, max_rows, hidden;
+  float scale_log2;           // log2(e) / sqrt(head_dim)
+};
+
+template <int D>
+struct CoreSmem {
+  static constexpr int kKRow = D + 8;     // bf16 per staged K row (272 B at D=128)
+  static constexpr int kVRow = kBN + 4;   // bf16 per staged V^T row (136 B)
+  bf16 k[2][kBN * kKRow];
+  bf16 v[2][D * kVRow];
+};
+
+// Global -> register staging of one 64-key block (K rows and V^T columns).
+template <int D>
+struct KvStage {
+  static constexpr int kKChunks = kBN * D / 8 / kThreads;   // 16-byte pieces per thread
+  static constexpr int kVChunks = D * kBN / 8 / kThreads;
+  bf16x8 kr[kKChunks];
+  bf16x8 vr[kVChunks];
+
+  __device__ void load(const bf16 *kseg, const bf16 *vseg, int64_t vstride, int k0) {
+#pragma unroll
+    for (int i = 0; i < kKChunks; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      kr[i] = *reinterpret_cast<const bf16x8 *>(kseg + static_cast<int64_t>(k0 + row) * D + col);
+    }
+#pragma unroll
+    for (int i = 0; i < kVChunks; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int d = c / (kBN / 8), col = (c % (kBN / 8)) * 8;
+      vr[i] = *reinterpret_cast<const bf16x8 *>(vseg + d * vstride + k0 + col);
+    }
+  }
+  __device__ void store(CoreSmem<D> &sm, int buf) const {
+#pragma unroll
+    for (int i = 0; i < kKChunks; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      *reinterpret_cast<bf16x8 *>(&sm.k[buf][row * CoreSmem<D>::kKRow + col]) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kVChunks; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int d = c / (kBN / 8), col = (c % (kBN / 8)) * 8;
+      bf16 *p = &sm.v[buf][d * CoreSmem<D>::kVRow + col];
+      *reinterpret_cast<bf16x4 *>(p) = bf16x4{vr[i][0], vr[i][1], vr[i][2], vr[i][3]};
+      *reinterpret_cast<bf16x4 *>(p + 4) = bf16x4{vr[i][4], vr[i][5], vr[i][6], vr[i][7]};
+    }
+  }
+};
+
+// Blocks are enumerated as (batch, head, unit) with the units of one (batch,
+// head) contiguous: first the 128-row blocks of every tile (tile order), then
+// the audio query blocks of every tile.  Hardware hands consecutive workgroup
+// ids to the 8 XCDs in turn; the id is remapped so each XCD walks a
+// contiguous range of units and the blocks sharing a tile's K/V run together
+// on one L2.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
+  __shared__ __attribute__((aligned(16))) CoreSmem<D> sm;
+  constexpr int kSteps = D / 16;   // MFMA k-steps over head_dim
+  constexpr int kDT = D / 32;      // 32-row tiles of O^T
+
+  const int64_t G = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t lid = (bid % 8) * (G / 8) + bid / 8;   // gridDim.x is a multiple of 8
+  if (lid >= a.total_units) return;
+  const int64_t bh = lid / a.units_per_bh;
+  const int64_t u = lid - bh * a.units_per_bh;
+  const int64_t b = bh / a.heads;
+  const int h = static_cast<int>(bh - b * a.heads);
+
+  int32_t t, q0;
+  bool audio_q;
+  if (u < a.npb) {
+    t = a.blk_tile[u];
+    if (t < 0) return;
+    q0 = a.blk_q0[u];
+    audio_q = false;
+  } else {
+    const int64_t ua = u - a.npb;
+    t = static_cast<int32_t>(ua / a.n_aqb);
+    q0 = static_cast<int32_t>((ua - static_cast<int64_t>(t) * a.n_aqb) * kRowPad);
+    audio_q = true;
+  }
+  int64_t r0;
+  int32_t len0;
+  tile_rows(a.trb, t, a.n_rows, a.max_rows, &r0, &len0);
+  const int64_t pad0 = static_cast<int64_t>(a.pad_begin[t]) * kRowPad;
+  len0 = static_cast<int32_t>(min(static_cast<int64_t>(len0),
+                                  static_cast<int64_t>(a.pad_begin[t + 1]) * kRowPad - pad0));
+  const int32_t nq = audio_q ? (a.A - q0) : (len0 - q0);
+  if (nq <= 0) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  // Q fragments (B operand of S^T = K Q^T): query row wave*32 + l32.
+  const bf16 *qsrc = audio_q ? a.qa + ((bh * a.a_pad) + q0) * D
+                             : a.q + ((bh * a.n_pad) + pad0 + q0) * D;
+  bf16x8 qf[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + (wave * 32 + l32) * D + 16 * s + 8 * hh);
+
+  const bf16 *kseg0 = a.k + (bh * a.n_pad + pad0) * D;
+  const bf16 *vseg0 = a.vt + bh * D * a.n_pad + pad0;
+  const bf16 *kseg1 = a.ka + bh * a.a_pad * D;
+  const bf16 *vseg1 = a.vta + bh * D * a.a_pad;
+  const int nkb0 = static_cast<int>(ceil_div(len0, kBN));
+  const int nkb = nkb0 + static_cast<int>(ceil_div(a.A, kBN));
+  if (nkb == 0) return;
+
+  f32x16 o[kDT];
+#pragma unroll
+  for (int i = 0; i < kDT; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  KvStage<D> st;
+  if (nkb0 > 0) st.load(kseg0, vseg0, a.n_pad, 0);
+  else st.load(kseg1, vseg1, a.a_pad, 0);
+  st.store(sm, 0);
+  __syncthreads();
+
+  for (int j = 0; j < nkb; ++j) {
+    const int buf = j & 1;
+    const bool seg1 = j >= nkb0;
+    const int kvalid = seg1 ? min(kBN, a.A - (j - nkb0) * kBN) : min(kBN, len0 - j * kBN);
+    if (j + 1 < nkb) {
+      const int jn = j + 1;
+      if (jn < nkb0) st.load(kseg0, vseg0, a.n_pad, jn * kBN);
+      else st.load(kseg1, vseg1, a.a_pad, (jn - nkb0) * kBN);
+    }
+
+    // S^T for keys [32 kt, 32 kt + 32) of the block, this wave's 32 queries.
+    f32x16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      s[kt] = f32x16{};
+#pragma unroll
+      for (int st_ = 0; st_ < kSteps; ++st_) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
+            &sm.k[buf][(32 * kt + l32) * CoreSmem<D>::kKRow + 16 * st_ + 8 * hh]);
+        s[kt] = mfma32(kf, qf[st_], s[kt]);
+      }
+    }
+    if (kvalid < kBN) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (32 * kt + 8 * (v / 4) + 4 * hh + (v % 4) >= kvalid) s[kt][v] = -INFINITY;
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f((m_run - m_new) * a.scale_log2);
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int i = 0; i < kDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      l_run *= alpha;
+    }
+    m_run = m_new;
+    const float mb = m_new * a.scale_log2;
+
+    // P (bf16) as the B operand of O^T += V^T P^T: step (kt, u) holds keys
+    // 32 kt + 16 u + {4 hh + 0..3, 8 + 4 hh + 0..3}, i.e. s[kt][8u .. 8u+7].
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = exp2f(fmaf(s[kt][v], a.scale_log2, -mb));
+        l_run += p;
+        pf[kt][v / 8][v % 8] = static_cast<bf16>(p);
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+          const bf16 *vp = &sm.v[buf][(32 * dt + l32) * CoreSmem<D>::kVRow + 32 * kt + 16 * uu + 4 * hh];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vp);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vp + 8);
+          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[dt] = mfma32(vf, pf[kt][uu], o[dt]);
+        }
+      }
+    }
+    if (j + 1 < nkb) st.store(sm, buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  const int row = wave * 32 + l32;
+  if (row < nq) {
+    bf16 *dst = audio_q
+        ? a.oa + ((static_cast<int64_t>(t) * a.batch + b) * a.A + q0 + row) * a.hidden
+        : a.o + (b * a.n_rows + r0 + q0 + row) * a.hidden;
+    dst += h * D + 4 * hh;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v4;
+        v4[0] = static_cast<bf16>(o[dt][4 * g + 0] * inv);
+        v4[1] = static_cast<bf16>(o[dt][4 * g + 1] * inv);
+        v4[2] = static_cast<bf16>(o[dt][4 * g + 2] * inv);
+        v4[3] = static_cast<bf16>(o[dt][4 * g + 3] * inv);
+        *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * g) = v4;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// out_proj
+// ---------------------------------------------------------------------------
+
+template <typename TY>
+__device__ inline void store_y(TY *p, float v);
+template <>
+__device__ inline void store_y<float>(float *p, float v) { *p = v; }
+template <>
+__device__ inline void store_y<bf16>(bf16 *p, float v) { *p = static_cast<bf16>(v); }
+
+// Y[M][128] = O[M][hidden] Wo; one workgroup = 128 rows (4 waves x 32), all
+// 128 outputs.  Wo^T is staged through LDS 64 k at a time and shared by the
+// four waves; O rows are read straight from HBM as A operands.
+template <typename TY>
+__global__ __launch_bounds__(kThreads, 2) void out_proj_kernel(const bf16 *__restrict__ o,
+                                                               const bf16 *__restrict__ wot,
+                                                               TY *__restrict__ y, int64_t M,
+                                                               int32_t hidden) {
+  constexpr int kK = 64;
+  constexpr int kRow = kK + 8;
+  __shared__ __attribute__((aligned(16))) bf16 sB[kC * kRow];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + l32;
+  const bool valid = row < M;
+  const bf16 *arow = o + (valid ? row : 0) * hidden;
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  for (int k0 = 0; k0 < hidden; k0 += kK) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kC * kK / 8 / kThreads; ++i) {
+      const int c = threadIdx.x + i * kThreads;
+      const int r = c / (kK / 8), col = (c % (kK / 8)) * 8;
+      *reinterpret_cast<bf16x8 *>(&sB[r * kRow + col]) =
+          *reinterpret_cast<const bf16x8 *>(wot + static_cast<int64_t>(r) * hidden + k0 + col);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kK / 16; ++ks) {
+      const bf16x8 af = valid ? *reinterpret_cast<const bf16x8 *>(arow + k0 + 16 * ks + 8 * hh)
+                              : bf16x8{};
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(&sB[(32 * ct + l32) * kRow + 16 * ks + 8 * hh]);
+        acc[ct] = mfma32(af, bfr, acc[ct]);
+      }
+    }
+  }
+  // acc[ct][v]: row 8 (v/4) + 4 hh + v%4 of the wave's 32, column 32 ct + l32
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
+    if (r < M) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) store_y<TY>(y + r * kC + 32 * ct + l32, acc[ct][v]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+struct Call {
+  const tdp_attn_desc *d;
+  int32_t n_tiles;
+  const int64_t *trb;
+  int32_t max_rows;
+  int64_t n_rows;
+  void *ws;
+  size_t ws_bytes;
+  Layout L;
+};
+
+tdp_status check_call(Call *c) {
+  const tdp_status s = make_layout(c->d, c->n_tiles, c->n_rows, &c->L);
+  if (s != TDP_OK) return s;
+  if (c->max_rows < 1 || c->max_rows > c->n_rows) return TDP_ERR_ARG;
+  if (!c->trb || !c->ws) return TDP_ERR_NULL;
+  if (!aligned16(c->ws)) return TDP_ERR_ALIGN;
+  if (c->ws_bytes < c->L.total) return TDP_ERR_BUFFER;
+  return TDP_OK;
+}
+
+}  // namespace
+}  // namespace tdp
+
+using namespace tdp;
+
+extern "C" tdp_status tdp_tile_attention_workspace(const tdp_attn_desc *desc, int32_t n_tiles,
+                                                   int64_t n_rows, size_t *bytes) {
+  if (!bytes) return TDP_ERR_NULL;
+  Layout L;
+  const tdp_status s = make_layout(desc, n_tiles, n_rows, &L);
+  if (s != TDP_OK) return s;
+  *bytes = L.total;
+  return TDP_OK;
+}
+
+extern "C" tdp_status tdp_attn_prepare(const tdp_attn_desc *desc, int32_t n_tiles,
+                                       const int64_t *tile_row_begin, int32_t max_tile_rows,
+                                       int64_t n_rows, const void *wq, const void *wk,
+                                       const void *wv, const void *wo, void *workspace,
+                                       size_t workspace_bytes, void *hip_stream) {
+  Call c{desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace, workspace_bytes, {}};
+  tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  if (!wq || !wk || !wv || !wo) return TDP_ERR_NULL;
+  if (!aligned16(wq) || !aligned16(wk) || !aligned16(wv) || !aligned16(wo)) return TDP_ERR_ALIGN;
+  const Layout &L = c.L;
+  const hipStream_t stream = as_stream(hip_stream);
+  const int64_t n_el = 4LL * L.hidden * kC;
+  hipLaunchKernelGGL(transpose_weights_kernel, dim3(static_cast<uint32_t>(ceil_div(n_el, 256))),
+                     dim3(256), 0, stream, static_cast<const bf16 *>(wq),
+                     static_cast<const bf16 *>(wk), static_cast<const bf16 *>(wv),
+                     static_cast<const bf16 *>(wo), L.hidden, ws_at<bf16>(workspace, L.off_wt),
+                     ws_at<bf16>(workspace, L.off_wot));
+  if ((s = launch_status()) != TDP_OK) return s;
+  hipLaunchKernelGGL(block_table_kernel, dim3(1), dim3(1024), 0, stream, tile_row_begin, n_tiles,
+                     n_rows, max_tile_rows, L.npb, ws_at<int32_t>(workspace, L.off_pad_begin),
+                     ws_at<int32_t>(workspace, L.off_blk_tile),
+                     ws_at<int32_t>(workspace, L.off_blk_q0));
+  return launch_status();
+}
+
+namespace {
+
+template <typename TX, int D>
+void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const void *x_audio,
+                hipStream_t stream) {
+  const Layout &L = c.L;
+  QkvArgs a{};
+  a.blk_tile = ws_at<int32_t>(c.ws, L.off_blk_tile);
+  a.blk_q0 = ws_at<int32_t>(c.ws, L.off_blk_q0);
+  a.pad_begin = ws_at<int32_t>(c.ws, L.off_pad_begin);
+  a.trb = c.trb;
+  a.n_rows = c.n_rows;
+  a.max_rows = c.max_rows;
+  a.row_pos = row_pos;
+  a.wt = ws_at<bf16>(c.ws, L.off_wt);
+  a.heads = c.d->heads;
+  a.hidden = L.hidden;
+  a.log2_theta_step = -std::log2(static_cast<double>(c.d->rope_base)) / (D / 6);
+  // tile rows
+  a.x = x_tiles;
+  a.x_rows = c.n_rows;
+  a.n_pad = L.n_pad;
+  a.q = ws_at<bf16>(c.ws, L.off_q);
+  a.k = ws_at<bf16>(c.ws, L.off_k);
+  a.vt = ws_at<bf16>(c.ws, L.off_vt);
+  hipLaunchKernelGGL((qkv_rope_kernel<TX, D, false>), dim3(static_cast<uint32_t>(L.npb), c.d->batch),
+                     dim3(kThreads), 0, stream, a);
+  if (c.d->n_audio > 0) {
+    a.x = x_audio;
+    a.x_rows = c.d->n_audio;
+    a.n_pad = L.a_pad;
+    a.q = ws_at<bf16>(c.ws, L.off_qa);
+    a.k = ws_at<bf16>(c.ws, L.off_ka);
+    a.vt = ws_at<bf16>(c.ws, L.off_vta);
+    hipLaunchKernelGGL((qkv_rope_kernel<TX, D, true>),
+                       dim3(static_cast<uint32_t>(L.a_pad / kRowPad), c.d->batch), dim3(kThreads),
+                       0, stream, a);
+  }
+}
+
+template <int D>
+void launch_core(const Call &c, hipStream_t stream) {
+  const Layout &L = c.L;
+  CoreArgs a{};
+  a.q = ws_at<bf16>(c.ws, L.off_q);
+  a.k = ws_at<bf16>(c.ws, L.off_k);
+  a.vt = ws_at<bf16>(c.ws, L.off_vt);
+  a.qa = ws_at<bf16>(c.ws, L.off_qa);
+  a.ka = ws_at<bf16>(c.ws, L.off_ka);
+  a.vta = ws_at<bf16>(c.ws, L.off_vta);
+  a.o = ws_at<bf16>(c.ws, L.off_o);
+  a.oa = ws_at<bf16>(c.ws, L.off_oa);
+  a.blk_tile = ws_at<int32_t>(c.ws, L.off_blk_tile);
+  a.blk_q0 = ws_at<int32_t>(c.ws, L.off_blk_q0);
+  a.pad_begin = ws_at<int32_t>(c.ws, L.off_pad_begin);
+  a.trb = c.trb;
+  a.npb = L.npb;
+  a.n_pad = L.n_pad;
+  a.a_pad = L.a_pad;
+  a.n_rows = c.n_rows;
+  a.units_per_bh = L.npb + static_cast<int64_t>(c.n_tiles) * L.n_aqb;
+  a.total_units = a.units_per_bh * c.d->batch * c.d->heads;
+  a.T = c.n_tiles;
+  a.heads = c.d->heads;
+  a.batch = c.d->batch;
+  a.A = c.d->n_audio;
+  a.n_aqb = L.n_aqb;
+  a.max_rows = c.max_rows;
+  a.hidden = L.hidden;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+  const int64_t grid = ceil_div(a.total_units, 8) * 8;
+  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
+                     stream, a);
+}
+
+}  // namespace
+
+extern "C" tdp_status tdp_attn_qkv_rope(const tdp_attn_desc *desc, int32_t n_tiles,
+                                        const int64_t *tile_row_begin, int32_t max_tile_rows,
+                                        int64_t n_rows, const void *x_tiles, const float *row_pos,
+                                        const void *x_audio, void *workspace,
+                                        size_t workspace_bytes, void *hip_stream) {
+  Call c{desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace, workspace_bytes, {}};
+  const tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  if (!x_tiles || !row_pos || (desc->n_audio > 0 && !x_audio)) return TDP_ERR_NULL;
+  if (!aligned16(x_tiles) || (desc->n_audio > 0 && !aligned16(x_audio))) return TDP_ERR_ALIGN;
+  if (c.L.npb > INT32_MAX) return TDP_ERR_ARG;
+  const hipStream_t stream = as_stream(hip_stream);
+  const bool f32 = desc->x_dtype == TDP_F32;
+  if (desc->head_dim == 64) {
+    if (f32) launch_qkv<float, 64>(c, x_tiles, row_pos, x_audio, stream);
+    else launch_qkv<bf16, 64>(c, x_tiles, row_pos, x_audio, stream);
+  } else {
+    if (f32) launch_qkv<float, 128>(c, x_tiles, row_pos, x_audio, stream);
+    else launch_qkv<bf16, 128>(c, x_tiles, row_pos, x_audio, stream);
+  }
+  return launch_status();
+}
+
+extern "C" tdp_status tdp_attn_core(const tdp_attn_desc *desc, int32_t n_tiles,
+                                    const int64_t *tile_row_begin, int32_t max_tile_rows,
+                                    int64_t n_rows, void *workspace, size_t workspace_bytes,
+                                    void *hip_stream) {
+  Call c{desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace, workspace_bytes, {}};
+  const tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  const int64_t units = (c.L.npb + static_cast<int64_t>(n_tiles) * c.L.n_aqb) * desc->batch * desc->heads;
+  if (ceil_div(units, 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
+  const hipStream_t stream = as_stream(hip_stream);
+  if (desc->head_dim == 64) launch_core<64>(c, stream);
+  else launch_core<128>(c, stream);
+  return launch_status();
+}
+
+extern "C" tdp_status tdp_attn_out_proj(const tdp_attn_desc *desc, int32_t n_tiles,
+                                        const int64_t *tile_row_begin, int32_t max_tile_rows,
+                                        int64_t n_rows, void *y_tiles, float *y_audio_tiles,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *hip_stream) {
+  Call c{desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace, workspace_bytes, {}};
+  tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  if (!y_tiles || (desc->n_audio > 0 && !y_audio_tiles)) return TDP_ERR_NULL;
+  if (!aligned16(y_tiles) || (desc->n_audio > 0 && !aligned16(y_audio_tiles))) return TDP_ERR_ALIGN;
+  const Layout &L = c.L;
+  const hipStream_t stream = as_stream(hip_stream);
+  const bf16 *wot = ws_at<bf16>(workspace, L.off_wot);
+  const int64_t M = static_cast<int64_t>(desc->batch) * n_rows;
+  if (ceil_div(M, 128) > INT32_MAX) return TDP_ERR_ARG;
+  const dim3 grid(static_cast<uint32_t>(ceil_div(M, 128)));
+  if (desc->y_dtype == TDP_F32) {
+    hipLaunchKernelGGL(out_proj_kernel<float>, grid, dim3(kThreads), 0, stream,
+                       ws_at<bf16>(workspace, L.off_o), wot, static_cast<float *>(y_tiles), M,
+                       L.hidden);
+  } else {
+    hipLaunchKernelGGL(out_proj_kernel<bf16>, grid, dim3(kThreads), 0, stream,
+                       ws_at<bf16>(workspace, L.off_o), wot, static_cast<bf16 *>(y_tiles), M,
+                       L.hidden);
+  }
+  if ((s = launch_status()) != TDP_OK) return s;
+  if (desc->n_audio > 0) {
+    const int64_t Ma = static_cast<int64_t>(n_tiles) * desc->batch * desc->n_audio;
+    hipLaunchKernelGGL(out_proj_kernel<float>, dim3(static_cast<uint32_t>(ceil_div(Ma, 128))),
+                       dim3(kThreads), 0, stream, ws_at<bf16>(workspace, L.off_oa), wot,
+                       y_audio_tiles, Ma, L.hidden);
+    s = launch_status();
+  }
+  return s;
+}
+
+extern "C" tdp_status tdp_tile_attention(const tdp_attn_desc *desc, int32_t n_tiles,
+                                         const int64_t *tile_row_begin, int32_t max_tile_rows,
+                                         int64_t n_rows, const void *x_tiles,
+                                         const float *row_pos, const void *wq, const void *wk,
+                                         const void *wv, const void *wo, const void *x_audio,
+                                         void *y_tiles, float *y_audio_tiles, void *workspace,
+                                         size_t workspace_bytes, void *hip_stream) {
+  // Validate every argument before the first launch.
+  Call c{desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace, workspace_bytes, {}};
+  tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  if (!x_tiles || !row_pos || !wq || !wk || !wv || !wo || !y_tiles ||
+      (desc->n_audio > 0 && (!x_audio || !y_audio_tiles)))
+    return TDP_ERR_NULL;
+  s = tdp_attn_prepare(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, wq, wk, wv, wo,
+                       workspace, workspace_bytes, hip_stream);
+  if (s != TDP_OK) return s;
+  s = tdp_attn_qkv_rope(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_tiles, row_pos,
+                        x_audio, workspace, workspace_bytes, hip_stream);
+  if (s != TDP_OK) return s;
+  s = tdp_attn_core(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace,
+                    workspace_bytes, hip_stream);
+  if (s != TDP_OK) return s;
+  return tdp_attn_out_proj(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, y_tiles,
+                           y_audio_tiles, workspace, workspace_bytes, hip_stream);
+}

@@ -1,0 +1,306 @@
+"""ctypes binding of libtdp.so, one Python function per C entry point.
+
+Argument marshalling only: every step of the path runs in the library.  Device
+buffers are torch tensors on the GPU (their ``data_ptr()`` is passed); the
+stream is torch's current stream unless one is given.  A non-zero status from
+the library raises ``TdpError``.  If the library has not been built the first
+call raises ``RuntimeError``: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+import re
+from typing import Optional
+
+import numpy as np
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtdp.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "tdp.h")
+
+TDP_F32, TDP_BF16 = 0, 1
+STATUS = {0: "TDP_OK", -1: "TDP_ERR_NULL", -2: "TDP_ERR_ARG", -3: "TDP_ERR_SHAPE",
+          -4: "TDP_ERR_UNSUPPORTED", -5: "TDP_ERR_BUFFER", -6: "TDP_ERR_HIP",
+          -7: "TDP_ERR_ALIGN"}
+
+
+class TdpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class DimTiling(C.Structure):
+    _fields_ = [("num_tiles", C.c_int32), ("overlap", C.c_int32)]
+
+
+class PlanDesc(C.Structure):
+    _fields_ = [("grid", C.c_int32 * 3), ("tiling", DimTiling * 3), ("n_cond", C.c_int32),
+                ("cond_pos", C.POINTER(C.c_float)), ("normalize_positions", C.c_int32),
+                ("world_size", C.c_int32), ("rank", C.c_int32)]
+
+
+class PlanSizes(C.Structure):
+    _fields_ = [("n_tiles_total", C.c_int32), ("n_tiles_local", C.c_int32),
+                ("max_tile_rows", C.c_int32), ("n_gen_total", C.c_int32),
+                ("n_rows", C.c_int64), ("n_dst_rows", C.c_int64)]
+
+
+class PlanOut(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "tile_id", "tile_box", "tile_offset", "tile_row_begin", "tile_n_gen", "row_src",
+        "row_weight", "row_pos", "cond_keep_count", "dst_row_begin", "dst_rows")]
+
+
+class AttnDesc(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("C", C.c_int32), ("heads", C.c_int32),
+                ("head_dim", C.c_int32), ("n_audio", C.c_int32), ("x_dtype", C.c_int32),
+                ("y_dtype", C.c_int32), ("rope_base", C.c_float)]
+
+
+_P, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_SIGS = {
+    "tdp_status_string": (C.c_char_p, [_I32]),
+    "tdp_plan_query": (_I32, [C.POINTER(PlanDesc), C.POINTER(PlanSizes)]),
+    "tdp_plan": (_I32, [C.POINTER(PlanDesc), C.POINTER(PlanSizes), C.POINTER(PlanOut)]),
+    "tdp_gather_tiles": (_I32, [_P, _I32, _I32, _I64, _I32, _P, _I64, _P, _P]),
+    "tdp_tile_attention_workspace": (_I32, [C.POINTER(AttnDesc), _I32, _I64, C.POINTER(_SZ)]),
+    "tdp_tile_attention": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P, _P,
+                                  _P, _P, _P, _P, _P, _SZ, _P]),
+    "tdp_attn_prepare": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P, _P,
+                                _SZ, _P]),
+    "tdp_attn_qkv_rope": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P, _SZ,
+                                 _P]),
+    "tdp_attn_core": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _SZ, _P]),
+    "tdp_attn_out_proj": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _SZ,
+                                 _P]),
+    "tdp_blend_accumulate": (_I32, [_P, _I32, _I32, _I64, _I32, _P, _P, _P, _I64, _P, _I32, _P]),
+    "tdp_audio_accumulate": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Function names declared in include/tdp.h."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tdp_[a-z_0-9]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().tdp_status_string(int(status)).decode()
+
+
+def tdp_status_string(status: int) -> str:
+    return status_string(status)
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise TdpError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# plan (host)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Plan:
+    sizes: dict
+    tile_id: np.ndarray
+    tile_box: np.ndarray
+    tile_offset: np.ndarray
+    tile_row_begin: np.ndarray
+    tile_n_gen: np.ndarray
+    row_src: np.ndarray
+    row_weight: np.ndarray
+    row_pos: np.ndarray
+    cond_keep_count: np.ndarray
+    dst_row_begin: np.ndarray
+    dst_rows: np.ndarray
+
+    @property
+    def n_rows(self) -> int:
+        return int(self.sizes["n_rows"])
+
+    @property
+    def n_tiles_local(self) -> int:
+        return int(self.sizes["n_tiles_local"])
+
+    @property
+    def n_tiles_total(self) -> int:
+        return int(self.sizes["n_tiles_total"])
+
+    @property
+    def max_tile_rows(self) -> int:
+        return int(self.sizes["max_tile_rows"])
+
+    @property
+    def n_dst_rows(self) -> int:
+        return int(self.sizes["n_dst_rows"])
+
+
+def _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank):
+    d = PlanDesc()
+    for i in range(3):
+        d.grid[i] = int(grid[i])
+        d.tiling[i].num_tiles = int(tiling[i][0])
+        d.tiling[i].overlap = int(tiling[i][1])
+    keep = None
+    if cond_pos is not None and len(cond_pos) > 0:
+        keep = np.ascontiguousarray(cond_pos, dtype=np.float32).reshape(-1, 3, 2)
+        d.n_cond = keep.shape[0]
+        d.cond_pos = keep.ctypes.data_as(C.POINTER(C.c_float))
+    d.normalize_positions = int(bool(normalize_positions))
+    d.world_size = int(world_size)
+    d.rank = int(rank)
+    return d, keep
+
+
+def tdp_plan_query(grid, tiling, cond_pos=None, normalize_positions=True, world_size=1,
+                   rank=0) -> dict:
+    d, _keep = _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank)
+    s = PlanSizes()
+    _check(lib().tdp_plan_query(C.byref(d), C.byref(s)), "tdp_plan_query")
+    return {f: getattr(s, f) for f, _ in PlanSizes._fields_}
+
+
+def tdp_plan(grid, tiling, cond_pos=None, normalize_positions=True, world_size=1,
+             rank=0) -> Plan:
+    """Query sizes, allocate the host arrays and fill them (host only)."""
+    d, _keep = _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank)
+    s = PlanSizes()
+    _check(lib().tdp_plan_query(C.byref(d), C.byref(s)), "tdp_plan_query")
+    T, R, M = s.n_tiles_local, s.n_rows, d.n_cond
+    arrs = dict(
+        tile_id=np.zeros(T, np.int32), tile_box=np.zeros((T, 3, 2), np.int32),
+        tile_offset=np.zeros((T, 3), np.float32), tile_row_begin=np.zeros(T + 1, np.int64),
+        tile_n_gen=np.zeros(T, np.int32), row_src=np.zeros(R, np.int32),
+        row_weight=np.zeros(R, np.float32), row_pos=np.zeros((R, 3, 2), np.float32),
+        cond_keep_count=np.zeros(max(M, 1), np.int32),
+        dst_row_begin=np.zeros(s.n_dst_rows + 1, np.int64), dst_rows=np.zeros(max(R, 1), np.int32))
+    out = PlanOut(**{k: v.ctypes.data for k, v in arrs.items()})
+    _check(lib().tdp_plan(C.byref(d), C.byref(s), C.byref(out)), "tdp_plan")
+    arrs["cond_keep_count"] = arrs["cond_keep_count"][:M]
+    arrs["dst_rows"] = arrs["dst_rows"][:R]
+    return Plan(sizes={f: getattr(s, f) for f, _ in PlanSizes._fields_}, **arrs)
+
+
+# ---------------------------------------------------------------------------
+# device calls
+# ---------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return TDP_F32
+    if t.dtype == torch.bfloat16:
+        return TDP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def tdp_gather_tiles(x_global, dtype, batch, n_src_rows, C_, row_src, n_rows, x_tiles,
+                     stream=None) -> None:
+    _check(lib().tdp_gather_tiles(_ptr(x_global), dtype, batch, n_src_rows, C_, _ptr(row_src),
+                                  n_rows, _ptr(x_tiles), _stream(stream)), "tdp_gather_tiles")
+
+
+def attn_desc(batch, C_, heads, head_dim, n_audio, x_dtype, y_dtype, rope_base=10000.0):
+    return AttnDesc(batch, C_, heads, head_dim, n_audio, x_dtype, y_dtype, rope_base)
+
+
+def tdp_tile_attention_workspace(desc: AttnDesc, n_tiles, n_rows) -> int:
+    n = C.c_size_t()
+    _check(lib().tdp_tile_attention_workspace(C.byref(desc), n_tiles, n_rows, C.byref(n)),
+           "tdp_tile_attention_workspace")
+    return n.value
+
+
+def tdp_tile_attention(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_tiles, row_pos,
+                       wq, wk, wv, wo, x_audio, y_tiles, y_audio_tiles, workspace,
+                       workspace_bytes, stream=None) -> None:
+    _check(lib().tdp_tile_attention(
+        C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows, n_rows, _ptr(x_tiles),
+        _ptr(row_pos), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(x_audio), _ptr(y_tiles),
+        _ptr(y_audio_tiles), _ptr(workspace), workspace_bytes, _stream(stream)),
+        "tdp_tile_attention")
+
+
+def tdp_attn_prepare(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, wq, wk, wv, wo,
+                     workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().tdp_attn_prepare(C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows,
+                                  n_rows, _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo),
+                                  _ptr(workspace), workspace_bytes, _stream(stream)),
+           "tdp_attn_prepare")
+
+
+def tdp_attn_qkv_rope(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_tiles, row_pos,
+                      x_audio, workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().tdp_attn_qkv_rope(C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows,
+                                   n_rows, _ptr(x_tiles), _ptr(row_pos), _ptr(x_audio),
+                                   _ptr(workspace), workspace_bytes, _stream(stream)),
+           "tdp_attn_qkv_rope")
+
+
+def tdp_attn_core(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace,
+                  workspace_bytes, stream=None) -> None:
+    _check(lib().tdp_attn_core(C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows,
+                               n_rows, _ptr(workspace), workspace_bytes, _stream(stream)),
+           "tdp_attn_core")
+
+
+def tdp_attn_out_proj(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, y_tiles,
+                      y_audio_tiles, workspace, workspace_bytes, stream=None) -> None:
+    _check(lib().tdp_attn_out_proj(C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows,
+                                   n_rows, _ptr(y_tiles), _ptr(y_audio_tiles), _ptr(workspace),
+                                   workspace_bytes, _stream(stream)), "tdp_attn_out_proj")
+
+
+def tdp_blend_accumulate(y_tiles, dtype, batch, n_rows, C_, dst_row_begin, dst_rows, row_weight,
+                         n_dst_rows, y_global, accumulate, stream=None) -> None:
+    _check(lib().tdp_blend_accumulate(_ptr(y_tiles), dtype, batch, n_rows, C_,
+                                      _ptr(dst_row_begin), _ptr(dst_rows), _ptr(row_weight),
+                                      n_dst_rows, _ptr(y_global), int(accumulate),
+                                      _stream(stream)), "tdp_blend_accumulate")
+
+
+def tdp_audio_accumulate(y_audio_tiles, n_tiles_local, n_tiles_total, batch, n_audio, C_,
+                         y_audio, accumulate, stream=None) -> None:
+    _check(lib().tdp_audio_accumulate(_ptr(y_audio_tiles), n_tiles_local, n_tiles_total, batch,
+                                      n_audio, C_, _ptr(y_audio), int(accumulate),
+                                      _stream(stream)), "tdp_audio_accumulate")
