@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of one TDP upscale step on one MI355X (gfx950).
+
+A step is one pass of the device hot path over one batch of synthetic input:
+gather of tile rows -> per-tile attention (QKV + 3D RoPE, flash attention,
+output projection) -> blend into the global latent -> audio average.  The host
+plan (tiles, masks, positions, keep rule) is computed once per shape, outside
+the timed region, and reported as ``plan_ms``.
+
+Default workload: the 16-tile step (latent 16x64x64, 128 channels, 4x4 tiles
+with overlap 8, 32 heads x 128, bf16).  Prints ONE JSON line.
+
+  value        latent tokens/s = B*N / (wall time per step)
+  roofline     the attention core kernel (dominant): algorithmic flops
+               sum over (tile, batch, head) of 4*d*n_t^2, divided by its mean
+               launch time from HIP events on the launch stream, against the
+               dense bf16 MFMA peak
+  blend_stress gather and blend alone on the 32x96x160 fp32 latent
+               (6x10 tiles, overlap 16, identity denoiser), algorithmic bytes
+               per launch over mean launch time, against 8 TB/s
+  cpu_baseline the CPU oracle (float64 NumPy) on a bounded sample of the same
+               step, scaled to a whole step by attention flops
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def attn_flops(plan, wl) -> float:
+    import numpy as np
+    n = np.diff(plan.tile_row_begin).astype(np.float64) + wl.n_audio
+    return float(4.0 * wl.head_dim * wl.heads * wl.batch * np.sum(n * n))
+
+
+def gather_bytes(plan, wl) -> float:
+    es = 2 if wl.latent_dtype == "bf16" else 4
+    return 2.0 * wl.batch * plan.n_rows * wl.channels * es + 4.0 * plan.n_rows
+
+
+def blend_bytes(plan, wl) -> float:
+    es = 2 if wl.latent_dtype == "bf16" else 4
+    rows = plan.n_rows
+    return (wl.batch * rows * wl.channels * es          # y_tiles read
+            + wl.batch * plan.n_dst_rows * wl.channels * 4  # y_global written
+            + 4.0 * rows + 4.0 * rows                    # dst_rows, row_weight
+            + 8.0 * (plan.n_dst_rows + 1))               # dst_row_begin
+
+
+def cpu_baseline(inp, plan, budget_s: float = 15.0) -> dict:
+    """Time the oracle on whole tiles until the budget is spent; scale by flops."""
+    import numpy as np
+    import oracle
+    wl = inp.workload
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        if info:
+            threads = max(int(i.get("num_threads", 0)) for i in info)
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    x_tiles = oracle.gather_tiles(inp.x_global, p)
+    t_plan_gather = time.perf_counter() - t0
+    order = np.argsort(np.diff(p.tile_row_begin))           # smallest tiles first
+    done_flops, t_tiles, n_tiles = 0.0, 0.0, 0
+    y_tiles = np.zeros(x_tiles.shape, dtype=np.float64)
+    for t in order:
+        r0, r1 = int(p.tile_row_begin[t]), int(p.tile_row_begin[t + 1])
+        t1 = time.perf_counter()
+        for b in range(wl.batch):
+            xa = None if inp.x_aud is None else inp.x_aud[b]
+            y, _ = oracle.tile_forward(x_tiles[b, r0:r1], p.row_pos[r0:r1], xa, inp.wq, inp.wk,
+                                       inp.wv, inp.wo, wl.heads, wl.head_dim)
+            y_tiles[b, r0:r1] = y
+        t_tiles += time.perf_counter() - t1
+        n = (r1 - r0) + wl.n_audio
+        done_flops += 4.0 * wl.head_dim * wl.heads * wl.batch * n * n
+        n_tiles += 1
+        if t_tiles >= budget_s:
+            break
+    t1 = time.perf_counter()
+    oracle.blend_tiles(y_tiles, p)
+    t_blend = time.perf_counter() - t1
+    total_flops = attn_flops(plan, wl)
+    est = t_plan_gather + t_blend + t_tiles * total_flops / done_flops
+    tokens = wl.batch * wl.n_gen
+    return {"value": tokens / est, "unit": "latent tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"float64 NumPy oracle: plan + gather + blend of the whole step, "
+                       f"denoiser on {n_tiles} of {p.tile_id.size} tiles "
+                       f"({t_tiles:.1f} s), scaled to the step by attention flops; "
+                       f"estimated {est:.1f} s per step")}
+
+
+def run(args) -> dict:
+    import numpy as np
+    import torch
+
+    import tdp_inputs as ti
+    from tiled_video_diffusion_amd import tdp
+    from tiled_video_diffusion_amd.step import TdpStep
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    torch.cuda.set_device(0)
+    inp = ti.make_inputs(args.workload)
+    wl = inp.workload
+    t0 = time.perf_counter()
+    tdp.tdp_plan(wl.grid, wl.tiling, inp.cond_pos)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    step = TdpStep(inp)
+    p = step.plan
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+
+    names = ["gather", "prepare", "qkv", "core", "out", "blend", "audio"]
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)] for n in names}
+
+    def stage(i, name, fn):
+        ev[name][i][0].record(stream)
+        fn()
+        ev[name][i][1].record(stream)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        stage(i, "gather", step.gather)
+        if not step.identity:
+            stage(i, "prepare", step.attn_prepare)
+            stage(i, "qkv", step.attn_qkv)
+            stage(i, "core", step.attn_core)
+            stage(i, "out", step.attn_out)
+        stage(i, "blend", step.blend)
+        if step.n_audio:
+            stage(i, "audio", step.audio)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    def mean_ms(name):
+        vals = [a.elapsed_time(b) for a, b in ev[name]]
+        return float(np.mean(vals))
+
+    used = ["gather", "blend"] + ([] if step.identity else ["prepare", "qkv", "core", "out"]) + \
+        (["audio"] if step.n_audio else [])
+    stage_ms = {n: mean_ms(n) for n in used}
+    tokens = wl.batch * wl.n_gen
+    value = tokens / (ms_per_step * 1e-3)
+
+    flops = attn_flops(p, wl)
+    core_ms = stage_ms.get("core", float("nan"))
+    achieved = flops / (core_ms * 1e-3) / 1e12
+    roofline = {"kernel": "attn_core_kernel", "bound": "mfma", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "traffic": None, "flops_per_launch": flops, "ms_per_launch": core_ms}
+
+    # gather + blend stress, alone
+    bs = None
+    if not args.skip_blend_stress:
+        binp = ti.make_inputs("blend_32x96x160")
+        bstep = TdpStep(binp)
+        bwl = binp.workload
+        for _ in range(3):
+            bstep.run()
+        torch.cuda.synchronize()
+        nrep = 20
+        ge = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nrep)]
+        be = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nrep)]
+        for i in range(nrep):
+            ge[i][0].record(stream); bstep.gather(); ge[i][1].record(stream)
+            be[i][0].record(stream); bstep.blend(); be[i][1].record(stream)
+        torch.cuda.synchronize()
+        g_ms = float(np.mean([a.elapsed_time(b) for a, b in ge]))
+        b_ms = float(np.mean([a.elapsed_time(b) for a, b in be]))
+        gb = gather_bytes(bstep.plan, bwl) / (g_ms * 1e-3) / 1e9
+        bb = blend_bytes(bstep.plan, bwl) / (b_ms * 1e-3) / 1e9
+        bs = {"workload": "blend_32x96x160", "unit": "GB/s", "peak": PEAK_HBM_GBS,
+              "gather": {"achieved": gb, "frac": gb / PEAK_HBM_GBS, "ms_per_launch": g_ms,
+                         "bytes_per_launch": gather_bytes(bstep.plan, bwl)},
+              "blend": {"achieved": bb, "frac": bb / PEAK_HBM_GBS, "ms_per_launch": b_ms,
+                        "bytes_per_launch": blend_bytes(bstep.plan, bwl)}}
+        del bstep
+
+    out = {
+        "metric": "latent tokens/s per TDP step (1 GPU); attn MFMA %; blend HBM GB/s",
+        "value": value, "unit": "latent tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.latent_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "grid": list(wl.grid),
+                   "tiling": [list(t) for t in wl.tiling], "tiles": p.n_tiles_total,
+                   "batch": wl.batch, "channels": wl.channels, "heads": wl.heads,
+                   "head_dim": wl.head_dim, "n_cond": wl.n_cond, "n_audio": wl.n_audio,
+                   "rows": p.n_rows, "parallelism": "all tiles on one GPU"},
+        "roofline": roofline,
+        "stage_ms": stage_ms, "plan_ms": plan_ms,
+        "attn_mfma_frac_whole_attention": flops / (sum(stage_ms.get(n, 0.0) for n in
+                                                       ("prepare", "qkv", "core", "out")) * 1e-3)
+        / (PEAK_BF16_TFLOPS * 1e12) if not step.identity else None,
+        "blend_stress": bs,
+    }
+    if not args.skip_cpu_baseline:
+        del step
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(inp, p, args.cpu_budget)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="t16_16x64x64")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle denoiser work in the CPU baseline sample")
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-blend-stress", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the multi-GPU path of this build is design only", file=sys.stderr)
+        sys.exit(2)
+    print(json.dumps(run(args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()
