@@ -10,9 +10,9 @@
 //   prepare   W^T copies of the weights; a table mapping every 128-row block
 //             of the padded row space to (tile, first row).
 //   qkv_rope  Q, K (row-major per token) and V^T (keys contiguous) in bf16,
-//             RoPE applied to the fp32 accumulator; tiles padded to 128 rows
+//             RoPE applied to the fp32 accumulator; tiles padded to 256 rows
 //             with zero rows so every K/V block load is aligned and finite.
-//   core      flash attention per (batch, head, 128-query block): S^T = K Q^T
+//   core      flash attention per (batch, head, 256-query block): S^T = K Q^T
 //             and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16.  With keys on
 //             the MFMA rows, a lane holds one query's scores, so the online
 //             softmax needs one cross-half exchange per 64-key block, and P
@@ -26,21 +26,23 @@ namespace tdp {
 namespace {
 
 constexpr int kC = 128;       // channels per token row
-constexpr int kBM = 128;      // query rows per attention block (4 waves x 32)
+constexpr int kBlk = 128;     // rows per block of the padded row space (one QKV workgroup)
+constexpr int kQPW = 64;      // query rows per wave in the attention core (two groups of 32)
+constexpr int kUnit = 4 * kQPW;  // query rows per attention workgroup; tiles are padded to it
 constexpr int kBN = 64;       // keys per attention iteration
-constexpr int kRowPad = 128;  // tile rows are padded to a multiple of this
 constexpr int kThreads = 256;
-static_assert(kBM == kRowPad && kBM == 4 * 32, "a query block is one padded row block, 32 rows per wave");
+constexpr float kLazy = 8.0f; // log2 headroom before the running softmax max is moved
+static_assert(kUnit % kBlk == 0 && kUnit % kBN == 0, "tile padding covers whole blocks");
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Workspace layout (byte offsets, each 256-aligned).
 struct Layout {
-  int64_t npb = 0;    // 128-row blocks of the padded tile row space (upper bound)
+  int64_t npb = 0;    // 128-row blocks of the padded tile row space (upper bound, even)
   int64_t n_pad = 0;  // npb * 128 rows per (batch, head) slab
-  int64_t a_pad = 0;  // audio rows padded to 128
-  int32_t n_aqb = 0;  // 128-query audio blocks per tile
+  int64_t a_pad = 0;  // audio rows padded to 256
+  int32_t n_aqb = 0;  // 256-query audio units per tile
   int32_t hidden = 0;
   size_t off_wt = 0, off_wot = 0, off_pad_begin = 0, off_blk_tile = 0, off_blk_q0 = 0;
   size_t off_q = 0, off_k = 0, off_vt = 0, off_qa = 0, off_ka = 0, off_vta = 0;
@@ -60,10 +62,11 @@ tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, 
   const int64_t hidden = static_cast<int64_t>(d->heads) * d->head_dim;
   if (hidden > (1 << 16)) return TDP_ERR_UNSUPPORTED;
   L->hidden = static_cast<int32_t>(hidden);
-  L->npb = (n_rows + static_cast<int64_t>(kRowPad - 1) * n_tiles) / kRowPad;
-  L->n_pad = L->npb * kRowPad;
-  L->a_pad = ceil_div(d->n_audio, kRowPad) * kRowPad;
-  L->n_aqb = static_cast<int32_t>(L->a_pad / kRowPad);
+  // Each tile takes ceil(rows/256) units of 256 rows: at most (rows + 255)/256.
+  L->npb = (n_rows + static_cast<int64_t>(kUnit - 1) * n_tiles) / kUnit * (kUnit / kBlk);
+  L->n_pad = L->npb * kBlk;
+  L->a_pad = ceil_div(d->n_audio, kUnit) * kUnit;
+  L->n_aqb = static_cast<int32_t>(L->a_pad / kUnit);
   const size_t B = d->batch, H = d->heads, D = d->head_dim, T = n_tiles, A = d->n_audio;
   size_t off = 0;
   auto take = [&off](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
@@ -121,9 +124,10 @@ __device__ inline void tile_rows(const int64_t *trb, int32_t t, int64_t n_rows, 
   *len = static_cast<int32_t>(min(b - a, static_cast<int64_t>(max_rows)));
 }
 
-// pad_begin[t] = first 128-row block of tile t in the padded row space (clamped
-// to npb); blk_tile/blk_q0 map each block to its tile and first tile row (-1
-// for blocks past the last tile).  One workgroup.
+// pad_begin[t] = first 128-row block of tile t in the padded row space, where
+// each tile takes a whole number of 256-row units (clamped to npb);
+// blk_tile/blk_q0 map each block to its tile and first tile row (-1 for blocks
+// past the last tile).  One workgroup.
 __global__ __launch_bounds__(1024) void block_table_kernel(const int64_t *__restrict__ trb,
                                                            int32_t T, int64_t n_rows,
                                                            int32_t max_rows, int64_t npb,
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(1024) void block_table_kernel(const int64_t *__rest
     int64_t r0;
     int32_t len;
     tile_rows(trb, t, n_rows, max_rows, &r0, &len);
-    pad_begin[t + 1] = static_cast<int32_t>(ceil_div(len, kRowPad));
+    pad_begin[t + 1] = static_cast<int32_t>(ceil_div(len, kUnit) * (kUnit / kBlk));
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(1024) void block_table_kernel(const int64_t *__rest
         if (pad_begin[mid] <= pb) lo = mid; else hi = mid - 1;
       }
       tile = lo;
-      q0 = static_cast<int32_t>((pb - pad_begin[lo]) * kRowPad);
+      q0 = static_cast<int32_t>((pb - pad_begin[lo]) * kBlk);
     }
     blk_tile[pb] = tile;
     blk_q0[pb] = q0;
@@ -220,9 +224,9 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
   int64_t src0 = 0, pad_row0 = 0;
   int32_t nvalid = 0, tile = 0;
   if (AUDIO) {
-    src0 = pb * kRowPad;
-    pad_row0 = pb * kRowPad;
-    nvalid = static_cast<int32_t>(min(static_cast<int64_t>(kRowPad), a.x_rows - src0));
+    src0 = pb * kBlk;
+    pad_row0 = pb * kBlk;
+    nvalid = static_cast<int32_t>(min(static_cast<int64_t>(kBlk), a.x_rows - src0));
   } else {
     tile = a.blk_tile[pb];
     if (tile < 0) return;
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
     int32_t len;
     tile_rows(a.trb, tile, a.n_rows, a.max_rows, &r0, &len);
     src0 = r0 + q0;
-    pad_row0 = static_cast<int64_t>(a.pad_begin[tile]) * kRowPad + q0;
+    pad_row0 = static_cast<int64_t>(a.pad_begin[tile]) * kBlk + q0;
     nvalid = len - q0;
   }
   const int my = wave * 32 + l32;
@@ -337,7 +341,7 @@ struct CoreArgs {
   bf16 *o, *oa;
   const int32_t *blk_tile, *blk_q0, *pad_begin;
   const int64_t *trb;
-  int64_t npb, n_pad, a_pad, n_rows, units_per_bh, total_units;
+  int64_t n_units, n_pad, a_pad, n_rows, units_per_bh, total_units;
   int32_t T, heads, batch, A, n_aqb, max_rows, hidden;
   float scale_log2;           // log2(e) / sqrt(head_dim)
 };
@@ -390,59 +394,179 @@ struct KvStage {
   }
 };
 
-// Blocks are enumerated as (batch, head, unit) with the units of one (batch,
-// head) contiguous: first the 128-row blocks of every tile (tile order), then
-// the audio query blocks of every tile.  Hardware hands consecutive workgroup
-// ids to the 8 XCDs in turn; the id is remapped so each XCD walks a
-// contiguous range of units and the blocks sharing a tile's K/V run together
-// on one L2.
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// One 64-key block for the wave's NG groups of 32 queries.
+//  S^T[key][query] = K Q^T: keys on the MFMA rows, so lane l owns query l%32
+//  and 16 of the block's keys per 32-key tile; a K fragment read from LDS
+//  feeds every group.  Online softmax in the log2 domain with a lazily moved
+//  maximum: the running max only moves when a block max exceeds it by more
+//  than kLazy (p <= 2^kLazy otherwise), so the O rescale is rare.
+//  O^T[d][query] += V^T P^T: P stays in registers as the B operand; step
+//  (kt, u) covers keys 32 kt + 16 u + {4 hh + 0..3, 8 + 4 hh + 0..3}, exactly
+//  the keys held in s[kt][8u .. 8u+7], and the V^T fragment is read in the
+//  same key order.  Row sums add the bf16-rounded P that the MFMA consumes.
+//  Keys past the end of a segment (kvalid < 64) are the zero rows the QKV
+//  stage writes into the padding: their score is exactly 0 and their V row is
+//  0, so they change only the row sum, by exactly the bf16 weight of a zero
+//  score per padded key a lane holds, which is taken off again.  (The lazy max
+//  keeps that weight at most 2^kLazy.)
+template <int D, int NG>
+__device__ __forceinline__ void core_block(const bf16 *__restrict__ ks,
+                                           const bf16 *__restrict__ vs, int kvalid,
+                                           const bf16x8 (&qf)[NG][D / 16],
+                                           f32x16 (&o)[NG][D / 32], float (&m_run)[NG],
+                                           float (&l_run)[NG], float sl2, int l32, int hh) {
+  constexpr int kSteps = D / 16;
+  constexpr int kDT = D / 32;
+  constexpr int KR = CoreSmem<D>::kKRow, VR = CoreSmem<D>::kVRow;
+  f32x16 s[NG][2];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) s[g][kt] = f32x16{};
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + (32 * kt + l32) * KR + 16 * st + 8 * hh);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(kf, qf[g][st], s[g][kt]);
+    }
+  }
+  float mb[NG];
+  bool grow = false;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float mx = fmaxf(s[g][0][0], s[g][1][0]);
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s[g][0][v], s[g][1][v]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mb[g] = mx * sl2;
+    grow = grow || (mb[g] > m_run[g] + kLazy);
+  }
+  if (__builtin_expect(__ballot(grow) != 0, 0)) {
+    // Rare after the first block; the empty asm keeps this a real branch.
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const float m_new = fmaxf(m_run[g], mb[g]);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+#pragma unroll
+      for (int i = 0; i < kDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[g][i][v] *= alpha;
+      l_run[g] *= alpha;
+      m_run[g] = m_new;
+    }
+  }
+  bf16x8 pf[NG][2][2];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+    float lsum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[g][kt][v], sl2, -m_run[g]));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[g][kt][v + 1], sl2, -m_run[g]));
+        const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
+        pf[g][kt][v / 8][v % 8] = pp[0];
+        pf[g][kt][v / 8][v % 8 + 1] = pp[1];
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+      }
+    }
+    if (kvalid < kBN) {
+      // this lane's keys are 8 i + 4 hh + 0..3, i = 0..7
+      int n_zero = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) n_zero += min(max(8 * i + 4 * hh + 4 - kvalid, 0), 4);
+      const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_run[g])));
+      lsum -= static_cast<float>(n_zero) * pz;
+    }
+    l_run[g] += lsum;
+  }
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const bf16 *vp = vs + (32 * dt + l32) * VR + 32 * kt + 16 * uu + 4 * hh;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vp);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vp + 8);
+        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int g = 0; g < NG; ++g) o[g][dt] = mfma32(vf, pf[g][kt][uu], o[g][dt]);
+      }
+    }
+  }
+}
+
+// One workgroup = 4 waves x NG x 32 query rows of one (batch, head, tile)
+// against all keys of the tile, then the audio keys.  A 256-row unit of the
+// padded row space is split over 2/NG workgroups.  Work items of one (batch,
+// head) are contiguous: first the units of every tile (tile order), then the
+// audio query units of every tile.  Consecutive workgroup ids go to the 8
+// XCDs in turn; the id is remapped so each XCD walks a contiguous range of
+// work items and the workgroups sharing a tile's K/V run together on one L2.
+template <int D, int NG>
+__global__ __launch_bounds__(kThreads, 3 - NG) void attn_core_kernel(CoreArgs a) {
   __shared__ __attribute__((aligned(16))) CoreSmem<D> sm;
-  constexpr int kSteps = D / 16;   // MFMA k-steps over head_dim
-  constexpr int kDT = D / 32;      // 32-row tiles of O^T
+  constexpr int kSteps = D / 16;
+  constexpr int kDT = D / 32;
+  constexpr int kRowsWG = 4 * 32 * NG;        // query rows per workgroup
+  constexpr int kSplit = kUnit / kRowsWG;     // workgroups per 256-row unit
 
   const int64_t G = gridDim.x;
   const int64_t bid = blockIdx.x;
   const int64_t lid = (bid % 8) * (G / 8) + bid / 8;   // gridDim.x is a multiple of 8
-  if (lid >= a.total_units) return;
-  const int64_t bh = lid / a.units_per_bh;
-  const int64_t u = lid - bh * a.units_per_bh;
+  if (lid >= a.total_units * kSplit) return;
+  const int64_t item = lid / kSplit;
+  const int part = static_cast<int>(lid - item * kSplit);
+  const int64_t bh = item / a.units_per_bh;
+  const int64_t u = item - bh * a.units_per_bh;
   const int64_t b = bh / a.heads;
   const int h = static_cast<int>(bh - b * a.heads);
 
   int32_t t, q0;
   bool audio_q;
-  if (u < a.npb) {
-    t = a.blk_tile[u];
+  if (u < a.n_units) {
+    t = a.blk_tile[u * (kUnit / kBlk)];
     if (t < 0) return;
-    q0 = a.blk_q0[u];
+    q0 = a.blk_q0[u * (kUnit / kBlk)];
     audio_q = false;
   } else {
-    const int64_t ua = u - a.npb;
+    const int64_t ua = u - a.n_units;
     t = static_cast<int32_t>(ua / a.n_aqb);
-    q0 = static_cast<int32_t>((ua - static_cast<int64_t>(t) * a.n_aqb) * kRowPad);
+    q0 = static_cast<int32_t>((ua - static_cast<int64_t>(t) * a.n_aqb) * kUnit);
     audio_q = true;
   }
+  q0 += part * kRowsWG;
   int64_t r0;
   int32_t len0;
   tile_rows(a.trb, t, a.n_rows, a.max_rows, &r0, &len0);
-  const int64_t pad0 = static_cast<int64_t>(a.pad_begin[t]) * kRowPad;
+  const int64_t pad0 = static_cast<int64_t>(a.pad_begin[t]) * kBlk;
   len0 = static_cast<int32_t>(min(static_cast<int64_t>(len0),
-                                  static_cast<int64_t>(a.pad_begin[t + 1]) * kRowPad - pad0));
+                                  static_cast<int64_t>(a.pad_begin[t + 1]) * kBlk - pad0));
   const int32_t nq = audio_q ? (a.A - q0) : (len0 - q0);
   if (nq <= 0) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // Q fragments (B operand of S^T = K Q^T): query row wave*32 + l32.
+  // Q fragments (B operand of S^T = K Q^T): group g holds query row
+  // wave*32*NG + 32 g + l32.
   const bf16 *qsrc = audio_q ? a.qa + ((bh * a.a_pad) + q0) * D
                              : a.q + ((bh * a.n_pad) + pad0 + q0) * D;
-  bf16x8 qf[kSteps];
+  bf16x8 qf[NG][kSteps];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + (wave * 32 + l32) * D + 16 * s + 8 * hh);
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      qf[g][s] = *reinterpret_cast<const bf16x8 *>(qsrc + (wave * 32 * NG + 32 * g + l32) * D +
+                                                   16 * s + 8 * hh);
 
   const bf16 *kseg0 = a.k + (bh * a.n_pad + pad0) * D;
   const bf16 *vseg0 = a.vt + bh * D * a.n_pad + pad0;
@@ -452,10 +576,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
   const int nkb = nkb0 + static_cast<int>(ceil_div(a.A, kBN));
   if (nkb == 0) return;
 
-  f32x16 o[kDT];
+  f32x16 o[NG][kDT];
 #pragma unroll
-  for (int i = 0; i < kDT; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < kDT; ++i) o[g][i] = f32x16{};
+  float m_run[NG], l_run[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+  }
 
   KvStage<D> st;
   if (nkb0 > 0) st.load(kseg0, vseg0, a.n_pad, 0);
@@ -472,96 +603,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
       if (jn < nkb0) st.load(kseg0, vseg0, a.n_pad, jn * kBN);
       else st.load(kseg1, vseg1, a.a_pad, (jn - nkb0) * kBN);
     }
-
-    // S^T for keys [32 kt, 32 kt + 32) of the block, this wave's 32 queries.
-    f32x16 s[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = f32x16{};
-#pragma unroll
-      for (int st_ = 0; st_ < kSteps; ++st_) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(
-            &sm.k[buf][(32 * kt + l32) * CoreSmem<D>::kKRow + 16 * st_ + 8 * hh]);
-        s[kt] = mfma32(kf, qf[st_], s[kt]);
-      }
-    }
-    if (kvalid < kBN) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (32 * kt + 8 * (v / 4) + 4 * hh + (v % 4) >= kvalid) s[kt][v] = -INFINITY;
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f((m_run - m_new) * a.scale_log2);
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int i = 0; i < kDT; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      l_run *= alpha;
-    }
-    m_run = m_new;
-    const float mb = m_new * a.scale_log2;
-
-    // P (bf16) as the B operand of O^T += V^T P^T: step (kt, u) holds keys
-    // 32 kt + 16 u + {4 hh + 0..3, 8 + 4 hh + 0..3}, i.e. s[kt][8u .. 8u+7].
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(fmaf(s[kt][v], a.scale_log2, -mb));
-        l_run += p;
-        pf[kt][v / 8][v % 8] = static_cast<bf16>(p);
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int uu = 0; uu < 2; ++uu) {
-          const bf16 *vp = &sm.v[buf][(32 * dt + l32) * CoreSmem<D>::kVRow + 32 * kt + 16 * uu + 4 * hh];
-          const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vp);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vp + 8);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          o[dt] = mfma32(vf, pf[kt][uu], o[dt]);
-        }
-      }
-    }
+    core_block<D, NG>(sm.k[buf], sm.v[buf], kvalid, qf, o, m_run, l_run, a.scale_log2, l32, hh);
     if (j + 1 < nkb) st.store(sm, buf ^ 1);
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.0f / l_tot;
-  const int row = wave * 32 + l32;
-  if (row < nq) {
-    bf16 *dst = audio_q
-        ? a.oa + ((static_cast<int64_t>(t) * a.batch + b) * a.A + q0 + row) * a.hidden
-        : a.o + (b * a.n_rows + r0 + q0 + row) * a.hidden;
-    dst += h * D + 4 * hh;
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
+  for (int g = 0; g < NG; ++g) {
+    const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32);
+    const float inv = 1.0f / l_tot;
+    const int row = wave * 32 * NG + 32 * g + l32;
+    if (row < nq) {
+      bf16 *dst = audio_q
+          ? a.oa + ((static_cast<int64_t>(t) * a.batch + b) * a.A + q0 + row) * a.hidden
+          : a.o + (b * a.n_rows + r0 + q0 + row) * a.hidden;
+      dst += h * D + 4 * hh;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v4;
-        v4[0] = static_cast<bf16>(o[dt][4 * g + 0] * inv);
-        v4[1] = static_cast<bf16>(o[dt][4 * g + 1] * inv);
-        v4[2] = static_cast<bf16>(o[dt][4 * g + 2] * inv);
-        v4[3] = static_cast<bf16>(o[dt][4 * g + 3] * inv);
-        *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * g) = v4;
+      for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          bf16x4 v4;
+          v4[0] = static_cast<bf16>(o[g][dt][4 * gg + 0] * inv);
+          v4[1] = static_cast<bf16>(o[g][dt][4 * gg + 1] * inv);
+          v4[2] = static_cast<bf16>(o[g][dt][4 * gg + 2] * inv);
+          v4[3] = static_cast<bf16>(o[g][dt][4 * gg + 3] * inv);
+          *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * gg) = v4;
+        }
       }
     }
   }
 }
+
+#ifndef TDP_ATTN_GROUPS
+#define TDP_ATTN_GROUPS 1
+#endif
+constexpr int kAttnGroups = TDP_ATTN_GROUPS;   // query groups of 32 per wave
 
 // ---------------------------------------------------------------------------
 // out_proj
@@ -727,7 +803,7 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
     a.k = ws_at<bf16>(c.ws, L.off_ka);
     a.vt = ws_at<bf16>(c.ws, L.off_vta);
     hipLaunchKernelGGL((qkv_rope_kernel<TX, D, true>),
-                       dim3(static_cast<uint32_t>(L.a_pad / kRowPad), c.d->batch), dim3(kThreads),
+                       dim3(static_cast<uint32_t>(L.a_pad / kBlk), c.d->batch), dim3(kThreads),
                        0, stream, a);
   }
 }
@@ -748,11 +824,11 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.blk_q0 = ws_at<int32_t>(c.ws, L.off_blk_q0);
   a.pad_begin = ws_at<int32_t>(c.ws, L.off_pad_begin);
   a.trb = c.trb;
-  a.npb = L.npb;
+  a.n_units = L.npb / (kUnit / kBlk);
   a.n_pad = L.n_pad;
   a.a_pad = L.a_pad;
   a.n_rows = c.n_rows;
-  a.units_per_bh = L.npb + static_cast<int64_t>(c.n_tiles) * L.n_aqb;
+  a.units_per_bh = a.n_units + static_cast<int64_t>(c.n_tiles) * L.n_aqb;
   a.total_units = a.units_per_bh * c.d->batch * c.d->heads;
   a.T = c.n_tiles;
   a.heads = c.d->heads;
@@ -762,9 +838,9 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.max_rows = c.max_rows;
   a.hidden = L.hidden;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
-  const int64_t grid = ceil_div(a.total_units, 8) * 8;
-  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
-                     stream, a);
+  const int64_t grid = ceil_div(a.total_units * (kUnit / (4 * 32 * kAttnGroups)), 8) * 8;
+  hipLaunchKernelGGL((attn_core_kernel<D, kAttnGroups>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace
@@ -799,8 +875,9 @@ extern "C" tdp_status tdp_attn_core(const tdp_attn_desc *desc, int32_t n_tiles,
   Call c{desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, workspace, workspace_bytes, {}};
   const tdp_status s = check_call(&c);
   if (s != TDP_OK) return s;
-  const int64_t units = (c.L.npb + static_cast<int64_t>(n_tiles) * c.L.n_aqb) * desc->batch * desc->heads;
-  if (ceil_div(units, 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
+  const int64_t units = (c.L.npb / (kUnit / kBlk) + static_cast<int64_t>(n_tiles) * c.L.n_aqb) *
+                        desc->batch * desc->heads;
+  if (ceil_div(units * (kUnit / (4 * 32 * kAttnGroups)), 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
   const hipStream_t stream = as_stream(hip_stream);
   if (desc->head_dim == 64) launch_core<64>(c, stream);
   else launch_core<128>(c, stream);
