@@ -1,7 +1,8 @@
 """Build libtdp.so in-tree: host plan with g++, gfx950 kernels with hipcc.
 
 Every HIP source is compiled with packed-fp32 instructions disabled
-(``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host plan is
+(``-Xclang -target-feature -Xclang -packed-fp32-ops``) and, for the device
+pass only, without NaN semantics (``-fno-honor-nans``); the host plan is
 compiled with ``-ffp-contract=off`` so its float32 outputs are single IEEE
 operations.
 """
@@ -22,6 +23,9 @@ ARCH = "gfx950"
 
 HIP_FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # device code only: no NaN semantics, so max3 needs no canonicalizing moves
+             # (host-side argument checks keep their NaN tests)
+             "-Xarch_device", "-fno-honor-nans",
              "-I", INCLUDE, "-I", CSRC]
 CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-ffp-contract=off",
              "-I", INCLUDE]

@@ -27,8 +27,7 @@ namespace {
 
 constexpr int kC = 128;       // channels per token row
 constexpr int kBlk = 128;     // rows per block of the padded row space (one QKV workgroup)
-constexpr int kQPW = 64;      // query rows per wave in the attention core (two groups of 32)
-constexpr int kUnit = 4 * kQPW;  // query rows per attention workgroup; tiles are padded to it
+constexpr int kUnit = 256;    // tiles are padded to whole units of this many rows
 constexpr int kBN = 64;       // keys per attention iteration
 constexpr int kThreads = 256;
 constexpr float kLazy = 8.0f; // log2 headroom before the running softmax max is moved
@@ -354,141 +353,102 @@ struct CoreSmem {
   bf16 v[2][D * kVRow];
 };
 
-// Global -> register staging of one 64-key block (K rows and V^T columns).
+// This thread's 16-byte pieces of a 64-key block: K piece i is row
+// kr0 + i*kKRowsPer of the block at column kc; V^T piece i is head-dim row
+// vd0 + i*kVRowsPer at key column vc.
 template <int D>
-struct KvStage {
-  static constexpr int kKChunks = kBN * D / 8 / kThreads;   // 16-byte pieces per thread
-  static constexpr int kVChunks = D * kBN / 8 / kThreads;
-  bf16x8 kr[kKChunks];
-  bf16x8 vr[kVChunks];
-
-  __device__ void load(const bf16 *kseg, const bf16 *vseg, int64_t vstride, int k0) {
-#pragma unroll
-    for (int i = 0; i < kKChunks; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      kr[i] = *reinterpret_cast<const bf16x8 *>(kseg + static_cast<int64_t>(k0 + row) * D + col);
-    }
-#pragma unroll
-    for (int i = 0; i < kVChunks; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int d = c / (kBN / 8), col = (c % (kBN / 8)) * 8;
-      vr[i] = *reinterpret_cast<const bf16x8 *>(vseg + d * vstride + k0 + col);
-    }
+struct Pieces {
+  static constexpr int kN = kBN * D / 8 / kThreads;    // pieces per thread (K and V^T alike)
+  static constexpr int kKRowsPer = kThreads / (D / 8);  // K rows covered per piece index
+  static constexpr int kVRowsPer = kThreads / (kBN / 8);
+  int kr0, kc, vd0, vc;
+  __device__ Pieces() {
+    kr0 = threadIdx.x / (D / 8);
+    kc = (threadIdx.x % (D / 8)) * 8;
+    vd0 = threadIdx.x / (kBN / 8);
+    vc = (threadIdx.x % (kBN / 8)) * 8;
   }
-  __device__ void store(CoreSmem<D> &sm, int buf) const {
+  __device__ void load_k(const bf16 *kblk, bf16x8 (&r)[kN]) const {
 #pragma unroll
-    for (int i = 0; i < kKChunks; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      *reinterpret_cast<bf16x8 *>(&sm.k[buf][row * CoreSmem<D>::kKRow + col]) = kr[i];
-    }
+    for (int i = 0; i < kN; ++i)
+      r[i] = *reinterpret_cast<const bf16x8 *>(kblk + (kr0 + i * kKRowsPer) * D + kc);
+  }
+  __device__ void load_v(const bf16 *vblk, int32_t vstride, bf16x8 (&r)[kN]) const {
 #pragma unroll
-    for (int i = 0; i < kVChunks; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int d = c / (kBN / 8), col = (c % (kBN / 8)) * 8;
-      bf16 *p = &sm.v[buf][d * CoreSmem<D>::kVRow + col];
-      *reinterpret_cast<bf16x4 *>(p) = bf16x4{vr[i][0], vr[i][1], vr[i][2], vr[i][3]};
-      *reinterpret_cast<bf16x4 *>(p + 4) = bf16x4{vr[i][4], vr[i][5], vr[i][6], vr[i][7]};
+    for (int i = 0; i < kN; ++i)
+      r[i] = *reinterpret_cast<const bf16x8 *>(vblk + (vd0 + i * kVRowsPer) * vstride + vc);
+  }
+  __device__ void store_k(bf16 *ks, const bf16x8 (&r)[kN]) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i)
+      *reinterpret_cast<bf16x8 *>(ks + (kr0 + i * kKRowsPer) * CoreSmem<D>::kKRow + kc) = r[i];
+  }
+  __device__ void store_v(bf16 *vs, const bf16x8 (&r)[kN]) const {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) {
+      bf16 *p = vs + (vd0 + i * kVRowsPer) * CoreSmem<D>::kVRow + vc;
+      *reinterpret_cast<bf16x4 *>(p) = bf16x4{r[i][0], r[i][1], r[i][2], r[i][3]};
+      *reinterpret_cast<bf16x4 *>(p + 4) = bf16x4{r[i][4], r[i][5], r[i][6], r[i][7]};
     }
   }
 };
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// One 64-key block for the wave's NG groups of 32 queries.
-//  S^T[key][query] = K Q^T: keys on the MFMA rows, so lane l owns query l%32
-//  and 16 of the block's keys per 32-key tile; a K fragment read from LDS
-//  feeds every group.  Online softmax in the log2 domain with a lazily moved
-//  maximum: the running max only moves when a block max exceeds it by more
-//  than kLazy (p <= 2^kLazy otherwise), so the O rescale is rare.
-//  O^T[d][query] += V^T P^T: P stays in registers as the B operand; step
-//  (kt, u) covers keys 32 kt + 16 u + {4 hh + 0..3, 8 + 4 hh + 0..3}, exactly
-//  the keys held in s[kt][8u .. 8u+7], and the V^T fragment is read in the
-//  same key order.  Row sums add the bf16-rounded P that the MFMA consumes.
-//  Keys past the end of a segment (kvalid < 64) are the zero rows the QKV
-//  stage writes into the padding: their score is exactly 0 and their V row is
-//  0, so they change only the row sum, by exactly the bf16 weight of a zero
-//  score per padded key a lane holds, which is taken off again.  (The lazy max
-//  keeps that weight at most 2^kLazy.)
-template <int D, int NG>
-__device__ __forceinline__ void core_block(const bf16 *__restrict__ ks,
-                                           const bf16 *__restrict__ vs, int kvalid,
-                                           const bf16x8 (&qf)[NG][D / 16],
-                                           f32x16 (&o)[NG][D / 32], float (&m_run)[NG],
-                                           float (&l_run)[NG], float sl2, int l32, int hh) {
-  constexpr int kSteps = D / 16;
-  constexpr int kDT = D / 32;
-  constexpr int KR = CoreSmem<D>::kKRow, VR = CoreSmem<D>::kVRow;
-  f32x16 s[NG][2];
+// S^T[key][query] = K Q^T for one 64-key block: keys on the MFMA rows, so
+// lane l owns query l%32 and, in s[kt][v], key 32 kt + 8 (v/4) + 4 hh + v%4.
+template <int D>
+__device__ __forceinline__ void qk_block(const bf16 *__restrict__ ks, const bf16x8 (&qf)[D / 16],
+                                         f32x16 (&s)[2], int l32, int hh) {
+  constexpr int KR = CoreSmem<D>::kKRow;
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
+  for (int kt = 0; kt < 2; ++kt) {
+    s[kt] = f32x16{};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) s[g][kt] = f32x16{};
+    for (int st = 0; st < D / 16; ++st) {
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + (32 * kt + l32) * KR + 16 * st + 8 * hh);
+      s[kt] = mfma32(kf, qf[st], s[kt]);
+    }
+  }
+}
+
+// Largest score of the block for this lane's query (both half-waves).
+__device__ __forceinline__ float block_max(const f32x16 (&s)[2]) {
+  float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s[0][v], s[1][v]));
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// P = 2^(s*sl2 - m) rounded to bf16 and packed as the B operands of
+// O^T += V^T P^T; step (kt, u) holds keys 32 kt + 16 u + {4 hh + 0..3,
+// 8 + 4 hh + 0..3} = s[kt][8u .. 8u+7].  Returns the sum of the bf16 values.
+__device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], float sl2, float m,
+                                          bf16x8 (&pf)[2][2]) {
+  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+  float lsum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + (32 * kt + l32) * KR + 16 * st + 8 * hh);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(kf, qf[g][st], s[g][kt]);
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][v], sl2, -m));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][v + 1], sl2, -m));
+      const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
+      pf[kt][v / 8][v % 8] = pp[0];
+      pf[kt][v / 8][v % 8 + 1] = pp[1];
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
     }
   }
-  float mb[NG];
-  bool grow = false;
+  return lsum;
+}
+
+// O^T[d][query] += V^T P^T; the V^T fragment is read in the key order of P.
+template <int D>
+__device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs, const bf16x8 (&pf)[2][2],
+                                         f32x16 (&o)[D / 32], int l32, int hh) {
+  constexpr int VR = CoreSmem<D>::kVRow;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    float mx = fmaxf(s[g][0][0], s[g][1][0]);
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s[g][0][v], s[g][1][v]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    mb[g] = mx * sl2;
-    grow = grow || (mb[g] > m_run[g] + kLazy);
-  }
-  if (__builtin_expect(__ballot(grow) != 0, 0)) {
-    // Rare after the first block; the empty asm keeps this a real branch.
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const float m_new = fmaxf(m_run[g], mb[g]);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-#pragma unroll
-      for (int i = 0; i < kDT; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[g][i][v] *= alpha;
-      l_run[g] *= alpha;
-      m_run[g] = m_new;
-    }
-  }
-  bf16x8 pf[NG][2][2];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
-    float lsum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[g][kt][v], sl2, -m_run[g]));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[g][kt][v + 1], sl2, -m_run[g]));
-        const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
-        pf[g][kt][v / 8][v % 8] = pp[0];
-        pf[g][kt][v / 8][v % 8 + 1] = pp[1];
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-      }
-    }
-    if (kvalid < kBN) {
-      // this lane's keys are 8 i + 4 hh + 0..3, i = 0..7
-      int n_zero = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) n_zero += min(max(8 * i + 4 * hh + 4 - kvalid, 0), 4);
-      const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_run[g])));
-      lsum -= static_cast<float>(n_zero) * pz;
-    }
-    l_run[g] += lsum;
-  }
-#pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) {
+  for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -497,27 +457,49 @@ __device__ __forceinline__ void core_block(const bf16 *__restrict__ ks,
         const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vp);
         const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vp + 8);
         const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int g = 0; g < NG; ++g) o[g][dt] = mfma32(vf, pf[g][kt][uu], o[g][dt]);
+        o[dt] = mfma32(vf, pf[kt][uu], o[dt]);
       }
     }
   }
 }
 
-// One workgroup = 4 waves x NG x 32 query rows of one (batch, head, tile)
-// against all keys of the tile, then the audio keys.  A 256-row unit of the
-// padded row space is split over 2/NG workgroups.  Work items of one (batch,
-// head) are contiguous: first the units of every tile (tile order), then the
-// audio query units of every tile.  Consecutive workgroup ids go to the 8
-// XCDs in turn; the id is remapped so each XCD walks a contiguous range of
-// work items and the workgroups sharing a tile's K/V run together on one L2.
-template <int D, int NG>
-__global__ __launch_bounds__(kThreads, 3 - NG) void attn_core_kernel(CoreArgs a) {
+// Keys >= kvalid among this lane's keys of a block (8 i + 4 hh + 0..3).
+__device__ __forceinline__ int padded_keys(int kvalid, int hh) {
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) n += min(max(8 * i + 4 * hh + 4 - kvalid, 0), 4);
+  return n;
+}
+
+// One workgroup = 128 query rows (4 waves x 32) of one (batch, head, tile)
+// against all keys of the tile, then the audio keys; a 256-row unit of the
+// padded row space is split over two workgroups.
+//
+// Per 64-key block j the wave (1) takes the block max of S(j) and moves the
+// running max lazily (only when a block max exceeds it by more than kLazy,
+// so p <= 2^kLazy; the O rescale is rare and sits on a real branch),
+// (2) issues the HBM loads of K(j+2) and V(j+1), (3) computes S(j+1) on MFMA
+// while the VALU turns S(j) into bf16 P, (4) accumulates O += V(j) P(j), and
+// (5) stores the loaded blocks into the LDS buffers freed in block j-1.  K is
+// staged one block ahead of V, so two K and two V buffers suffice.
+//
+// Keys past the end of a segment are the zero rows the QKV stage writes into
+// the padding: score exactly 0, V row 0.  They only add the bf16 weight of a
+// zero score to the row sum, once per padded key a lane holds, which is
+// taken off again.
+//
+// Work items of one (batch, head) are contiguous: the units of every tile in
+// tile order, then the audio query units of every tile.  Consecutive
+// workgroup ids go to the 8 XCDs in turn; the id is remapped so each XCD
+// walks a contiguous range of work items and the workgroups sharing a tile's
+// K/V run together on one L2.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
   __shared__ __attribute__((aligned(16))) CoreSmem<D> sm;
   constexpr int kSteps = D / 16;
   constexpr int kDT = D / 32;
-  constexpr int kRowsWG = 4 * 32 * NG;        // query rows per workgroup
-  constexpr int kSplit = kUnit / kRowsWG;     // workgroups per 256-row unit
+  constexpr int kRowsWG = 4 * 32;              // query rows per workgroup
+  constexpr int kSplit = kUnit / kRowsWG;      // workgroups per 256-row unit
 
   const int64_t G = gridDim.x;
   const int64_t bid = blockIdx.x;
@@ -556,88 +538,126 @@ __global__ __launch_bounds__(kThreads, 3 - NG) void attn_core_kernel(CoreArgs a)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // Q fragments (B operand of S^T = K Q^T): group g holds query row
-  // wave*32*NG + 32 g + l32.
+  // Q fragments (B operand of S^T = K Q^T): query row wave*32 + l32.
   const bf16 *qsrc = audio_q ? a.qa + ((bh * a.a_pad) + q0) * D
                              : a.q + ((bh * a.n_pad) + pad0 + q0) * D;
-  bf16x8 qf[NG][kSteps];
+  bf16x8 qf[kSteps];
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s)
-      qf[g][s] = *reinterpret_cast<const bf16x8 *>(qsrc + (wave * 32 * NG + 32 * g + l32) * D +
-                                                   16 * s + 8 * hh);
+  for (int s = 0; s < kSteps; ++s)
+    qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + (wave * 32 + l32) * D + 16 * s + 8 * hh);
 
+  // Segment 0: the tile's rows; segment 1: the audio rows.
   const bf16 *kseg0 = a.k + (bh * a.n_pad + pad0) * D;
   const bf16 *vseg0 = a.vt + bh * D * a.n_pad + pad0;
   const bf16 *kseg1 = a.ka + bh * a.a_pad * D;
   const bf16 *vseg1 = a.vta + bh * D * a.a_pad;
+  const int32_t vstr0 = static_cast<int32_t>(a.n_pad), vstr1 = static_cast<int32_t>(a.a_pad);
   const int nkb0 = static_cast<int>(ceil_div(len0, kBN));
-  const int nkb = nkb0 + static_cast<int>(ceil_div(a.A, kBN));
+  const int nkb1 = static_cast<int>(ceil_div(a.A, kBN));
+  const int nkb = nkb0 + nkb1;
   if (nkb == 0) return;
+  // padded keys this lane holds in the last block of each segment
+  const int nz0 = nkb0 > 0 ? padded_keys(len0 - (nkb0 - 1) * kBN, hh) : 0;
+  const int nz1 = nkb1 > 0 ? padded_keys(a.A - (nkb1 - 1) * kBN, hh) : 0;
 
-  f32x16 o[NG][kDT];
+  const Pieces<D> pc;
+  bf16x8 kreg[Pieces<D>::kN], vreg[Pieces<D>::kN];
+  // Block j (clamped to the last block) of the tile-then-audio key sequence.
+  auto load_k = [&](int j) {
+    j = min(j, nkb - 1);
+    const bf16 *kb = j < nkb0 ? kseg0 + static_cast<int64_t>(j) * kBN * D
+                              : kseg1 + static_cast<int64_t>(j - nkb0) * kBN * D;
+    pc.load_k(kb, kreg);
+  };
+  auto load_v = [&](int j) {
+    j = min(j, nkb - 1);
+    const bool s0 = j < nkb0;
+    pc.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0 ? vstr0 : vstr1, vreg);
+  };
+
+  f32x16 o[kDT];
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int i = 0; i < kDT; ++i) o[g][i] = f32x16{};
-  float m_run[NG], l_run[NG];
-#pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
+  for (int i = 0; i < kDT; ++i) o[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  // prologue: K(0), V(0), K(1) into LDS; S(0)
+  load_k(0);
+  pc.store_k(sm.k[0], kreg);
+  load_v(0);
+  pc.store_v(sm.v[0], vreg);
+  if (nkb > 1) {
+    load_k(1);
+    pc.store_k(sm.k[1], kreg);
   }
-
-  KvStage<D> st;
-  if (nkb0 > 0) st.load(kseg0, vseg0, a.n_pad, 0);
-  else st.load(kseg1, vseg1, a.a_pad, 0);
-  st.store(sm, 0);
   __syncthreads();
+  f32x16 sa[2], sb[2];
+  qk_block<D>(sm.k[0], qf, sa, l32, hh);
 
-  for (int j = 0; j < nkb; ++j) {
-    const int buf = j & 1;
-    const bool seg1 = j >= nkb0;
-    const int kvalid = seg1 ? min(kBN, a.A - (j - nkb0) * kBN) : min(kBN, len0 - j * kBN);
-    if (j + 1 < nkb) {
-      const int jn = j + 1;
-      if (jn < nkb0) st.load(kseg0, vseg0, a.n_pad, jn * kBN);
-      else st.load(kseg1, vseg1, a.a_pad, (jn - nkb0) * kBN);
+  auto step = [&](int j, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+    const float mb = block_max(scur) * sl2;
+    if (__builtin_expect(__ballot(mb > m_run + kLazy) != 0, 0)) {
+      // Rare after the first block; the empty asm keeps this a real branch.
+      asm volatile("" ::: "memory");
+      const float m_new = fmaxf(m_run, mb);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int i = 0; i < kDT; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
     }
-    core_block<D, NG>(sm.k[buf], sm.v[buf], kvalid, qf, o, m_run, l_run, a.scale_log2, l32, hh);
-    if (j + 1 < nkb) st.store(sm, buf ^ 1);
+    // Loads and S(j+1) run unconditionally so they share one basic block with
+    // the exp below; past the last block they re-read in-range data and the
+    // results are dropped.
+    const bool more_k = j + 2 < nkb, more_v = j + 1 < nkb;
+    load_k(j + 2);
+    load_v(j + 1);
+    qk_block<D>(sm.k[(j + 1) & 1], qf, snext, l32, hh);
+    bf16x8 pf[2][2];
+    float lsum = exp_pack(scur, sl2, m_run, pf);
+    const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
+    if (nz > 0) {
+      const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_run)));
+      lsum -= static_cast<float>(nz) * pz;
+    }
+    l_run += lsum;
+    pv_block<D>(sm.v[j & 1], pf, o, l32, hh);
+    if (more_k) pc.store_k(sm.k[j & 1], kreg);
+    if (more_v) pc.store_v(sm.v[(j + 1) & 1], vreg);
     __syncthreads();
+  };
+
+  for (int j = 0; j < nkb; j += 2) {
+    step(j, sa, sb);
+    if (j + 1 < nkb) step(j + 1, sb, sa);
   }
 
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float inv = 1.0f / l_tot;
+  const int row = wave * 32 + l32;
+  if (row < nq) {
+    bf16 *dst = audio_q
+        ? a.oa + ((static_cast<int64_t>(t) * a.batch + b) * a.A + q0 + row) * a.hidden
+        : a.o + (b * a.n_rows + r0 + q0 + row) * a.hidden;
+    dst += h * D + 4 * hh;
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const float l_tot = l_run[g] + __shfl_xor(l_run[g], 32);
-    const float inv = 1.0f / l_tot;
-    const int row = wave * 32 * NG + 32 * g + l32;
-    if (row < nq) {
-      bf16 *dst = audio_q
-          ? a.oa + ((static_cast<int64_t>(t) * a.batch + b) * a.A + q0 + row) * a.hidden
-          : a.o + (b * a.n_rows + r0 + q0 + row) * a.hidden;
-      dst += h * D + 4 * hh;
+    for (int dt = 0; dt < kDT; ++dt) {
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) {
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-          bf16x4 v4;
-          v4[0] = static_cast<bf16>(o[g][dt][4 * gg + 0] * inv);
-          v4[1] = static_cast<bf16>(o[g][dt][4 * gg + 1] * inv);
-          v4[2] = static_cast<bf16>(o[g][dt][4 * gg + 2] * inv);
-          v4[3] = static_cast<bf16>(o[g][dt][4 * gg + 3] * inv);
-          *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * gg) = v4;
-        }
+      for (int gg = 0; gg < 4; ++gg) {
+        bf16x4 v4;
+        v4[0] = static_cast<bf16>(o[dt][4 * gg + 0] * inv);
+        v4[1] = static_cast<bf16>(o[dt][4 * gg + 1] * inv);
+        v4[2] = static_cast<bf16>(o[dt][4 * gg + 2] * inv);
+        v4[3] = static_cast<bf16>(o[dt][4 * gg + 3] * inv);
+        *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * gg) = v4;
       }
     }
   }
 }
 
-#ifndef TDP_ATTN_GROUPS
-#define TDP_ATTN_GROUPS 1
-#endif
-constexpr int kAttnGroups = TDP_ATTN_GROUPS;   // query groups of 32 per wave
+constexpr int kCoreRowsWG = 4 * 32;   // query rows per attention workgroup
 
 // ---------------------------------------------------------------------------
 // out_proj
@@ -838,9 +858,9 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.max_rows = c.max_rows;
   a.hidden = L.hidden;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
-  const int64_t grid = ceil_div(a.total_units * (kUnit / (4 * 32 * kAttnGroups)), 8) * 8;
-  hipLaunchKernelGGL((attn_core_kernel<D, kAttnGroups>), dim3(static_cast<uint32_t>(grid)),
-                     dim3(kThreads), 0, stream, a);
+  const int64_t grid = ceil_div(a.total_units * (kUnit / kCoreRowsWG), 8) * 8;
+  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
+                     stream, a);
 }
 
 }  // namespace
@@ -877,7 +897,7 @@ extern "C" tdp_status tdp_attn_core(const tdp_attn_desc *desc, int32_t n_tiles,
   if (s != TDP_OK) return s;
   const int64_t units = (c.L.npb / (kUnit / kBlk) + static_cast<int64_t>(n_tiles) * c.L.n_aqb) *
                         desc->batch * desc->heads;
-  if (ceil_div(units * (kUnit / (4 * 32 * kAttnGroups)), 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
+  if (ceil_div(units * (kUnit / kCoreRowsWG), 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
   const hipStream_t stream = as_stream(hip_stream);
   if (desc->head_dim == 64) launch_core<64>(c, stream);
   else launch_core<128>(c, stream);
