@@ -262,3 +262,40 @@ def test_repeat_runs_are_deterministic():
     s.run()
     torch.cuda.synchronize()
     assert torch.equal(a, s.y_global)
+
+
+def _fallback_inputs():
+    """Inputs whose Cauchy-Schwarz bound |q| max|k| is far above every real
+    score while the scores stay ordinary: each head's K is zero on the first
+    half of its dims (RoPE rotates those pairs among themselves, so they stay
+    zero) and Q is large there."""
+    base = _variant("tiny_2x16x16", grid=(2, 8, 12), tiling=((1, 0), (1, 0), (2, 4)),
+                    n_cond=3, n_cond_neg=1, n_audio=5)
+    d, H = base.workload.head_dim, base.workload.heads
+    wq, wk = base.wq.copy(), base.wk.copy()
+    for h in range(H):
+        wk[:, h * d:h * d + d // 2] = 0.0
+        wq[:, h * d:h * d + d // 2] *= 32.0
+    return dataclasses.replace(base, wq=wq, wk=wk)
+
+
+def test_exact_fallback_when_static_bound_underflows():
+    """The static-bound pass underflows (every p < 2^-126) and the kernel must
+    rerun the tile with the exact online softmax."""
+    say("exact fallback")
+    inp = _fallback_inputs()
+    wl = inp.workload
+    p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    r0, r1 = int(p.tile_row_begin[0]), int(p.tile_row_begin[1])
+    seq = np.concatenate([inp.x_global[0, p.row_src[r0:r1]], inp.x_aud[0]]).astype(np.float64)
+    d = wl.head_dim
+    ang = np.concatenate([oracle.rope_angles(p.row_pos[r0:r1], d), np.zeros((5, d // 2))])
+    q = oracle.apply_rope((seq @ inp.wq)[:, :d], ang)
+    k = oracle.apply_rope((seq @ inp.wk)[:, :d], ang)
+    sl2 = 1.4426950408889634 / np.sqrt(d)
+    s_max = (q @ k.T).max(axis=1)
+    gap = (np.linalg.norm(q, axis=1) * np.linalg.norm(k, axis=1).max() - s_max) * sl2
+    assert gap.min() > 150 and np.abs(s_max * sl2).max() < 20
+    s = _step(inp)
+    s.run()
+    _check_full(inp, s)

@@ -19,6 +19,7 @@
 //             stays in registers as the B operand of the second MFMA.
 //   out_proj  Y = O Wo on MFMA, into y_tiles / y_audio_tiles.
 #include <cmath>
+#include <type_traits>
 
 #include "tdp_common.h"
 
@@ -44,6 +45,7 @@ struct Layout {
   int32_t n_aqb = 0;  // 256-query audio units per tile
   int32_t hidden = 0;
   size_t off_wt = 0, off_wot = 0, off_pad_begin = 0, off_blk_tile = 0, off_blk_q0 = 0;
+  size_t off_kmax = 0;  // [B][heads][T+1] largest squared K row norm per tile (slot T: audio)
   size_t off_q = 0, off_k = 0, off_vt = 0, off_qa = 0, off_ka = 0, off_vta = 0;
   size_t off_o = 0, off_oa = 0, total = 0;
 };
@@ -74,6 +76,7 @@ tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, 
   L->off_pad_begin = take((T + 1) * 4);
   L->off_blk_tile = take(L->npb * 4);
   L->off_blk_q0 = take(L->npb * 4);
+  L->off_kmax = take(B * H * (T + 1) * 4);
   L->off_q = take(B * H * L->n_pad * D * 2);
   L->off_k = take(B * H * L->n_pad * D * 2);
   L->off_vt = take(B * H * L->n_pad * D * 2);
@@ -126,13 +129,16 @@ __device__ inline void tile_rows(const int64_t *trb, int32_t t, int64_t n_rows, 
 // pad_begin[t] = first 128-row block of tile t in the padded row space, where
 // each tile takes a whole number of 256-row units (clamped to npb);
 // blk_tile/blk_q0 map each block to its tile and first tile row (-1 for blocks
-// past the last tile).  One workgroup.
+// past the last tile); also clears the per-tile K norm maxima.  One workgroup.
 __global__ __launch_bounds__(1024) void block_table_kernel(const int64_t *__restrict__ trb,
                                                            int32_t T, int64_t n_rows,
                                                            int32_t max_rows, int64_t npb,
                                                            int32_t *__restrict__ pad_begin,
                                                            int32_t *__restrict__ blk_tile,
-                                                           int32_t *__restrict__ blk_q0) {
+                                                           int32_t *__restrict__ blk_q0,
+                                                           uint32_t *__restrict__ kmax2,
+                                                           int64_t n_kmax) {
+  for (int64_t i = threadIdx.x; i < n_kmax; i += blockDim.x) kmax2[i] = 0u;
   for (int32_t t = threadIdx.x; t < T; t += blockDim.x) {
     int64_t r0;
     int32_t len;
@@ -170,6 +176,17 @@ __global__ __launch_bounds__(1024) void block_table_kernel(const int64_t *__rest
 // qkv_rope
 // ---------------------------------------------------------------------------
 
+// Column of key x (x % 16 = position in its 16-key group) in V^T: the middle
+// two quarters of every 16-key group are swapped, so the keys one lane half
+// feeds a 16-key MFMA step of P V, {0..3, 8..11} or {4..7, 12..15}, are
+// contiguous.  The map is its own inverse.  (Key blocks start at multiples
+// of 16 in the padded row space.)
+__device__ inline int vt_column(int x) {
+  const int q = (x >> 2) & 3;
+  const int q2 = (q == 1 || q == 2) ? 3 - q : q;
+  return (x & ~12) | (q2 << 2);
+}
+
 template <typename TX>
 __device__ inline bf16x8 load_x8(const TX *p);
 template <>
@@ -201,6 +218,8 @@ struct QkvArgs {
   int64_t n_pad;              // padded rows per (batch, head) slab of the outputs
   float log2_theta_step;      // -log2(rope_base) / p
   bf16 *q, *k, *vt;
+  uint32_t *kmax2;            // [B][heads][T+1] float bits of the largest squared K norm
+  int32_t n_tiles;
 };
 
 // One workgroup = 128 token rows (4 waves x 32) of one batch entry, all
@@ -288,6 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
     }
     __syncthreads();
     const int64_t slab = b * a.heads + h;
+    float kss = 0.f;   // squared norm of this lane's (rounded) K row of head h
 #pragma unroll
     for (int ft = 0; ft < kFT; ++ft) {
       f32x16 acc = {};
@@ -319,14 +339,32 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
           v4[2] = static_cast<bf16>(acc[4 * g + 2]);
           v4[3] = static_cast<bf16>(acc[4 * g + 3]);
           *reinterpret_cast<bf16x4 *>(dst + 8 * g) = v4;
+          if (m == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float r = static_cast<float>(v4[e]);
+              kss = fmaf(r, r, kss);
+            }
+          }
         }
       } else {
-        bf16 *dst = a.vt + (slab * D + 32 * ft + 4 * hh) * a.n_pad + pad_row0 + my;
+        bf16 *dst = a.vt + (slab * D + 32 * ft + 4 * hh) * a.n_pad + pad_row0 + vt_column(my);
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           dst[static_cast<int64_t>(8 * (v / 4) + (v % 4)) * a.n_pad] = static_cast<bf16>(acc[v]);
         }
       }
+    }
+    if (m == 1) {
+      // Largest squared K row norm of the block for this head and tile; the
+      // float bits of non-negative floats order like unsigned integers, so the
+      // maximum over workgroups is an integer atomic max (order-independent).
+      kss += __shfl_xor(kss, 32);
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) kss = fmaxf(kss, __shfl_xor(kss, off));
+      if (lane == 0)
+        atomicMax(a.kmax2 + slab * (a.n_tiles + 1) + (AUDIO ? a.n_tiles : tile),
+                  __float_as_uint(kss));
     }
   }
 }
@@ -342,71 +380,103 @@ struct CoreArgs {
   const int64_t *trb;
   int64_t n_units, n_pad, a_pad, n_rows, units_per_bh, total_units;
   int32_t T, heads, batch, A, n_aqb, max_rows, hidden;
+  const uint32_t *kmax2;      // [B][heads][T+1] float bits of the largest squared K norm
   float scale_log2;           // log2(e) / sqrt(head_dim)
 };
 
+// LDS staging of one 64-key block, unpadded rows with an XOR swizzle of the
+// 16-byte chunks inside a row:
+//   K   [64 keys][D]: chunk p of row r holds head-dim chunk p ^ ksw(r)
+//   V^T [D][64 keys]: chunk p of row d holds key chunk p ^ vsw(d)
+// Both swizzles make the 16 lanes of an LDS read phase hit 16 different
+// 16-byte bank groups.  Blocks arrive by direct global->LDS loads: each
+// 16-byte load of a wave lands at LDS base + 16 * lane, so each lane fetches
+// the global chunk that belongs at its LDS position.
 template <int D>
 struct CoreSmem {
-  static constexpr int kKRow = D + 8;     // bf16 per staged K row (272 B at D=128)
-  static constexpr int kVRow = kBN + 4;   // bf16 per staged V^T row (136 B)
-  bf16 k[2][kBN * kKRow];
-  bf16 v[2][D * kVRow];
+  static constexpr int kRB = 2 * D;                 // bytes per K row
+  static constexpr int kCPR = D / 8;                // 16-byte chunks per K row
+  bf16 k[2][kBN * D];
+  bf16 v[2][D * kBN];
+  __device__ static int ksw(int r) { return (r / (256 / kRB)) % kCPR; }
+  __device__ static int vsw(int d) { return (d / 2) % 8; }
 };
 
-// This thread's 16-byte pieces of a 64-key block: K piece i is row
-// kr0 + i*kKRowsPer of the block at column kc; V^T piece i is head-dim row
-// vd0 + i*kVRowsPer at key column vc.
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
 template <int D>
-struct Pieces {
-  static constexpr int kN = kBN * D / 8 / kThreads;    // pieces per thread (K and V^T alike)
-  static constexpr int kKRowsPer = kThreads / (D / 8);  // K rows covered per piece index
-  static constexpr int kVRowsPer = kThreads / (kBN / 8);
-  int kr0, kc, vd0, vc;
-  __device__ Pieces() {
-    kr0 = threadIdx.x / (D / 8);
-    kc = (threadIdx.x % (D / 8)) * 8;
-    vd0 = threadIdx.x / (kBN / 8);
-    vc = (threadIdx.x % (kBN / 8)) * 8;
-  }
-  __device__ void load_k(const bf16 *kblk, bf16x8 (&r)[kN]) const {
+struct DirectStage {
+  static constexpr int kKUnits = kBN * D * 2 / 1024 / 4;   // 1 KB loads per wave, K block
+  static constexpr int kVUnits = D * kBN * 2 / 1024 / 4;   // 1 KB loads per wave, V^T block
+  int32_t koff[kKUnits];                 // element offset of this lane's chunk in a K block
+  int32_t vrow[kVUnits], vcol[kVUnits];  // V^T row and key column of this lane's chunk
+  int wave;
+
+  __device__ DirectStage(int wave_, int lane) : wave(wave_) {
 #pragma unroll
-    for (int i = 0; i < kN; ++i)
-      r[i] = *reinterpret_cast<const bf16x8 *>(kblk + (kr0 + i * kKRowsPer) * D + kc);
-  }
-  __device__ void load_v(const bf16 *vblk, int32_t vstride, bf16x8 (&r)[kN]) const {
+    for (int i = 0; i < kKUnits; ++i) {
+      const int byte = (i * 4 + wave) * 1024 + 16 * lane;
+      const int r = byte / CoreSmem<D>::kRB, p = (byte % CoreSmem<D>::kRB) / 16;
+      koff[i] = r * D + 8 * (p ^ CoreSmem<D>::ksw(r));
+    }
 #pragma unroll
-    for (int i = 0; i < kN; ++i)
-      r[i] = *reinterpret_cast<const bf16x8 *>(vblk + (vd0 + i * kVRowsPer) * vstride + vc);
-  }
-  __device__ void store_k(bf16 *ks, const bf16x8 (&r)[kN]) const {
-#pragma unroll
-    for (int i = 0; i < kN; ++i)
-      *reinterpret_cast<bf16x8 *>(ks + (kr0 + i * kKRowsPer) * CoreSmem<D>::kKRow + kc) = r[i];
-  }
-  __device__ void store_v(bf16 *vs, const bf16x8 (&r)[kN]) const {
-#pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      bf16 *p = vs + (vd0 + i * kVRowsPer) * CoreSmem<D>::kVRow + vc;
-      *reinterpret_cast<bf16x4 *>(p) = bf16x4{r[i][0], r[i][1], r[i][2], r[i][3]};
-      *reinterpret_cast<bf16x4 *>(p + 4) = bf16x4{r[i][4], r[i][5], r[i][6], r[i][7]};
+    for (int i = 0; i < kVUnits; ++i) {
+      const int byte = (i * 4 + wave) * 1024 + 16 * lane;
+      const int d = byte / (2 * kBN), p = (byte % (2 * kBN)) / 16;
+      vrow[i] = d;
+      vcol[i] = 8 * (p ^ CoreSmem<D>::vsw(d));
     }
   }
+  __device__ void load_k(const bf16 *kblk, bf16 *kbuf) const {
+#pragma unroll
+    for (int i = 0; i < kKUnits; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(kblk + koff[i]),
+                                       (lvoid_t *)(kbuf + (i * 4 + wave) * 512), 16, 0, 0);
+  }
+  __device__ void load_v(const bf16 *vblk, int32_t vstride, bf16 *vbuf) const {
+#pragma unroll
+    for (int i = 0; i < kVUnits; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(vblk + vrow[i] * vstride + vcol[i]),
+                                       (lvoid_t *)(vbuf + (i * 4 + wave) * 512), 16, 0, 0);
+  }
 };
 
+// Wait for this wave's direct loads, then the workgroup barrier.
+__device__ __forceinline__ void loads_landed_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Per-lane element offsets of the MFMA fragments in the swizzled buffers.
+template <int D>
+struct FragOffsets {
+  int32_t k[D / 16];     // K row l32, head-dim chunk 2 st + hh  (+32 D per 32-key tile)
+  int32_t v[2][2];       // V^T row l32, key chunk 4 kt + 2 u + hh (+32*64 per 32-row tile)
+  __device__ FragOffsets(int l32, int hh) {
+    const int ks = CoreSmem<D>::ksw(l32), vs = CoreSmem<D>::vsw(l32);
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) k[st] = l32 * D + 8 * ((2 * st + hh) ^ ks);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) v[kt][u] = l32 * kBN + 8 * ((4 * kt + 2 * u + hh) ^ vs);
+  }
+};
 
 // S^T[key][query] = K Q^T for one 64-key block: keys on the MFMA rows, so
 // lane l owns query l%32 and, in s[kt][v], key 32 kt + 8 (v/4) + 4 hh + v%4.
 template <int D>
 __device__ __forceinline__ void qk_block(const bf16 *__restrict__ ks, const bf16x8 (&qf)[D / 16],
-                                         f32x16 (&s)[2], int l32, int hh) {
-  constexpr int KR = CoreSmem<D>::kKRow;
+                                         f32x16 (&s)[2], const FragOffsets<D> &fo) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     s[kt] = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + (32 * kt + l32) * KR + 16 * st + 8 * hh);
+      const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + 32 * kt * D + fo.k[st]);
       s[kt] = mfma32(kf, qf[st], s[kt]);
     }
   }
@@ -442,21 +512,18 @@ __device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], float sl2, float
   return lsum;
 }
 
-// O^T[d][query] += V^T P^T; the V^T fragment is read in the key order of P.
+// O^T[d][query] += V^T P^T.  The V^T chunk a lane reads holds exactly the
+// keys of its P operand, in the same order (see vt_column).
 template <int D>
 __device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs, const bf16x8 (&pf)[2][2],
-                                         f32x16 (&o)[D / 32], int l32, int hh) {
-  constexpr int VR = CoreSmem<D>::kVRow;
+                                         f32x16 (&o)[D / 32], const FragOffsets<D> &fo) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
-        const bf16 *vp = vs + (32 * dt + l32) * VR + 32 * kt + 16 * uu + 4 * hh;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(vp);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(vp + 8);
-        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vs + 32 * dt * kBN + fo.v[kt][uu]);
         o[dt] = mfma32(vf, pf[kt][uu], o[dt]);
       }
     }
@@ -560,81 +627,120 @@ __global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
   const int nz0 = nkb0 > 0 ? padded_keys(len0 - (nkb0 - 1) * kBN, hh) : 0;
   const int nz1 = nkb1 > 0 ? padded_keys(a.A - (nkb1 - 1) * kBN, hh) : 0;
 
-  const Pieces<D> pc;
-  bf16x8 kreg[Pieces<D>::kN], vreg[Pieces<D>::kN];
-  // Block j (clamped to the last block) of the tile-then-audio key sequence.
-  auto load_k = [&](int j) {
+  const DirectStage<D> ds(wave, lane);
+  const FragOffsets<D> fo(l32, hh);
+  // Block j (clamped to the last block) of the tile-then-audio key sequence,
+  // straight into an LDS buffer.
+  auto load_k = [&](int j, bf16 *buf) {
     j = min(j, nkb - 1);
     const bf16 *kb = j < nkb0 ? kseg0 + static_cast<int64_t>(j) * kBN * D
                               : kseg1 + static_cast<int64_t>(j - nkb0) * kBN * D;
-    pc.load_k(kb, kreg);
+    ds.load_k(kb, buf);
   };
-  auto load_v = [&](int j) {
+  auto load_v = [&](int j, bf16 *buf) {
     j = min(j, nkb - 1);
     const bool s0 = j < nkb0;
-    pc.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0 ? vstr0 : vstr1, vreg);
+    ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0 ? vstr0 : vstr1, buf);
   };
+
+  const float sl2 = a.scale_log2;
+  // Static softmax bound (Cauchy-Schwarz): every score of this query obeys
+  // s <= |q| * max_k |k|, over the tile's keys and the audio keys, so with
+  // m_q = |q| max|k| sl2 (plus a rounding margin) every p = 2^(s sl2 - m_q)
+  // is <= 1 and no running maximum is needed.  |q| is taken over the bf16 Q
+  // row held in registers; max|k| comes from the QKV stage.
+  float m_q;
+  {
+    float qq = 0.f;
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(qf[st][e]);
+        qq = fmaf(x, x, qq);
+      }
+    qq += __shfl_xor(qq, 32);
+    const uint32_t *km = a.kmax2 + bh * (a.T + 1);
+    float kk = nkb0 > 0 ? __uint_as_float(km[t]) : 0.f;
+    if (nkb1 > 0) kk = fmaxf(kk, __uint_as_float(km[a.T]));
+    m_q = sqrtf(qq) * sqrtf(kk) * sl2 * 1.0009765625f + 1e-30f;
+  }
 
   f32x16 o[kDT];
-#pragma unroll
-  for (int i = 0; i < kDT; ++i) o[i] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale_log2;
-
-  // prologue: K(0), V(0), K(1) into LDS; S(0)
-  load_k(0);
-  pc.store_k(sm.k[0], kreg);
-  load_v(0);
-  pc.store_v(sm.v[0], vreg);
-  if (nkb > 1) {
-    load_k(1);
-    pc.store_k(sm.k[1], kreg);
-  }
-  __syncthreads();
+  float m_run = 0.f, l_run = 0.f;
   f32x16 sa[2], sb[2];
-  qk_block<D>(sm.k[0], qf, sa, l32, hh);
 
-  auto step = [&](int j, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
-    const float mb = block_max(scur) * sl2;
-    if (__builtin_expect(__ballot(mb > m_run + kLazy) != 0, 0)) {
-      // Rare after the first block; the empty asm keeps this a real branch.
-      asm volatile("" ::: "memory");
-      const float m_new = fmaxf(m_run, mb);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  // K(0), V(0), K(1) into LDS; S(0).  The caller has passed a barrier since
+  // any earlier reads of these buffers.
+  auto prologue = [&]() {
 #pragma unroll
-      for (int i = 0; i < kDT; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    // Loads and S(j+1) run unconditionally so they share one basic block with
-    // the exp below; past the last block they re-read in-range data and the
-    // results are dropped.
-    const bool more_k = j + 2 < nkb, more_v = j + 1 < nkb;
-    load_k(j + 2);
-    load_v(j + 1);
-    qk_block<D>(sm.k[(j + 1) & 1], qf, snext, l32, hh);
-    bf16x8 pf[2][2];
-    float lsum = exp_pack(scur, sl2, m_run, pf);
-    const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
-    if (nz > 0) {
-      const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_run)));
-      lsum -= static_cast<float>(nz) * pz;
-    }
-    l_run += lsum;
-    pv_block<D>(sm.v[j & 1], pf, o, l32, hh);
-    if (more_k) pc.store_k(sm.k[j & 1], kreg);
-    if (more_v) pc.store_v(sm.v[(j + 1) & 1], vreg);
-    __syncthreads();
+    for (int i = 0; i < kDT; ++i) o[i] = f32x16{};
+    l_run = 0.f;
+    load_k(0, sm.k[0]);
+    load_v(0, sm.v[0]);
+    load_k(1, sm.k[1]);
+    loads_landed_barrier();
+    qk_block<D>(sm.k[0], qf, sa, fo);
   };
 
+  // One 64-key block.  EXACT = false: p = 2^(s sl2 - m_q) with the static
+  // bound.  EXACT = true: the exact online softmax with a lazily moved
+  // maximum (moved only when a block max exceeds it by more than kLazy, so
+  // p <= 2^kLazy; the O rescale is rare and sits on a real branch).  Loads
+  // and S(j+1) run unconditionally so they share one basic block with the
+  // exp; past the last block they re-read in-range data and the results are
+  // dropped, and the stores only refill buffers whose data was consumed in
+  // block j-1.
+  auto step = [&](auto exact_tag, int j, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+    constexpr bool kExact = decltype(exact_tag)::value;
+    if constexpr (kExact) {
+      const float mb = block_max(scur) * sl2;
+      if (__builtin_expect(__ballot(mb > m_run + kLazy) != 0, 0)) {
+        // Rare after the first block; the empty asm keeps this a real branch.
+        asm volatile("" ::: "memory");
+        const float m_new = fmaxf(m_run, mb);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+        for (int i = 0; i < kDT; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+    }
+    const float m_use = kExact ? m_run : m_q;
+    // K(j) and V(j-1) were consumed in block j-1: their buffers are free.
+    load_k(j + 2, sm.k[j & 1]);
+    load_v(j + 1, sm.v[(j + 1) & 1]);
+    qk_block<D>(sm.k[(j + 1) & 1], qf, snext, fo);
+    bf16x8 pf[2][2];
+    const float lsum = exp_pack(scur, sl2, m_use, pf);
+    const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
+    const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_use)));
+    l_run += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
+    pv_block<D>(sm.v[j & 1], pf, o, fo);
+    loads_landed_barrier();
+  };
+
+  prologue();
   for (int j = 0; j < nkb; j += 2) {
-    step(j, sa, sb);
-    if (j + 1 < nkb) step(j + 1, sb, sa);
+    step(std::false_type{}, j, sa, sb);
+    if (j + 1 < nkb) step(std::false_type{}, j + 1, sb, sa);
+  }
+  float l_tot = l_run + __shfl_xor(l_run, 32);
+  // The bound can exceed the real maximum by so much that every p underflows
+  // (huge |q||k| with no aligned key).  Then the workgroup runs the tile again
+  // with the exact online softmax.
+  if (__syncthreads_or(!(l_tot >= 0x1p-90f))) {
+    m_run = -INFINITY;
+    prologue();
+    for (int j = 0; j < nkb; j += 2) {
+      step(std::true_type{}, j, sa, sb);
+      if (j + 1 < nkb) step(std::true_type{}, j + 1, sb, sa);
+    }
+    l_tot = l_run + __shfl_xor(l_run, 32);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.0f / l_tot;
   const int row = wave * 32 + l32;
   if (row < nq) {
@@ -784,7 +890,9 @@ extern "C" tdp_status tdp_attn_prepare(const tdp_attn_desc *desc, int32_t n_tile
   hipLaunchKernelGGL(block_table_kernel, dim3(1), dim3(1024), 0, stream, tile_row_begin, n_tiles,
                      n_rows, max_tile_rows, L.npb, ws_at<int32_t>(workspace, L.off_pad_begin),
                      ws_at<int32_t>(workspace, L.off_blk_tile),
-                     ws_at<int32_t>(workspace, L.off_blk_q0));
+                     ws_at<int32_t>(workspace, L.off_blk_q0),
+                     ws_at<uint32_t>(workspace, L.off_kmax),
+                     static_cast<int64_t>(desc->batch) * desc->heads * (n_tiles + 1));
   return launch_status();
 }
 
@@ -803,6 +911,8 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
   a.max_rows = c.max_rows;
   a.row_pos = row_pos;
   a.wt = ws_at<bf16>(c.ws, L.off_wt);
+  a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
+  a.n_tiles = c.n_tiles;
   a.heads = c.d->heads;
   a.hidden = L.hidden;
   a.log2_theta_step = -std::log2(static_cast<double>(c.d->rope_base)) / (D / 6);
@@ -857,6 +967,7 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.n_aqb = L.n_aqb;
   a.max_rows = c.max_rows;
   a.hidden = L.hidden;
+  a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
   const int64_t grid = ceil_div(a.total_units * (kUnit / kCoreRowsWG), 8) * 8;
   hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
