@@ -409,35 +409,39 @@ template <int D>
 struct DirectStage {
   static constexpr int kKUnits = kBN * D * 2 / 1024 / 4;   // 1 KB loads per wave, K block
   static constexpr int kVUnits = D * kBN * 2 / 1024 / 4;   // 1 KB loads per wave, V^T block
-  int32_t koff[kKUnits];                 // element offset of this lane's chunk in a K block
-  int32_t vrow[kVUnits], vcol[kVUnits];  // V^T row and key column of this lane's chunk
-  int wave;
+  uint32_t koff[kKUnits];                 // byte offset of this lane's chunk in a K block
+  uint32_t voff0[kVUnits], voff1[kVUnits];  // ... in a V^T block of segment 0 / 1
+  int wave;                               // wave-uniform
 
-  __device__ DirectStage(int wave_, int lane) : wave(wave_) {
+  __device__ DirectStage(int wave_, int lane, int32_t vstr0, int32_t vstr1) : wave(wave_) {
 #pragma unroll
     for (int i = 0; i < kKUnits; ++i) {
       const int byte = (i * 4 + wave) * 1024 + 16 * lane;
       const int r = byte / CoreSmem<D>::kRB, p = (byte % CoreSmem<D>::kRB) / 16;
-      koff[i] = r * D + 8 * (p ^ CoreSmem<D>::ksw(r));
+      koff[i] = 2u * static_cast<uint32_t>(r * D + 8 * (p ^ CoreSmem<D>::ksw(r)));
     }
 #pragma unroll
     for (int i = 0; i < kVUnits; ++i) {
       const int byte = (i * 4 + wave) * 1024 + 16 * lane;
       const int d = byte / (2 * kBN), p = (byte % (2 * kBN)) / 16;
-      vrow[i] = d;
-      vcol[i] = 8 * (p ^ CoreSmem<D>::vsw(d));
+      const uint32_t col = 8 * (p ^ CoreSmem<D>::vsw(d));
+      voff0[i] = 2u * (static_cast<uint32_t>(d) * static_cast<uint32_t>(vstr0) + col);
+      voff1[i] = 2u * (static_cast<uint32_t>(d) * static_cast<uint32_t>(vstr1) + col);
     }
   }
+  // kblk / vblk: wave-uniform block bases; lane offsets are 32-bit.
   __device__ void load_k(const bf16 *kblk, bf16 *kbuf) const {
+    const char *base = reinterpret_cast<const char *>(kblk);
 #pragma unroll
     for (int i = 0; i < kKUnits; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(kblk + koff[i]),
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(base + koff[i]),
                                        (lvoid_t *)(kbuf + (i * 4 + wave) * 512), 16, 0, 0);
   }
-  __device__ void load_v(const bf16 *vblk, int32_t vstride, bf16 *vbuf) const {
+  __device__ void load_v(const bf16 *vblk, bool seg0, bf16 *vbuf) const {
+    const char *base = reinterpret_cast<const char *>(vblk);
 #pragma unroll
     for (int i = 0; i < kVUnits; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(vblk + vrow[i] * vstride + vcol[i]),
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(base + (seg0 ? voff0[i] : voff1[i])),
                                        (lvoid_t *)(vbuf + (i * 4 + wave) * 512), 16, 0, 0);
   }
 };
@@ -627,7 +631,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
   const int nz0 = nkb0 > 0 ? padded_keys(len0 - (nkb0 - 1) * kBN, hh) : 0;
   const int nz1 = nkb1 > 0 ? padded_keys(a.A - (nkb1 - 1) * kBN, hh) : 0;
 
-  const DirectStage<D> ds(wave, lane);
+  const DirectStage<D> ds(__builtin_amdgcn_readfirstlane(wave), lane, vstr0, vstr1);
   const FragOffsets<D> fo(l32, hh);
   // Block j (clamped to the last block) of the tile-then-audio key sequence,
   // straight into an LDS buffer.
@@ -640,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
   auto load_v = [&](int j, bf16 *buf) {
     j = min(j, nkb - 1);
     const bool s0 = j < nkb0;
-    ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0 ? vstr0 : vstr1, buf);
+    ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0, buf);
   };
 
   const float sl2 = a.scale_log2;
