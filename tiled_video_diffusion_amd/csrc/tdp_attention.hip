@@ -23,6 +23,20 @@
 
 #include "tdp_common.h"
 
+// Explicit MFMA / LDS / VALU interleaving of the attention inner block
+// (0 = the compiler's own schedule).
+#ifndef TDP_ATTN_SCHED
+#define TDP_ATTN_SCHED 0
+#endif
+// Wave priority raised while a wave issues its MFMA-heavy part (0 = off).
+#ifndef TDP_ATTN_PRIO
+#define TDP_ATTN_PRIO 0
+#endif
+// Waves (of 32 query rows each) per attention workgroup: 4 or 8.
+#ifndef TDP_ATTN_WAVES
+#define TDP_ATTN_WAVES 4
+#endif
+
 namespace tdp {
 namespace {
 
@@ -407,8 +421,9 @@ typedef __attribute__((address_space(3))) void lvoid_t;
 
 template <int D>
 struct DirectStage {
-  static constexpr int kKUnits = kBN * D * 2 / 1024 / 4;   // 1 KB loads per wave, K block
-  static constexpr int kVUnits = D * kBN * 2 / 1024 / 4;   // 1 KB loads per wave, V^T block
+  static constexpr int kWaves = TDP_ATTN_WAVES;
+  static constexpr int kKUnits = kBN * D * 2 / 1024 / kWaves;   // 1 KB loads per wave, K block
+  static constexpr int kVUnits = D * kBN * 2 / 1024 / kWaves;   // 1 KB loads per wave, V^T block
   uint32_t koff[kKUnits];                 // byte offset of this lane's chunk in a K block
   uint32_t voff0[kVUnits], voff1[kVUnits];  // ... in a V^T block of segment 0 / 1
   int wave;                               // wave-uniform
@@ -416,13 +431,13 @@ struct DirectStage {
   __device__ DirectStage(int wave_, int lane, int32_t vstr0, int32_t vstr1) : wave(wave_) {
 #pragma unroll
     for (int i = 0; i < kKUnits; ++i) {
-      const int byte = (i * 4 + wave) * 1024 + 16 * lane;
+      const int byte = (i * kWaves + wave) * 1024 + 16 * lane;
       const int r = byte / CoreSmem<D>::kRB, p = (byte % CoreSmem<D>::kRB) / 16;
       koff[i] = 2u * static_cast<uint32_t>(r * D + 8 * (p ^ CoreSmem<D>::ksw(r)));
     }
 #pragma unroll
     for (int i = 0; i < kVUnits; ++i) {
-      const int byte = (i * 4 + wave) * 1024 + 16 * lane;
+      const int byte = (i * kWaves + wave) * 1024 + 16 * lane;
       const int d = byte / (2 * kBN), p = (byte % (2 * kBN)) / 16;
       const uint32_t col = 8 * (p ^ CoreSmem<D>::vsw(d));
       voff0[i] = 2u * (static_cast<uint32_t>(d) * static_cast<uint32_t>(vstr0) + col);
@@ -435,14 +450,14 @@ struct DirectStage {
 #pragma unroll
     for (int i = 0; i < kKUnits; ++i)
       __builtin_amdgcn_global_load_lds((gvoid_t *)(base + koff[i]),
-                                       (lvoid_t *)(kbuf + (i * 4 + wave) * 512), 16, 0, 0);
+                                       (lvoid_t *)(kbuf + (i * kWaves + wave) * 512), 16, 0, 0);
   }
   __device__ void load_v(const bf16 *vblk, bool seg0, bf16 *vbuf) const {
     const char *base = reinterpret_cast<const char *>(vblk);
 #pragma unroll
     for (int i = 0; i < kVUnits; ++i)
       __builtin_amdgcn_global_load_lds((gvoid_t *)(base + (seg0 ? voff0[i] : voff1[i])),
-                                       (lvoid_t *)(vbuf + (i * 4 + wave) * 512), 16, 0, 0);
+                                       (lvoid_t *)(vbuf + (i * kWaves + wave) * 512), 16, 0, 0);
   }
 };
 
@@ -565,11 +580,11 @@ __device__ __forceinline__ int padded_keys(int kvalid, int hh) {
 // walks a contiguous range of work items and the workgroups sharing a tile's
 // K/V run together on one L2.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
+__global__ __launch_bounds__(64 * TDP_ATTN_WAVES, 8 / TDP_ATTN_WAVES) void attn_core_kernel(CoreArgs a) {
   __shared__ __attribute__((aligned(16))) CoreSmem<D> sm;
   constexpr int kSteps = D / 16;
   constexpr int kDT = D / 32;
-  constexpr int kRowsWG = 4 * 32;              // query rows per workgroup
+  constexpr int kRowsWG = TDP_ATTN_WAVES * 32;  // query rows per workgroup
   constexpr int kSplit = kUnit / kRowsWG;      // workgroups per 256-row unit
 
   const int64_t G = gridDim.x;
@@ -716,13 +731,42 @@ __global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
     // K(j) and V(j-1) were consumed in block j-1: their buffers are free.
     load_k(j + 2, sm.k[j & 1]);
     load_v(j + 1, sm.v[(j + 1) & 1]);
+#if TDP_ATTN_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
     qk_block<D>(sm.k[(j + 1) & 1], qf, snext, fo);
+#if TDP_ATTN_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
     bf16x8 pf[2][2];
     const float lsum = exp_pack(scur, sl2, m_use, pf);
     const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
     const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_use)));
     l_run += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
     pv_block<D>(sm.v[j & 1], pf, o, fo);
+#if TDP_ATTN_SCHED == 1
+    // S(j+1) MFMAs interleaved with the exp of block j, then the P V MFMAs.
+    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+#elif TDP_ATTN_SCHED == 2
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+#endif
     loads_landed_barrier();
   };
 
@@ -767,7 +811,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_core_kernel(CoreArgs a) {
   }
 }
 
-constexpr int kCoreRowsWG = 4 * 32;   // query rows per attention workgroup
+constexpr int kCoreRowsWG = TDP_ATTN_WAVES * 32;   // query rows per attention workgroup
 
 // ---------------------------------------------------------------------------
 // out_proj
@@ -974,7 +1018,7 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
   const int64_t grid = ceil_div(a.total_units * (kUnit / kCoreRowsWG), 8) * 8;
-  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(64 * TDP_ATTN_WAVES), 0,
                      stream, a);
 }
 
