@@ -40,6 +40,9 @@
 namespace tdp {
 namespace {
 
+typedef __attribute__((address_space(1))) void gvoid_t;   // global pointer for direct LDS loads
+typedef __attribute__((address_space(3))) void lvoid_t;   // LDS pointer
+
 constexpr int kC = 128;       // channels per token row
 constexpr int kBlk = 128;     // rows per block of the padded row space (one QKV workgroup)
 constexpr int kUnit = 256;    // tiles are padded to whole units of this many rows
@@ -201,6 +204,15 @@ __device__ inline int vt_column(int x) {
   return (x & ~12) | (q2 << 2);
 }
 
+// Workgroup barrier ordering LDS only: waves exchange data through LDS, so
+// outstanding global stores need not complete first (a plain __syncthreads
+// would wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename TX>
 __device__ inline bf16x8 load_x8(const TX *p);
 template <>
@@ -245,11 +257,22 @@ template <typename TX, int D, bool AUDIO>
 __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
   constexpr int kFT = D / 32;            // 32-feature MFMA tiles per head
   constexpr int kPairs = D / 4;          // rotation pairs held per lane
-  constexpr int kLdsRow = kC + 8;        // bf16 elements per staged W^T row
-  __shared__ __attribute__((aligned(16))) bf16 sW[D * kLdsRow];
+  // Waves 0-1 load W^T chunks, waves 2-3 copy output tiles out, so a wave
+  // waiting for its loads (vmcnt counts stores too) never waits for stores.
+  constexpr int kWUnits = D * kC * 2 / 1024 / 2;   // 1 KB direct loads per loader wave per chunk
+  // staged output rows, +8 bytes each: 8-byte aligned, lane rows hit distinct banks
+  constexpr int kVtRow = kBlk + 4;       // bf16 per staged V^T row (128 tokens)
+  constexpr int kQkRow = D + 4;          // bf16 per staged Q/K row (one token)
+  // W^T chunk [D][128]: unpadded 256-byte rows, 16-byte chunk p of row r holds
+  // channel chunk p ^ (r % 16) (conflict-free fragment reads).  sOut: the
+  // 128-token output tile of one head, [token][D] for Q/K, [D][token] for V^T.
+  __shared__ __attribute__((aligned(16))) bf16 sW[D * kC];
+  __shared__ __attribute__((aligned(16))) bf16 sOut[(kBlk * kQkRow > D * kVtRow) ? kBlk * kQkRow
+                                                                                  : D * kVtRow];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const int64_t b = blockIdx.y;
   const int64_t pb = blockIdx.x;
 
@@ -273,7 +296,32 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
   const int my = wave * 32 + l32;
   const bool valid = my < nvalid;
 
-  // X^T fragments (B operand): token `my`, channels 16s + 8hh + 0..7.
+  // W^T chunk (m, h) = rows [m*hidden + h*D, +D) of wt, straight into LDS.
+  uint32_t woff[kWUnits];
+#pragma unroll
+  for (int i = 0; i < kWUnits; ++i) {
+    const int byte = (i * 2 + (uwave & 1)) * 1024 + 16 * lane;
+    const int r = byte / 256, p = (byte % 256) / 16;
+    woff[i] = static_cast<uint32_t>(r * 256 + 16 * (p ^ (r % 16)));
+  }
+  auto load_w = [&](int chunk) {
+    const int m = chunk / a.heads, h = chunk - m * a.heads;
+    const char *src = reinterpret_cast<const char *>(
+        a.wt + (static_cast<int64_t>(m) * a.hidden + static_cast<int64_t>(h) * D) * kC);
+#pragma unroll
+    for (int i = 0; i < kWUnits; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(src + woff[i]),
+                                       (lvoid_t *)(sW + (i * 2 + uwave) * 512), 16, 0, 0);
+  };
+  // this lane's fragment offsets: row 32 ft + l32, channel chunk 2 s + hh
+  int32_t wro[kC / 16];
+#pragma unroll
+  for (int st = 0; st < kC / 16; ++st) wro[st] = l32 * kC + 8 * ((2 * st + hh) ^ (l32 % 16));
+
+  if (uwave < 2) load_w(0);
+
+  // X fragments: token `my`, channels 16s + 8hh + 0..7 (B operand of
+  // W^T X^T, A operand of X W).
   bf16x8 xf[kC / 16];
   const TX *xrow = static_cast<const TX *>(a.x) + (b * a.x_rows + src0 + (valid ? my : 0)) * kC;
 #pragma unroll
@@ -299,52 +347,49 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
       float c = 1.f, s = 0.f;
       if (ax < 3) {
         const float theta = exp2f(static_cast<float>(j - ax * p) * a.log2_theta_step);
-        sincosf(mid[ax] * theta, &s, &c);
+        const float mv = ax == 0 ? mid[0] : (ax == 1 ? mid[1] : mid[2]);   // no indexed array
+        sincosf(mv * theta, &s, &c);
       }
       rc[i] = c;
       rs[i] = s;
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-  for (int chunk = 0; chunk < 3 * a.heads; ++chunk) {
+  const int n_chunks = 3 * a.heads;
+  // The chunk loop is compiled twice: loader waves (W^T direct loads, which
+  // the compiler must wait for before LDS reads) and copy waves (global
+  // stores only), so copy waves never wait for their stores.  Both copies
+  // pass the same barriers.
+  auto chunk_loop = [&](auto loader_tag) {
+  constexpr bool loader = decltype(loader_tag)::value;
+  for (int chunk = 0; chunk < n_chunks; ++chunk) {
     const int m = chunk / a.heads, h = chunk - m * a.heads;
-    __syncthreads();
-    {  // stage W^T rows [m][h*D, h*D + D) into LDS
-      const bf16 *src = a.wt + (static_cast<int64_t>(m) * a.hidden + static_cast<int64_t>(h) * D) * kC;
-#pragma unroll
-      for (int i = 0; i < D * kC / 8 / kThreads; ++i) {
-        const int c = threadIdx.x + i * kThreads;
-        const int row = c / (kC / 8), col = (c % (kC / 8)) * 8;
-        *reinterpret_cast<bf16x8 *>(&sW[row * kLdsRow + col]) =
-            *reinterpret_cast<const bf16x8 *>(src + row * kC + col);
-      }
-    }
-    __syncthreads();
     const int64_t slab = b * a.heads + h;
     float kss = 0.f;   // squared norm of this lane's (rounded) K row of head h
+    if (m < 2) {
 #pragma unroll
-    for (int ft = 0; ft < kFT; ++ft) {
-      f32x16 acc = {};
+      for (int ft = 0; ft < kFT; ++ft) {
+        f32x16 acc = {};
 #pragma unroll
-      for (int s = 0; s < kC / 16; ++s) {
-        const bf16x8 w = *reinterpret_cast<const bf16x8 *>(&sW[(32 * ft + l32) * kLdsRow + 16 * s + 8 * hh]);
-        acc = mfma32(w, xf[s], acc);
-      }
-      // acc[v]: feature 32 ft + 8 (v/4) + 4 hh + v%4 of token `my`
-      if (!AUDIO && m < 2) {
+        for (int s = 0; s < kC / 16; ++s) {
+          const bf16x8 w = *reinterpret_cast<const bf16x8 *>(sW + 32 * ft * kC + wro[s]);
+          acc = mfma32(w, xf[s], acc);
+        }
+        // acc[v]: feature 32 ft + 8 (v/4) + 4 hh + v%4 of token `my`
+        if (!AUDIO) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+          for (int g = 0; g < 4; ++g) {
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int i = ft * 8 + g * 2 + e, v = 4 * g + 2 * e;
-            const float x0 = acc[v], x1 = acc[v + 1];
-            acc[v] = x0 * rc[i] - x1 * rs[i];
-            acc[v + 1] = x0 * rs[i] + x1 * rc[i];
+            for (int e = 0; e < 2; ++e) {
+              const int i = ft * 8 + g * 2 + e, v = 4 * g + 2 * e;
+              const float x0 = acc[v], x1 = acc[v + 1];
+              acc[v] = x0 * rc[i] - x1 * rs[i];
+              acc[v + 1] = x0 * rs[i] + x1 * rc[i];
+            }
           }
         }
-      }
-      if (m < 2) {
-        bf16 *dst = (m == 0 ? a.q : a.k) + (slab * a.n_pad + pad_row0 + my) * D + 32 * ft + 4 * hh;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           bf16x4 v4;
@@ -352,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
           v4[1] = static_cast<bf16>(acc[4 * g + 1]);
           v4[2] = static_cast<bf16>(acc[4 * g + 2]);
           v4[3] = static_cast<bf16>(acc[4 * g + 3]);
-          *reinterpret_cast<bf16x4 *>(dst + 8 * g) = v4;
+          *reinterpret_cast<bf16x4 *>(sOut + my * kQkRow + 32 * ft + 8 * g + 4 * hh) = v4;
           if (m == 1) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -361,11 +406,29 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
             }
           }
         }
-      } else {
-        bf16 *dst = a.vt + (slab * D + 32 * ft + 4 * hh) * a.n_pad + pad_row0 + vt_column(my);
+      }
+    } else {
+      // V = X Wv with tokens on the MFMA rows: lane holds head-dim row
+      // 32 ft + l32 of V^T and 4 consecutive tokens per group (vt_column keeps
+      // a quarter's order).
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          dst[static_cast<int64_t>(8 * (v / 4) + (v % 4)) * a.n_pad] = static_cast<bf16>(acc[v]);
+      for (int ft = 0; ft < kFT; ++ft) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < kC / 16; ++s) {
+          const bf16x8 w = *reinterpret_cast<const bf16x8 *>(sW + 32 * ft * kC + wro[s]);
+          acc = mfma32(xf[s], w, acc);
+        }
+        // acc[v]: token wave*32 + 8 (v/4) + 4 hh + v%4, head dim 32 ft + l32
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 v4;
+          v4[0] = static_cast<bf16>(acc[4 * g + 0]);
+          v4[1] = static_cast<bf16>(acc[4 * g + 1]);
+          v4[2] = static_cast<bf16>(acc[4 * g + 2]);
+          v4[3] = static_cast<bf16>(acc[4 * g + 3]);
+          *reinterpret_cast<bf16x4 *>(sOut + (32 * ft + l32) * kVtRow +
+                                      vt_column(wave * 32 + 8 * g + 4 * hh)) = v4;
         }
       }
     }
@@ -380,7 +443,43 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
         atomicMax(a.kmax2 + slab * (a.n_tiles + 1) + (AUDIO ? a.n_tiles : tile),
                   __float_as_uint(kss));
     }
+    lds_barrier();                          // sW read, sOut complete
+    if (loader && chunk + 1 < n_chunks) load_w(chunk + 1);
+    // Copy the tile out in 16-byte pieces: consecutive threads, consecutive bytes.
+    const int ct = threadIdx.x - 128;      // copy thread of waves 2-3
+    if constexpr (loader) {
+      // nothing to copy
+    } else if (m < 2) {
+      bf16 *dst = (m == 0 ? a.q : a.k) + (slab * a.n_pad + pad_row0) * D;
+#pragma unroll
+      for (int i = 0; i < kBlk * D / 8 / 128; ++i) {
+        const int piece = ct + i * 128;
+        const int r = piece / (D / 8), col = (piece % (D / 8)) * 8;
+        const bf16 *src = sOut + r * kQkRow + col;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(src);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(src + 4);
+        *reinterpret_cast<bf16x8 *>(dst + r * D + col) =
+            bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    } else {
+      bf16 *dst = a.vt + slab * D * a.n_pad + pad_row0;
+#pragma unroll
+      for (int i = 0; i < D * kBlk / 8 / 128; ++i) {
+        const int piece = ct + i * 128;
+        const int d = piece / (kBlk / 8), col = (piece % (kBlk / 8)) * 8;
+        const bf16 *src = sOut + d * kVtRow + col;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(src);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(src + 4);
+        *reinterpret_cast<bf16x8 *>(dst + d * a.n_pad + col) =
+            bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    }
+    if (loader) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();                          // W(chunk+1) landed, sOut free
   }
+  };
+  if (uwave < 2) chunk_loop(std::true_type{});
+  else chunk_loop(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -416,8 +515,6 @@ struct CoreSmem {
   __device__ static int vsw(int d) { return (d / 2) % 8; }
 };
 
-typedef __attribute__((address_space(1))) void gvoid_t;
-typedef __attribute__((address_space(3))) void lvoid_t;
 
 template <int D>
 struct DirectStage {
