@@ -582,18 +582,23 @@ struct FragOffsets {
   }
 };
 
-// S^T[key][query] = K Q^T for one 64-key block: keys on the MFMA rows, so
-// lane l owns query l%32 and, in s[kt][v], key 32 kt + 8 (v/4) + 4 hh + v%4.
-template <int D>
-__device__ __forceinline__ void qk_block(const bf16 *__restrict__ ks, const bf16x8 (&qf)[D / 16],
-                                         f32x16 (&s)[2], const FragOffsets<D> &fo) {
+// S^T[key][query] = K Q^T for one 64-key block and NG groups of 32 queries:
+// keys on the MFMA rows, so lane l owns query l%32 of each group and, in
+// s[g][kt][v], key 32 kt + 8 (v/4) + 4 hh + v%4.  Each K fragment read from
+// LDS feeds all NG groups.
+template <int D, int NG>
+__device__ __forceinline__ void qk_block(const bf16 *__restrict__ ks,
+                                         const bf16x8 (&qf)[NG][D / 16], f32x16 (&s)[NG][2],
+                                         const FragOffsets<D> &fo) {
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    s[kt] = f32x16{};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) s[g][kt] = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + 32 * kt * D + fo.k[st]);
-      s[kt] = mfma32(kf, qf[st], s[kt]);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(kf, qf[g][st], s[g][kt]);
     }
   }
 }
@@ -628,11 +633,13 @@ __device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], float sl2, float
   return lsum;
 }
 
-// O^T[d][query] += V^T P^T.  The V^T chunk a lane reads holds exactly the
-// keys of its P operand, in the same order (see vt_column).
-template <int D>
-__device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs, const bf16x8 (&pf)[2][2],
-                                         f32x16 (&o)[D / 32], const FragOffsets<D> &fo) {
+// O^T[d][query] += V^T P^T for NG groups.  The V^T chunk a lane reads holds
+// exactly the keys of its P operand, in the same order (see vt_column), and
+// feeds all NG groups.
+template <int D, int NG>
+__device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs,
+                                         const bf16x8 (&pf)[NG][2][2], f32x16 (&o)[NG][D / 32],
+                                         const FragOffsets<D> &fo) {
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -640,7 +647,8 @@ __device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs, const bf16
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vs + 32 * dt * kBN + fo.v[kt][uu]);
-        o[dt] = mfma32(vf, pf[kt][uu], o[dt]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) o[g][dt] = mfma32(vf, pf[g][kt][uu], o[g][dt]);
       }
     }
   }
@@ -654,17 +662,40 @@ __device__ __forceinline__ int padded_keys(int kvalid, int hh) {
   return n;
 }
 
-// One workgroup = 128 query rows (4 waves x 32) of one (batch, head, tile)
-// against all keys of the tile, then the audio keys; a 256-row unit of the
-// padded row space is split over two workgroups.
+// Query groups of 32 per wave (1 or 2): 2 halves the LDS fragment reads and
+// the K/V staging per flop, at one wave per SIMD.
+#ifndef TDP_ATTN_NG
+#define TDP_ATTN_NG 1
+#endif
+// 1: S of block j+1 is computed while block j is exponentiated (two S sets);
+// 0: each block's S is computed in its own step (one S set; with two query
+// groups the second group's S overlaps the first group's exp).
+// -1: 1 for head_dim 128 with one group, else 0 (measured: at head_dim 64 the
+// second S set costs more occupancy than the overlap gains).
+#ifndef TDP_ATTN_PIPE
+#define TDP_ATTN_PIPE (-1)
+#endif
+constexpr int kNG = TDP_ATTN_NG;
+template <int D>
+constexpr bool kPipeFor = TDP_ATTN_PIPE < 0 ? (D >= 128 && kNG == 1) : TDP_ATTN_PIPE != 0;
+constexpr int kCoreWaves = TDP_ATTN_WAVES;
+constexpr int kCoreRowsWG = kCoreWaves * 32 * kNG;   // query rows per attention workgroup
+static_assert(kUnit % kCoreRowsWG == 0, "a 256-row unit is split over whole workgroups");
+
+// One workgroup = kCoreWaves waves x kNG x 32 query rows of one (batch, head,
+// tile) against all keys of the tile, then the audio keys; a 256-row unit of
+// the padded row space is split over kUnit / kCoreRowsWG workgroups.
 //
-// Per 64-key block j the wave (1) takes the block max of S(j) and moves the
-// running max lazily (only when a block max exceeds it by more than kLazy,
-// so p <= 2^kLazy; the O rescale is rare and sits on a real branch),
-// (2) issues the HBM loads of K(j+2) and V(j+1), (3) computes S(j+1) on MFMA
-// while the VALU turns S(j) into bf16 P, (4) accumulates O += V(j) P(j), and
-// (5) stores the loaded blocks into the LDS buffers freed in block j-1.  K is
-// staged one block ahead of V, so two K and two V buffers suffice.
+// Per 64-key block j the wave (1) issues the direct loads of K(j+2) and
+// V(j+1) into the LDS buffers freed in block j-1, (2) computes S(j+1) on MFMA
+// while the VALU turns S(j) into bf16 P, (3) accumulates O += V(j) P(j), and
+// (4) waits for its loads and meets the others at the barrier.  K is staged
+// one block ahead of V, so two K and two V buffers suffice.  Without the
+// pipeline (head_dim 64) step j loads K(j+1) and V(j+1) and computes S(j)
+// itself, before its exp.
+//
+// Softmax: first with a static per-query bound (below); if that underflows
+// the whole tile is run again with the exact online softmax.
 //
 // Keys past the end of a segment are the zero rows the QKV stage writes into
 // the padding: score exactly 0, V row 0.  They only add the bf16 weight of a
@@ -677,12 +708,13 @@ __device__ __forceinline__ int padded_keys(int kvalid, int hh) {
 // walks a contiguous range of work items and the workgroups sharing a tile's
 // K/V run together on one L2.
 template <int D>
-__global__ __launch_bounds__(64 * TDP_ATTN_WAVES, 8 / TDP_ATTN_WAVES) void attn_core_kernel(CoreArgs a) {
+__global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_core_kernel(CoreArgs a) {
   __shared__ __attribute__((aligned(16))) CoreSmem<D> sm;
   constexpr int kSteps = D / 16;
   constexpr int kDT = D / 32;
-  constexpr int kRowsWG = TDP_ATTN_WAVES * 32;  // query rows per workgroup
-  constexpr int kSplit = kUnit / kRowsWG;      // workgroups per 256-row unit
+  constexpr int NG = kNG;
+  constexpr bool kPipe = kPipeFor<D>;
+  constexpr int kSplit = kUnit / kCoreRowsWG;   // workgroups per 256-row unit
 
   const int64_t G = gridDim.x;
   const int64_t bid = blockIdx.x;
@@ -708,7 +740,7 @@ __global__ __launch_bounds__(64 * TDP_ATTN_WAVES, 8 / TDP_ATTN_WAVES) void attn_
     q0 = static_cast<int32_t>((ua - static_cast<int64_t>(t) * a.n_aqb) * kUnit);
     audio_q = true;
   }
-  q0 += part * kRowsWG;
+  q0 += part * kCoreRowsWG;
   int64_t r0;
   int32_t len0;
   tile_rows(a.trb, t, a.n_rows, a.max_rows, &r0, &len0);
@@ -721,13 +753,17 @@ __global__ __launch_bounds__(64 * TDP_ATTN_WAVES, 8 / TDP_ATTN_WAVES) void attn_
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // Q fragments (B operand of S^T = K Q^T): query row wave*32 + l32.
+  // Q fragments (B operand of S^T = K Q^T): group g holds query row
+  // wave*32*NG + 32 g + l32.
   const bf16 *qsrc = audio_q ? a.qa + ((bh * a.a_pad) + q0) * D
                              : a.q + ((bh * a.n_pad) + pad0 + q0) * D;
-  bf16x8 qf[kSteps];
+  bf16x8 qf[NG][kSteps];
 #pragma unroll
-  for (int s = 0; s < kSteps; ++s)
-    qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + (wave * 32 + l32) * D + 16 * s + 8 * hh);
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+      qf[g][s] = *reinterpret_cast<const bf16x8 *>(qsrc + (wave * 32 * NG + 32 * g + l32) * D +
+                                                   16 * s + 8 * hh);
 
   // Segment 0: the tile's rows; segment 1: the audio rows.
   const bf16 *kseg0 = a.k + (bh * a.n_pad + pad0) * D;
@@ -747,56 +783,62 @@ __global__ __launch_bounds__(64 * TDP_ATTN_WAVES, 8 / TDP_ATTN_WAVES) void attn_
   const FragOffsets<D> fo(l32, hh);
   // Block j (clamped to the last block) of the tile-then-audio key sequence,
   // straight into an LDS buffer.
-  auto load_k = [&](int j, bf16 *buf) {
+  auto load_k = [&](int j, bf16 *buf) __attribute__((always_inline)) {
     j = min(j, nkb - 1);
     const bf16 *kb = j < nkb0 ? kseg0 + static_cast<int64_t>(j) * kBN * D
                               : kseg1 + static_cast<int64_t>(j - nkb0) * kBN * D;
     ds.load_k(kb, buf);
   };
-  auto load_v = [&](int j, bf16 *buf) {
+  auto load_v = [&](int j, bf16 *buf) __attribute__((always_inline)) {
     j = min(j, nkb - 1);
     const bool s0 = j < nkb0;
     ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0, buf);
   };
 
   const float sl2 = a.scale_log2;
-  // Static softmax bound (Cauchy-Schwarz): every score of this query obeys
+  // Static softmax bound (Cauchy-Schwarz): every score of a query obeys
   // s <= |q| * max_k |k|, over the tile's keys and the audio keys, so with
   // m_q = |q| max|k| sl2 (plus a rounding margin) every p = 2^(s sl2 - m_q)
   // is <= 1 and no running maximum is needed.  |q| is taken over the bf16 Q
   // row held in registers; max|k| comes from the QKV stage.
-  float m_q;
+  float m_q[NG];
   {
-    float qq = 0.f;
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = static_cast<float>(qf[st][e]);
-        qq = fmaf(x, x, qq);
-      }
-    qq += __shfl_xor(qq, 32);
     const uint32_t *km = a.kmax2 + bh * (a.T + 1);
     float kk = nkb0 > 0 ? __uint_as_float(km[t]) : 0.f;
     if (nkb1 > 0) kk = fmaxf(kk, __uint_as_float(km[a.T]));
-    m_q = sqrtf(qq) * sqrtf(kk) * sl2 * 1.0009765625f + 1e-30f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float qq = 0.f;
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = static_cast<float>(qf[g][st][e]);
+          qq = fmaf(x, x, qq);
+        }
+      qq += __shfl_xor(qq, 32);
+      m_q[g] = sqrtf(qq) * sqrtf(kk) * sl2 * 1.0009765625f + 1e-30f;
+    }
   }
 
-  f32x16 o[kDT];
-  float m_run = 0.f, l_run = 0.f;
-  f32x16 sa[2], sb[2];
+  f32x16 o[NG][kDT];
+  float m_run[NG], l_run[NG];
+  f32x16 sa[NG][2], sb[NG][2];   // S of two consecutive blocks (sb unused without kPipe)
 
   // K(0), V(0), K(1) into LDS; S(0).  The caller has passed a barrier since
   // any earlier reads of these buffers.
-  auto prologue = [&]() {
+  auto prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kDT; ++i) o[i] = f32x16{};
-    l_run = 0.f;
+    for (int g = 0; g < NG; ++g) {
+#pragma unroll
+      for (int i = 0; i < kDT; ++i) o[g][i] = f32x16{};
+      l_run[g] = 0.f;
+    }
     load_k(0, sm.k[0]);
     load_v(0, sm.v[0]);
-    load_k(1, sm.k[1]);
+    if constexpr (kPipe) load_k(1, sm.k[1]);
     loads_landed_barrier();
-    qk_block<D>(sm.k[0], qf, sa, fo);
+    if constexpr (kPipe) qk_block<D, NG>(sm.k[0], qf, sa, fo);
   };
 
   // One 64-key block.  EXACT = false: p = 2^(s sl2 - m_q) with the static
@@ -805,110 +847,119 @@ __global__ __launch_bounds__(64 * TDP_ATTN_WAVES, 8 / TDP_ATTN_WAVES) void attn_
   // p <= 2^kLazy; the O rescale is rare and sits on a real branch).  Loads
   // and S(j+1) run unconditionally so they share one basic block with the
   // exp; past the last block they re-read in-range data and the results are
-  // dropped, and the stores only refill buffers whose data was consumed in
-  // block j-1.
-  auto step = [&](auto exact_tag, int j, f32x16 (&scur)[2], f32x16 (&snext)[2]) {
+  // dropped.  K(j) and V(j-1) were consumed in block j-1, so their buffers
+  // take K(j+2) and V(j+1).
+  auto step = [&](auto exact_tag, int j, f32x16 (&scur)[NG][2], f32x16 (&snext)[NG][2]) __attribute__((always_inline)) {
     constexpr bool kExact = decltype(exact_tag)::value;
+    if constexpr (!kPipe) {
+      // K(j+1), V(j+1) into the buffers of block j-1, then S(j) from K(j).
+      load_k(j + 1, sm.k[(j + 1) & 1]);
+      load_v(j + 1, sm.v[(j + 1) & 1]);
+      qk_block<D, NG>(sm.k[j & 1], qf, scur, fo);
+    }
     if constexpr (kExact) {
-      const float mb = block_max(scur) * sl2;
-      if (__builtin_expect(__ballot(mb > m_run + kLazy) != 0, 0)) {
+      float mb[NG];
+      bool grow = false;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        mb[g] = block_max(scur[g]) * sl2;
+        grow = grow || (mb[g] > m_run[g] + kLazy);
+      }
+      if (__builtin_expect(__ballot(grow) != 0, 0)) {
         // Rare after the first block; the empty asm keeps this a real branch.
         asm volatile("" ::: "memory");
-        const float m_new = fmaxf(m_run, mb);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-        for (int i = 0; i < kDT; ++i)
+        for (int g = 0; g < NG; ++g) {
+          const float m_new = fmaxf(m_run[g], mb[g]);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) o[i][v] *= alpha;
-        l_run *= alpha;
-        m_run = m_new;
+          for (int i = 0; i < kDT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[g][i][v] *= alpha;
+          l_run[g] *= alpha;
+          m_run[g] = m_new;
+        }
       }
     }
-    const float m_use = kExact ? m_run : m_q;
-    // K(j) and V(j-1) were consumed in block j-1: their buffers are free.
-    load_k(j + 2, sm.k[j & 1]);
-    load_v(j + 1, sm.v[(j + 1) & 1]);
+    if constexpr (kPipe) {
+      load_k(j + 2, sm.k[j & 1]);
+      load_v(j + 1, sm.v[(j + 1) & 1]);
 #if TDP_ATTN_PRIO
-    __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_s_setprio(1);
 #endif
-    qk_block<D>(sm.k[(j + 1) & 1], qf, snext, fo);
+      qk_block<D, NG>(sm.k[(j + 1) & 1], qf, snext, fo);
 #if TDP_ATTN_PRIO
-    __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_s_setprio(0);
 #endif
-    bf16x8 pf[2][2];
-    const float lsum = exp_pack(scur, sl2, m_use, pf);
+    }
+    bf16x8 pf[NG][2][2];
     const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
-    const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_use)));
-    l_run += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
-    pv_block<D>(sm.v[j & 1], pf, o, fo);
-#if TDP_ATTN_SCHED == 1
-    // S(j+1) MFMAs interleaved with the exp of block j, then the P V MFMAs.
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    for (int g = 0; g < NG; ++g) {
+      const float m_use = kExact ? m_run[g] : m_q[g];
+      const float lsum = exp_pack(scur[g], sl2, m_use, pf[g]);
+      const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_use)));
+      l_run[g] += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-#elif TDP_ATTN_SCHED == 2
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-    }
-#endif
+    pv_block<D, NG>(sm.v[j & 1], pf, o, fo);
     loads_landed_barrier();
   };
 
-  prologue();
-  for (int j = 0; j < nkb; j += 2) {
-    step(std::false_type{}, j, sa, sb);
-    if (j + 1 < nkb) step(std::false_type{}, j + 1, sb, sa);
+  auto run = [&](auto exact_tag) __attribute__((always_inline)) {
+    prologue();
+    if constexpr (kPipe) {
+      for (int j = 0; j < nkb; j += 2) {
+        step(exact_tag, j, sa, sb);
+        if (j + 1 < nkb) step(exact_tag, j + 1, sb, sa);
+      }
+    } else {
+      for (int j = 0; j < nkb; ++j) step(exact_tag, j, sa, sa);
+    }
+  };
+  run(std::false_type{});
+  float l_tot[NG];
+  bool bad = false;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    l_tot[g] = l_run[g] + __shfl_xor(l_run[g], 32);
+    bad = bad || !(l_tot[g] >= 0x1p-90f);
   }
-  float l_tot = l_run + __shfl_xor(l_run, 32);
   // The bound can exceed the real maximum by so much that every p underflows
   // (huge |q||k| with no aligned key).  Then the workgroup runs the tile again
   // with the exact online softmax.
-  if (__syncthreads_or(!(l_tot >= 0x1p-90f))) {
-    m_run = -INFINITY;
-    prologue();
-    for (int j = 0; j < nkb; j += 2) {
-      step(std::true_type{}, j, sa, sb);
-      if (j + 1 < nkb) step(std::true_type{}, j + 1, sb, sa);
-    }
-    l_tot = l_run + __shfl_xor(l_run, 32);
+  if (__syncthreads_or(bad)) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) m_run[g] = -INFINITY;
+    run(std::true_type{});
+#pragma unroll
+    for (int g = 0; g < NG; ++g) l_tot[g] = l_run[g] + __shfl_xor(l_run[g], 32);
   }
 
-  const float inv = 1.0f / l_tot;
-  const int row = wave * 32 + l32;
-  if (row < nq) {
-    bf16 *dst = audio_q
-        ? a.oa + ((static_cast<int64_t>(t) * a.batch + b) * a.A + q0 + row) * a.hidden
-        : a.o + (b * a.n_rows + r0 + q0 + row) * a.hidden;
-    dst += h * D + 4 * hh;
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) {
+  for (int g = 0; g < NG; ++g) {
+    const float inv = 1.0f / l_tot[g];
+    const int row = wave * 32 * NG + 32 * g + l32;
+    if (row < nq) {
+      bf16 *dst = audio_q
+          ? a.oa + ((static_cast<int64_t>(t) * a.batch + b) * a.A + q0 + row) * a.hidden
+          : a.o + (b * a.n_rows + r0 + q0 + row) * a.hidden;
+      dst += h * D + 4 * hh;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        bf16x4 v4;
-        v4[0] = static_cast<bf16>(o[dt][4 * gg + 0] * inv);
-        v4[1] = static_cast<bf16>(o[dt][4 * gg + 1] * inv);
-        v4[2] = static_cast<bf16>(o[dt][4 * gg + 2] * inv);
-        v4[3] = static_cast<bf16>(o[dt][4 * gg + 3] * inv);
-        *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * gg) = v4;
+      for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          bf16x4 v4;
+          v4[0] = static_cast<bf16>(o[g][dt][4 * gg + 0] * inv);
+          v4[1] = static_cast<bf16>(o[g][dt][4 * gg + 1] * inv);
+          v4[2] = static_cast<bf16>(o[g][dt][4 * gg + 2] * inv);
+          v4[3] = static_cast<bf16>(o[g][dt][4 * gg + 3] * inv);
+          *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * gg) = v4;
+        }
       }
     }
   }
 }
 
-constexpr int kCoreRowsWG = TDP_ATTN_WAVES * 32;   // query rows per attention workgroup
 
 // ---------------------------------------------------------------------------
 // out_proj
@@ -1115,7 +1166,7 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
   a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
   const int64_t grid = ceil_div(a.total_units * (kUnit / kCoreRowsWG), 8) * 8;
-  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(64 * TDP_ATTN_WAVES), 0,
+  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(64 * kCoreWaves), 0,
                      stream, a);
 }
 
