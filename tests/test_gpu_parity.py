@@ -252,16 +252,32 @@ def test_multi_rank_sum_equals_single_rank(W):
     assert rel_err(_np(acc_a), _np(full.y_audio)) <= BLEND_TOL
 
 
-def test_repeat_runs_are_deterministic():
-    say("determinism d64")
-    inp = ti.make_inputs("d64_8x32x32")
+DETERMINISM_CASES = {
+    # head_dim 64: each block's S computed in its own step
+    "d64": ("d64_8x32x32", {}),
+    # head_dim 128 with audio: S(j+1) overlapped with block j, K staged two
+    # blocks ahead (a missing barrier there once let a wave's K(2) load
+    # overwrite K(0) while another wave still read it)
+    "d128_audio": ("audio_32x48x80", dict(grid=(8, 48, 80), heads=4)),
+}
+
+
+@pytest.mark.parametrize("case", list(DETERMINISM_CASES))
+def test_repeat_runs_are_deterministic(case):
+    """Five runs of the same step give bit-identical outputs."""
+    say("determinism", case)
+    base, kw = DETERMINISM_CASES[case]
+    inp = _variant(base, **kw) if kw else ti.make_inputs(base)
     s = _step(inp)
     s.run()
     torch.cuda.synchronize()
     a = s.y_global.clone()
-    s.run()
-    torch.cuda.synchronize()
-    assert torch.equal(a, s.y_global)
+    at = s.y_tiles.clone()
+    for _ in range(4):
+        s.run()
+        torch.cuda.synchronize()
+        assert torch.equal(at, s.y_tiles)
+        assert torch.equal(a, s.y_global)
 
 
 def _fallback_inputs():
@@ -279,10 +295,37 @@ def _fallback_inputs():
     return dataclasses.replace(base, wq=wq, wk=wk)
 
 
-def test_exact_fallback_when_static_bound_underflows():
-    """The static-bound pass underflows (every p < 2^-126) and the kernel must
-    rerun the tile with the exact online softmax."""
-    say("exact fallback")
+def _score_bounds(inp):
+    """Per tile (batch 0): the largest Cauchy-Schwarz bound |q| max|k| over
+    its queries and the largest score, both in log2 units (scale log2(e)/sqrt(d)),
+    max|k| over the tile's and the audio keys, as the kernel takes it."""
+    wl = inp.workload
+    d = wl.head_dim
+    p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    sl2 = 1.4426950408889634 / np.sqrt(d)
+    xa = inp.x_aud[0] if inp.x_aud is not None else np.zeros((0, wl.channels))
+    out = []
+    for t in range(p.tile_id.size):
+        r0, r1 = int(p.tile_row_begin[t]), int(p.tile_row_begin[t + 1])
+        seq = np.concatenate([inp.x_global[0, p.row_src[r0:r1]], xa]).astype(np.float64)
+        ang = np.concatenate([oracle.rope_angles(p.row_pos[r0:r1], d),
+                              np.zeros((len(xa), d // 2))])
+        u_max, s_max = 0.0, -np.inf
+        for h in range(wl.heads):
+            q = oracle.apply_rope((seq @ inp.wq)[:, h * d:(h + 1) * d], ang)
+            k = oracle.apply_rope((seq @ inp.wk)[:, h * d:(h + 1) * d], ang)
+            u = np.linalg.norm(q, axis=1) * np.linalg.norm(k, axis=1).max() * sl2
+            u_max = max(u_max, float(u.max()))
+            s_max = max(s_max, float((q @ k.T).max() * sl2))
+        out.append((u_max, s_max))
+    return out
+
+
+def test_exact_path_when_score_bound_is_large():
+    """|q| max|k| is far above the shift-free range (and above every real
+    score by > 150 in log2 units): the kernel must take the exact online
+    softmax for the whole tile."""
+    say("exact path, large bound")
     inp = _fallback_inputs()
     wl = inp.workload
     p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
@@ -296,6 +339,43 @@ def test_exact_fallback_when_static_bound_underflows():
     s_max = (q @ k.T).max(axis=1)
     gap = (np.linalg.norm(q, axis=1) * np.linalg.norm(k, axis=1).max() - s_max) * sl2
     assert gap.min() > 150 and np.abs(s_max * sl2).max() < 20
+    s = _step(inp)
+    s.run()
+    _check_full(inp, s)
+
+
+def test_shift_free_softmax_near_its_limit():
+    """Wq = c Wk: each query's own key scores at its bound, so with the bound
+    just under the shift-free limit (64 in log2 units) p reaches about 2^60."""
+    say("shift-free near limit")
+    base = _variant("tiny_2x16x16", grid=(2, 8, 12), tiling=((1, 0), (1, 0), (2, 4)),
+                    n_cond=3, n_cond_neg=1, n_audio=5)
+    u1 = max(u for u, _ in _score_bounds(dataclasses.replace(base, wq=base.wk.copy())))
+    c = 60.0 / u1
+    inp = dataclasses.replace(base, wq=ti.round_to_bf16(base.wk * c))
+    bounds = _score_bounds(inp)
+    say("  bounds", [(round(u, 1), round(sm, 1)) for u, sm in bounds])
+    assert 55.0 < max(u for u, _ in bounds) < 62.0
+    assert max(sm for _, sm in bounds) > 50.0
+    s = _step(inp)
+    s.run()
+    _check_full(inp, s)
+
+
+def test_shift_free_and_exact_workgroups_in_one_launch():
+    """Rows only tile 0 holds are scaled up: tile 0's bound leaves the
+    shift-free range (exact online softmax) while tile 1 stays inside it."""
+    say("mixed shift-free / exact")
+    base = _variant("tiny_2x16x16", grid=(2, 8, 12), tiling=((1, 0), (1, 0), (2, 4)),
+                    n_cond=3, n_cond_neg=1, n_audio=5)
+    F, H, W = base.workload.grid
+    x = base.x_global.copy()
+    n = np.arange(F * H * W)
+    x[:, n[(n % W) < 4]] *= 2.5     # columns 0-3 lie in tile 0 only (boxes [0,8), [4,12))
+    inp = dataclasses.replace(base, x_global=x)
+    bounds = _score_bounds(inp)
+    say("  bounds", [(round(u, 1), round(sm, 1)) for u, sm in bounds])
+    assert bounds[0][0] > 80.0 and bounds[1][0] < 48.0
     s = _step(inp)
     s.run()
     _check_full(inp, s)

@@ -243,6 +243,7 @@ struct QkvArgs {
   int32_t heads, hidden;
   int64_t n_pad;              // padded rows per (batch, head) slab of the outputs
   float log2_theta_step;      // -log2(rope_base) / p
+  float q_scale;              // log2(e) / sqrt(head_dim), applied to Q before rounding
   bf16 *q, *k, *vt;
   uint32_t *kmax2;            // [B][heads][T+1] float bits of the largest squared K norm
   int32_t n_tiles;
@@ -390,6 +391,12 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
             }
           }
         }
+        // Q carries the softmax scale in log2 units, so Q K^T is log2 of the
+        // unnormalized attention weight.
+        if (m == 0) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[v] *= a.q_scale;
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           bf16x4 v4;
@@ -494,7 +501,6 @@ struct CoreArgs {
   int64_t n_units, n_pad, a_pad, n_rows, units_per_bh, total_units;
   int32_t T, heads, batch, A, n_aqb, max_rows, hidden;
   const uint32_t *kmax2;      // [B][heads][T+1] float bits of the largest squared K norm
-  float scale_log2;           // log2(e) / sqrt(head_dim)
 };
 
 // LDS staging of one 64-key block, unpadded rows with an XOR swizzle of the
@@ -611,19 +617,19 @@ __device__ __forceinline__ float block_max(const f32x16 (&s)[2]) {
   return fmaxf(mx, __shfl_xor(mx, 32));
 }
 
-// P = 2^(s*sl2 - m) rounded to bf16 and packed as the B operands of
-// O^T += V^T P^T; step (kt, u) holds keys 32 kt + 16 u + {4 hh + 0..3,
+// P = 2^(s - m) (SHIFT) or 2^s rounded to bf16 and packed as the B operands
+// of O^T += V^T P^T; step (kt, u) holds keys 32 kt + 16 u + {4 hh + 0..3,
 // 8 + 4 hh + 0..3} = s[kt][8u .. 8u+7].  Returns the sum of the bf16 values.
-__device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], float sl2, float m,
-                                          bf16x8 (&pf)[2][2]) {
+template <bool SHIFT>
+__device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], float m, bf16x8 (&pf)[2][2]) {
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
   float lsum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[kt][v], sl2, -m));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[kt][v + 1], sl2, -m));
+      const float p0 = __builtin_amdgcn_exp2f(SHIFT ? s[kt][v] - m : s[kt][v]);
+      const float p1 = __builtin_amdgcn_exp2f(SHIFT ? s[kt][v + 1] - m : s[kt][v + 1]);
       const bf16x2 pp = {static_cast<bf16>(p0), static_cast<bf16>(p1)};
       pf[kt][v / 8][v % 8] = pp[0];
       pf[kt][v / 8][v % 8 + 1] = pp[1];
@@ -795,13 +801,16 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
     ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0, buf);
   };
 
-  const float sl2 = a.scale_log2;
-  // Static softmax bound (Cauchy-Schwarz): every score of a query obeys
-  // s <= |q| * max_k |k|, over the tile's keys and the audio keys, so with
-  // m_q = |q| max|k| sl2 (plus a rounding margin) every p = 2^(s sl2 - m_q)
-  // is <= 1 and no running maximum is needed.  |q| is taken over the bf16 Q
-  // row held in registers; max|k| comes from the QKV stage.
-  float m_q[NG];
+  // Softmax without a running maximum.  Q carries log2(e)/sqrt(d), so a score
+  // s = q.k is log2 of the unnormalized weight and, by Cauchy-Schwarz,
+  // |s| <= U = |q| max|k| over the tile's and the audio keys (|q| from the
+  // bf16 row in registers, max|k| from the QKV stage).  When U <= kNoShift
+  // for every query of the workgroup, p = 2^s needs no shift: every p lies
+  // in [2^-kNoShift, 2^kNoShift], normal in bf16 and fp32, the sums stay
+  // finite, and the final division by l cancels the missing common factor.
+  // Otherwise the workgroup runs the exact online softmax instead.
+  constexpr float kNoShift = 64.f;
+  bool need_exact = false;
   {
     const uint32_t *km = a.kmax2 + bh * (a.T + 1);
     float kk = nkb0 > 0 ? __uint_as_float(km[t]) : 0.f;
@@ -817,7 +826,8 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
           qq = fmaf(x, x, qq);
         }
       qq += __shfl_xor(qq, 32);
-      m_q[g] = sqrtf(qq) * sqrtf(kk) * sl2 * 1.0009765625f + 1e-30f;
+      const float u = sqrtf(qq) * sqrtf(kk) * 1.0009765625f;
+      need_exact = need_exact || !(u <= kNoShift);   // NaN included
     }
   }
 
@@ -825,8 +835,9 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
   float m_run[NG], l_run[NG];
   f32x16 sa[NG][2], sb[NG][2];   // S of two consecutive blocks (sb unused without kPipe)
 
-  // K(0), V(0), K(1) into LDS; S(0).  The caller has passed a barrier since
-  // any earlier reads of these buffers.
+  // K(0), V(0), K(1) into LDS; S(0), then a barrier so that no wave's load of
+  // K(2) into k[0] overtakes another wave's reads of K(0).  The caller has
+  // passed a barrier since any earlier reads of these buffers.
   auto prologue = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -838,11 +849,14 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
     load_v(0, sm.v[0]);
     if constexpr (kPipe) load_k(1, sm.k[1]);
     loads_landed_barrier();
-    if constexpr (kPipe) qk_block<D, NG>(sm.k[0], qf, sa, fo);
+    if constexpr (kPipe) {
+      qk_block<D, NG>(sm.k[0], qf, sa, fo);
+      // Step 0 loads K(2) into k[0]: every wave must have read K(0) first.
+      __syncthreads();
+    }
   };
 
-  // One 64-key block.  EXACT = false: p = 2^(s sl2 - m_q) with the static
-  // bound.  EXACT = true: the exact online softmax with a lazily moved
+  // One 64-key block.  EXACT = false: p = 2^s (see above).  EXACT = true: the exact online softmax with a lazily moved
   // maximum (moved only when a block max exceeds it by more than kLazy, so
   // p <= 2^kLazy; the O rescale is rare and sits on a real branch).  Loads
   // and S(j+1) run unconditionally so they share one basic block with the
@@ -862,7 +876,7 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
       bool grow = false;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        mb[g] = block_max(scur[g]) * sl2;
+        mb[g] = block_max(scur[g]);
         grow = grow || (mb[g] > m_run[g] + kLazy);
       }
       if (__builtin_expect(__ballot(grow) != 0, 0)) {
@@ -893,13 +907,17 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
 #endif
     }
     bf16x8 pf[NG][2][2];
-    const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const float m_use = kExact ? m_run[g] : m_q[g];
-      const float lsum = exp_pack(scur[g], sl2, m_use, pf[g]);
-      const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_use)));
-      l_run[g] += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
+      const float lsum = exp_pack<kExact>(scur[g], kExact ? m_run[g] : 0.f, pf[g]);
+      if constexpr (kExact) {
+        // a padded key scores exactly 0: it added bf16(2^-m) to lsum
+        const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
+        const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_run[g])));
+        l_run[g] += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
+      } else {
+        l_run[g] += lsum;   // padded keys (p = 1 each) are taken off after the loop
+      }
     }
     pv_block<D, NG>(sm.v[j & 1], pf, o, fo);
     loads_landed_barrier();
@@ -916,18 +934,23 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
       for (int j = 0; j < nkb; ++j) step(exact_tag, j, sa, sa);
     }
   };
-  run(std::false_type{});
   float l_tot[NG];
-  bool bad = false;
+  bool exact = __syncthreads_or(need_exact);
+  if (!exact) {
+    run(std::false_type{});
+    // l >= 2^-kNoShift here unless the inputs hold Inf or NaN; such rows
+    // take the exact path too.
+    bool bad = false;
+    const float pad_ones = static_cast<float>(nz0 + nz1);
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    l_tot[g] = l_run[g] + __shfl_xor(l_run[g], 32);
-    bad = bad || !(l_tot[g] >= 0x1p-90f);
+    for (int g = 0; g < NG; ++g) {
+      l_run[g] -= pad_ones;
+      l_tot[g] = l_run[g] + __shfl_xor(l_run[g], 32);
+      bad = bad || !(l_tot[g] >= 0x1p-90f);
+    }
+    exact = __syncthreads_or(bad);
   }
-  // The bound can exceed the real maximum by so much that every p underflows
-  // (huge |q||k| with no aligned key).  Then the workgroup runs the tile again
-  // with the exact online softmax.
-  if (__syncthreads_or(bad)) {
+  if (exact) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) m_run[g] = -INFINITY;
     run(std::true_type{});
@@ -1112,6 +1135,7 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
   a.heads = c.d->heads;
   a.hidden = L.hidden;
   a.log2_theta_step = -std::log2(static_cast<double>(c.d->rope_base)) / (D / 6);
+  a.q_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
   // tile rows
   a.x = x_tiles;
   a.x_rows = c.n_rows;
@@ -1164,7 +1188,6 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.max_rows = c.max_rows;
   a.hidden = L.hidden;
   a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
-  a.scale_log2 = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
   const int64_t grid = ceil_div(a.total_units * (kUnit / kCoreRowsWG), 8) * 8;
   hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(64 * kCoreWaves), 0,
                      stream, a);
