@@ -63,7 +63,8 @@ struct Layout {
   int32_t hidden = 0;
   size_t off_wt = 0, off_wot = 0, off_pad_begin = 0, off_blk_tile = 0, off_blk_q0 = 0;
   size_t off_kmax = 0;  // [B][heads][T+1] largest squared K row norm per tile (slot T: audio)
-  size_t off_q = 0, off_k = 0, off_vt = 0, off_qa = 0, off_ka = 0, off_vta = 0;
+  int64_t vt_cols = 0;  // columns per V^T row: the padded tile rows, then the padded audio rows
+  size_t off_q = 0, off_k = 0, off_vt = 0, off_qa = 0, off_ka = 0;
   size_t off_o = 0, off_oa = 0, total = 0;
 };
 
@@ -85,6 +86,9 @@ tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, 
   L->n_pad = L->npb * kBlk;
   L->a_pad = ceil_div(d->n_audio, kUnit) * kUnit;
   L->n_aqb = static_cast<int32_t>(L->a_pad / kUnit);
+  L->vt_cols = L->n_pad + L->a_pad;
+  // lane offsets into a (batch, head) slab of V^T are 32-bit byte offsets
+  if (L->vt_cols * d->head_dim * 2 > static_cast<int64_t>(UINT32_MAX)) return TDP_ERR_UNSUPPORTED;
   const size_t B = d->batch, H = d->heads, D = d->head_dim, T = n_tiles, A = d->n_audio;
   size_t off = 0;
   auto take = [&off](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
@@ -96,10 +100,9 @@ tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, 
   L->off_kmax = take(B * H * (T + 1) * 4);
   L->off_q = take(B * H * L->n_pad * D * 2);
   L->off_k = take(B * H * L->n_pad * D * 2);
-  L->off_vt = take(B * H * L->n_pad * D * 2);
+  L->off_vt = take(B * H * static_cast<size_t>(L->vt_cols) * D * 2);
   L->off_qa = take(B * H * L->a_pad * D * 2);
   L->off_ka = take(B * H * L->a_pad * D * 2);
-  L->off_vta = take(B * H * L->a_pad * D * 2);
   L->off_o = take(B * static_cast<size_t>(n_rows) * hidden * 2);
   L->off_oa = take(T * B * A * hidden * 2);
   L->total = off;
@@ -241,7 +244,9 @@ struct QkvArgs {
   const float *row_pos;       // [n_rows][3][2]
   const bf16 *wt;             // [3][hidden][C]
   int32_t heads, hidden;
-  int64_t n_pad;              // padded rows per (batch, head) slab of the outputs
+  int64_t n_pad;              // padded rows per (batch, head) slab of Q and K
+  int64_t vt_cols;            // columns per V^T row
+  int64_t vt_col0;            // first V^T column of this launch's rows (audio: after the tiles)
   float log2_theta_step;      // -log2(rope_base) / p
   float q_scale;              // log2(e) / sqrt(head_dim), applied to Q before rounding
   bf16 *q, *k, *vt;
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
             bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     } else {
-      bf16 *dst = a.vt + slab * D * a.n_pad + pad_row0;
+      bf16 *dst = a.vt + slab * D * a.vt_cols + a.vt_col0 + pad_row0;
 #pragma unroll
       for (int i = 0; i < D * kBlk / 8 / 128; ++i) {
         const int piece = ct + i * 128;
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
         const bf16 *src = sOut + d * kVtRow + col;
         const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(src);
         const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(src + 4);
-        *reinterpret_cast<bf16x8 *>(dst + d * a.n_pad + col) =
+        *reinterpret_cast<bf16x8 *>(dst + d * a.vt_cols + col) =
             bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     }
@@ -494,17 +499,17 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
 // ---------------------------------------------------------------------------
 
 struct CoreArgs {
-  const bf16 *q, *k, *vt, *qa, *ka, *vta;
+  const bf16 *q, *k, *vt, *qa, *ka;   // vt: [B*H][D][vt_cols], tile columns then audio columns
   bf16 *o, *oa;
   const int32_t *blk_tile, *blk_q0, *pad_begin;
   const int64_t *trb;
-  int64_t n_units, n_pad, a_pad, n_rows, units_per_bh, total_units;
+  int64_t n_units, n_pad, a_pad, vt_cols, n_rows, units_per_bh, total_units;
   int32_t T, heads, batch, A, n_aqb, max_rows, hidden;
   const uint32_t *kmax2;      // [B][heads][T+1] float bits of the largest squared K norm
 };
 
 // LDS staging of one 64-key block, unpadded rows with an XOR swizzle of the
-// 16-byte chunks inside a row:
+// 16-byte chunks inside a row (the layout; the kernel declares the buffers):
 //   K   [64 keys][D]: chunk p of row r holds head-dim chunk p ^ ksw(r)
 //   V^T [D][64 keys]: chunk p of row d holds key chunk p ^ vsw(d)
 // Both swizzles make the 16 lanes of an LDS read phase hit 16 different
@@ -515,8 +520,6 @@ template <int D>
 struct CoreSmem {
   static constexpr int kRB = 2 * D;                 // bytes per K row
   static constexpr int kCPR = D / 8;                // 16-byte chunks per K row
-  bf16 k[2][kBN * D];
-  bf16 v[2][D * kBN];
   __device__ static int ksw(int r) { return (r / (256 / kRB)) % kCPR; }
   __device__ static int vsw(int d) { return (d / 2) % 8; }
 };
@@ -528,10 +531,10 @@ struct DirectStage {
   static constexpr int kKUnits = kBN * D * 2 / 1024 / kWaves;   // 1 KB loads per wave, K block
   static constexpr int kVUnits = D * kBN * 2 / 1024 / kWaves;   // 1 KB loads per wave, V^T block
   uint32_t koff[kKUnits];                 // byte offset of this lane's chunk in a K block
-  uint32_t voff0[kVUnits], voff1[kVUnits];  // ... in a V^T block of segment 0 / 1
+  uint32_t voff[kVUnits];                 // ... in a V^T block (rows of vstr columns)
   int wave;                               // wave-uniform
 
-  __device__ DirectStage(int wave_, int lane, int32_t vstr0, int32_t vstr1) : wave(wave_) {
+  __device__ DirectStage(int wave_, int lane, uint32_t vstr) : wave(wave_) {
 #pragma unroll
     for (int i = 0; i < kKUnits; ++i) {
       const int byte = (i * kWaves + wave) * 1024 + 16 * lane;
@@ -543,8 +546,7 @@ struct DirectStage {
       const int byte = (i * kWaves + wave) * 1024 + 16 * lane;
       const int d = byte / (2 * kBN), p = (byte % (2 * kBN)) / 16;
       const uint32_t col = 8 * (p ^ CoreSmem<D>::vsw(d));
-      voff0[i] = 2u * (static_cast<uint32_t>(d) * static_cast<uint32_t>(vstr0) + col);
-      voff1[i] = 2u * (static_cast<uint32_t>(d) * static_cast<uint32_t>(vstr1) + col);
+      voff[i] = 2u * (static_cast<uint32_t>(d) * vstr + col);
     }
   }
   // kblk / vblk: wave-uniform block bases; lane offsets are 32-bit.
@@ -555,11 +557,11 @@ struct DirectStage {
       __builtin_amdgcn_global_load_lds((gvoid_t *)(base + koff[i]),
                                        (lvoid_t *)(kbuf + (i * kWaves + wave) * 512), 16, 0, 0);
   }
-  __device__ void load_v(const bf16 *vblk, bool seg0, bf16 *vbuf) const {
+  __device__ void load_v(const bf16 *vblk, bf16 *vbuf) const {
     const char *base = reinterpret_cast<const char *>(vblk);
 #pragma unroll
     for (int i = 0; i < kVUnits; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(base + (seg0 ? voff0[i] : voff1[i])),
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(base + voff[i]),
                                        (lvoid_t *)(vbuf + (i * kWaves + wave) * 512), 16, 0, 0);
   }
 };
@@ -715,7 +717,20 @@ static_assert(kUnit % kCoreRowsWG == 0, "a 256-row unit is split over whole work
 // K/V run together on one L2.
 template <int D>
 __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_core_kernel(CoreArgs a) {
-  __shared__ __attribute__((aligned(16))) CoreSmem<D> sm;
+  // Two K and two V^T buffers, as four separate arrays: a direct load into one
+  // and fragment reads from another are then provably disjoint, so the
+  // compiler does not make the reads wait for the loads.  Every buffer choice
+  // below is a compile-time parity.
+  __shared__ __attribute__((aligned(16))) bf16 sk0[kBN * D], sk1[kBN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sv0[D * kBN], sv1[D * kBN];
+  auto kbuf = [&](auto par) -> bf16 * {
+    if constexpr (decltype(par)::value) return sk1; else return sk0;
+  };
+  auto vbuf = [&](auto par) -> bf16 * {
+    if constexpr (decltype(par)::value) return sv1; else return sv0;
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   constexpr int kSteps = D / 16;
   constexpr int kDT = D / 32;
   constexpr int NG = kNG;
@@ -773,10 +788,9 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
 
   // Segment 0: the tile's rows; segment 1: the audio rows.
   const bf16 *kseg0 = a.k + (bh * a.n_pad + pad0) * D;
-  const bf16 *vseg0 = a.vt + bh * D * a.n_pad + pad0;
+  const bf16 *vseg0 = a.vt + bh * D * a.vt_cols + pad0;
   const bf16 *kseg1 = a.ka + bh * a.a_pad * D;
-  const bf16 *vseg1 = a.vta + bh * D * a.a_pad;
-  const int32_t vstr0 = static_cast<int32_t>(a.n_pad), vstr1 = static_cast<int32_t>(a.a_pad);
+  const bf16 *vseg1 = a.vt + bh * D * a.vt_cols + a.n_pad;
   const int nkb0 = static_cast<int>(ceil_div(len0, kBN));
   const int nkb1 = static_cast<int>(ceil_div(a.A, kBN));
   const int nkb = nkb0 + nkb1;
@@ -785,7 +799,8 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
   const int nz0 = nkb0 > 0 ? padded_keys(len0 - (nkb0 - 1) * kBN, hh) : 0;
   const int nz1 = nkb1 > 0 ? padded_keys(a.A - (nkb1 - 1) * kBN, hh) : 0;
 
-  const DirectStage<D> ds(__builtin_amdgcn_readfirstlane(wave), lane, vstr0, vstr1);
+  const DirectStage<D> ds(__builtin_amdgcn_readfirstlane(wave), lane,
+                          static_cast<uint32_t>(a.vt_cols));
   const FragOffsets<D> fo(l32, hh);
   // Block j (clamped to the last block) of the tile-then-audio key sequence,
   // straight into an LDS buffer.
@@ -798,7 +813,7 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
   auto load_v = [&](int j, bf16 *buf) __attribute__((always_inline)) {
     j = min(j, nkb - 1);
     const bool s0 = j < nkb0;
-    ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, s0, buf);
+    ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, buf);
   };
 
   // Softmax without a running maximum.  Q carries log2(e)/sqrt(d), so a score
@@ -845,12 +860,12 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
       for (int i = 0; i < kDT; ++i) o[g][i] = f32x16{};
       l_run[g] = 0.f;
     }
-    load_k(0, sm.k[0]);
-    load_v(0, sm.v[0]);
-    if constexpr (kPipe) load_k(1, sm.k[1]);
+    load_k(0, sk0);
+    load_v(0, sv0);
+    if constexpr (kPipe) load_k(1, sk1);
     loads_landed_barrier();
     if constexpr (kPipe) {
-      qk_block<D, NG>(sm.k[0], qf, sa, fo);
+      qk_block<D, NG>(sk0, qf, sa, fo);
       // Step 0 loads K(2) into k[0]: every wave must have read K(0) first.
       __syncthreads();
     }
@@ -862,14 +877,18 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
   // and S(j+1) run unconditionally so they share one basic block with the
   // exp; past the last block they re-read in-range data and the results are
   // dropped.  K(j) and V(j-1) were consumed in block j-1, so their buffers
-  // take K(j+2) and V(j+1).
-  auto step = [&](auto exact_tag, int j, f32x16 (&scur)[NG][2], f32x16 (&snext)[NG][2]) __attribute__((always_inline)) {
+  // take K(j+2) and V(j+1).  PAR = j % 2.
+  auto step = [&](auto exact_tag, auto par, int j, f32x16 (&scur)[NG][2],
+                  f32x16 (&snext)[NG][2]) __attribute__((always_inline)) {
     constexpr bool kExact = decltype(exact_tag)::value;
+    constexpr int kPar = decltype(par)::value;
+    const std::integral_constant<int, kPar> cur{};
+    const std::integral_constant<int, 1 - kPar> oth{};
     if constexpr (!kPipe) {
       // K(j+1), V(j+1) into the buffers of block j-1, then S(j) from K(j).
-      load_k(j + 1, sm.k[(j + 1) & 1]);
-      load_v(j + 1, sm.v[(j + 1) & 1]);
-      qk_block<D, NG>(sm.k[j & 1], qf, scur, fo);
+      load_k(j + 1, kbuf(oth));
+      load_v(j + 1, vbuf(oth));
+      qk_block<D, NG>(kbuf(cur), qf, scur, fo);
     }
     if constexpr (kExact) {
       float mb[NG];
@@ -896,12 +915,12 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
       }
     }
     if constexpr (kPipe) {
-      load_k(j + 2, sm.k[j & 1]);
-      load_v(j + 1, sm.v[(j + 1) & 1]);
+      load_k(j + 2, kbuf(cur));
+      load_v(j + 1, vbuf(oth));
 #if TDP_ATTN_PRIO
       __builtin_amdgcn_s_setprio(1);
 #endif
-      qk_block<D, NG>(sm.k[(j + 1) & 1], qf, snext, fo);
+      qk_block<D, NG>(kbuf(oth), qf, snext, fo);
 #if TDP_ATTN_PRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
@@ -919,19 +938,20 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
         l_run[g] += lsum;   // padded keys (p = 1 each) are taken off after the loop
       }
     }
-    pv_block<D, NG>(sm.v[j & 1], pf, o, fo);
+    pv_block<D, NG>(vbuf(cur), pf, o, fo);
     loads_landed_barrier();
   };
 
   auto run = [&](auto exact_tag) __attribute__((always_inline)) {
     prologue();
-    if constexpr (kPipe) {
-      for (int j = 0; j < nkb; j += 2) {
-        step(exact_tag, j, sa, sb);
-        if (j + 1 < nkb) step(exact_tag, j + 1, sb, sa);
+    for (int j = 0; j < nkb; j += 2) {
+      if constexpr (kPipe) {
+        step(exact_tag, P0{}, j, sa, sb);
+        if (j + 1 < nkb) step(exact_tag, P1{}, j + 1, sb, sa);
+      } else {
+        step(exact_tag, P0{}, j, sa, sa);
+        if (j + 1 < nkb) step(exact_tag, P1{}, j + 1, sa, sa);
       }
-    } else {
-      for (int j = 0; j < nkb; ++j) step(exact_tag, j, sa, sa);
     }
   };
   float l_tot[NG];
@@ -1140,6 +1160,8 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
   a.x = x_tiles;
   a.x_rows = c.n_rows;
   a.n_pad = L.n_pad;
+  a.vt_cols = L.vt_cols;
+  a.vt_col0 = 0;
   a.q = ws_at<bf16>(c.ws, L.off_q);
   a.k = ws_at<bf16>(c.ws, L.off_k);
   a.vt = ws_at<bf16>(c.ws, L.off_vt);
@@ -1149,9 +1171,9 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
     a.x = x_audio;
     a.x_rows = c.d->n_audio;
     a.n_pad = L.a_pad;
+    a.vt_col0 = L.n_pad;
     a.q = ws_at<bf16>(c.ws, L.off_qa);
     a.k = ws_at<bf16>(c.ws, L.off_ka);
-    a.vt = ws_at<bf16>(c.ws, L.off_vta);
     hipLaunchKernelGGL((qkv_rope_kernel<TX, D, true>),
                        dim3(static_cast<uint32_t>(L.a_pad / kBlk), c.d->batch), dim3(kThreads),
                        0, stream, a);
@@ -1167,7 +1189,6 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.vt = ws_at<bf16>(c.ws, L.off_vt);
   a.qa = ws_at<bf16>(c.ws, L.off_qa);
   a.ka = ws_at<bf16>(c.ws, L.off_ka);
-  a.vta = ws_at<bf16>(c.ws, L.off_vta);
   a.o = ws_at<bf16>(c.ws, L.off_o);
   a.oa = ws_at<bf16>(c.ws, L.off_oa);
   a.blk_tile = ws_at<int32_t>(c.ws, L.off_blk_tile);
@@ -1177,6 +1198,7 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.n_units = L.npb / (kUnit / kBlk);
   a.n_pad = L.n_pad;
   a.a_pad = L.a_pad;
+  a.vt_cols = L.vt_cols;
   a.n_rows = c.n_rows;
   a.units_per_bh = a.n_units + static_cast<int64_t>(c.n_tiles) * L.n_aqb;
   a.total_units = a.units_per_bh * c.d->batch * c.d->heads;
