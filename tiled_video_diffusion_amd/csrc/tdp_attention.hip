@@ -207,6 +207,22 @@ __device__ inline int vt_column(int x) {
   return (x & ~12) | (q2 << 2);
 }
 
+// Q, K and V^T are written once with a non-temporal hint (measured on the
+// 16-tile step: 3 GB in 0.65 ms instead of 0.93).  The attention core's O
+// stays an ordinary store and load: the output projection reads it right
+// after, and the part still in the last-level cache then hits (a
+// non-temporal O read measured 0.55 ms instead of 0.34).
+#ifndef TDP_STREAM_HINTS
+#define TDP_STREAM_HINTS 1
+#endif
+__device__ __forceinline__ void store_stream(bf16x8 *p, bf16x8 v) {
+#if TDP_STREAM_HINTS
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
 // Workgroup barrier ordering LDS only: waves exchange data through LDS, so
 // outstanding global stores need not complete first (a plain __syncthreads
 // would wait for them).
@@ -470,8 +486,8 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
         const bf16 *src = sOut + r * kQkRow + col;
         const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(src);
         const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(src + 4);
-        *reinterpret_cast<bf16x8 *>(dst + r * D + col) =
-            bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        store_stream(reinterpret_cast<bf16x8 *>(dst + r * D + col),
+                     bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
     } else {
       bf16 *dst = a.vt + slab * D * a.vt_cols + a.vt_col0 + pad_row0;
@@ -482,8 +498,8 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
         const bf16 *src = sOut + d * kVtRow + col;
         const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(src);
         const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(src + 4);
-        *reinterpret_cast<bf16x8 *>(dst + d * a.vt_cols + col) =
-            bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        store_stream(reinterpret_cast<bf16x8 *>(dst + d * a.vt_cols + col),
+                     bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
       }
     }
     if (loader) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1015,11 +1031,19 @@ __device__ inline void store_y<float>(float *p, float v) { *p = v; }
 template <>
 __device__ inline void store_y<bf16>(bf16 *p, float v) { *p = static_cast<bf16>(v); }
 
-// Y[M][128] = O[M][hidden] Wo; one workgroup = 128 rows (4 waves x 32), all
-// 128 outputs.  Wo^T is staged through LDS 64 k at a time and shared by the
-// four waves; O rows are read straight from HBM as A operands.
+// Y[M][128] = O[M][hidden] Wo; one workgroup = kOutWaves x 32 rows, all 128
+// outputs.  Wo^T is staged through LDS 64 k at a time and shared by the
+// waves (every workgroup streams all of Wo^T, so more rows per workgroup
+// means fewer passes over it); O rows are read straight from HBM as A
+// operands.
+#ifndef TDP_OUT_WAVES
+#define TDP_OUT_WAVES 4
+#endif
+constexpr int kOutWaves = TDP_OUT_WAVES;
+constexpr int kOutThreads = 64 * kOutWaves;
+constexpr int kOutRows = 32 * kOutWaves;
 template <typename TY>
-__global__ __launch_bounds__(kThreads, 2) void out_proj_kernel(const bf16 *__restrict__ o,
+__global__ __launch_bounds__(kOutThreads, 8 / kOutWaves) void out_proj_kernel(const bf16 *__restrict__ o,
                                                                const bf16 *__restrict__ wot,
                                                                TY *__restrict__ y, int64_t M,
                                                                int32_t hidden) {
@@ -1028,7 +1052,7 @@ __global__ __launch_bounds__(kThreads, 2) void out_proj_kernel(const bf16 *__res
   __shared__ __attribute__((aligned(16))) bf16 sB[kC * kRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32 + l32;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kOutRows + wave * 32 + l32;
   const bool valid = row < M;
   const bf16 *arow = o + (valid ? row : 0) * hidden;
   f32x16 acc[4];
@@ -1037,8 +1061,8 @@ __global__ __launch_bounds__(kThreads, 2) void out_proj_kernel(const bf16 *__res
   for (int k0 = 0; k0 < hidden; k0 += kK) {
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < kC * kK / 8 / kThreads; ++i) {
-      const int c = threadIdx.x + i * kThreads;
+    for (int i = 0; i < kC * kK / 8 / kOutThreads; ++i) {
+      const int c = threadIdx.x + i * kOutThreads;
       const int r = c / (kK / 8), col = (c % (kK / 8)) * 8;
       *reinterpret_cast<bf16x8 *>(&sB[r * kRow + col]) =
           *reinterpret_cast<const bf16x8 *>(wot + static_cast<int64_t>(r) * hidden + k0 + col);
@@ -1056,7 +1080,7 @@ __global__ __launch_bounds__(kThreads, 2) void out_proj_kernel(const bf16 *__res
     }
   }
   // acc[ct][v]: row 8 (v/4) + 4 hh + v%4 of the wave's 32, column 32 ct + l32
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * 128 + wave * 32;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kOutRows + wave * 32;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
@@ -1270,22 +1294,22 @@ extern "C" tdp_status tdp_attn_out_proj(const tdp_attn_desc *desc, int32_t n_til
   const hipStream_t stream = as_stream(hip_stream);
   const bf16 *wot = ws_at<bf16>(workspace, L.off_wot);
   const int64_t M = static_cast<int64_t>(desc->batch) * n_rows;
-  if (ceil_div(M, 128) > INT32_MAX) return TDP_ERR_ARG;
-  const dim3 grid(static_cast<uint32_t>(ceil_div(M, 128)));
+  if (ceil_div(M, kOutRows) > INT32_MAX) return TDP_ERR_ARG;
+  const dim3 grid(static_cast<uint32_t>(ceil_div(M, kOutRows)));
   if (desc->y_dtype == TDP_F32) {
-    hipLaunchKernelGGL(out_proj_kernel<float>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(out_proj_kernel<float>, grid, dim3(kOutThreads), 0, stream,
                        ws_at<bf16>(workspace, L.off_o), wot, static_cast<float *>(y_tiles), M,
                        L.hidden);
   } else {
-    hipLaunchKernelGGL(out_proj_kernel<bf16>, grid, dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL(out_proj_kernel<bf16>, grid, dim3(kOutThreads), 0, stream,
                        ws_at<bf16>(workspace, L.off_o), wot, static_cast<bf16 *>(y_tiles), M,
                        L.hidden);
   }
   if ((s = launch_status()) != TDP_OK) return s;
   if (desc->n_audio > 0) {
     const int64_t Ma = static_cast<int64_t>(n_tiles) * desc->batch * desc->n_audio;
-    hipLaunchKernelGGL(out_proj_kernel<float>, dim3(static_cast<uint32_t>(ceil_div(Ma, 128))),
-                       dim3(kThreads), 0, stream, ws_at<bf16>(workspace, L.off_oa), wot,
+    hipLaunchKernelGGL(out_proj_kernel<float>, dim3(static_cast<uint32_t>(ceil_div(Ma, kOutRows))),
+                       dim3(kOutThreads), 0, stream, ws_at<bf16>(workspace, L.off_oa), wot,
                        y_audio_tiles, Ma, L.hidden);
     s = launch_status();
   }
