@@ -32,9 +32,20 @@
 #ifndef TDP_ATTN_PRIO
 #define TDP_ATTN_PRIO 0
 #endif
-// Waves (of 32 query rows each) per attention workgroup: 4 or 8.
+// Waves (of 32 query rows each) per attention workgroup, 4 or 8, and keys
+// per iteration, 64 or 128; 0 = per head dim (measured best: 8 waves and
+// 128-key blocks at head_dim 128, one workgroup per CU; 4 waves and 64-key
+// blocks at head_dim 64).
 #ifndef TDP_ATTN_WAVES
-#define TDP_ATTN_WAVES 4
+#define TDP_ATTN_WAVES 0
+#endif
+#ifndef TDP_ATTN_BN
+#define TDP_ATTN_BN 0
+#endif
+// Query groups of 32 per wave (1 or 2): 2 halves the LDS fragment reads and
+// the K/V staging per flop, at one wave per SIMD.
+#ifndef TDP_ATTN_NG
+#define TDP_ATTN_NG 1
 #endif
 
 namespace tdp {
@@ -46,10 +57,22 @@ typedef __attribute__((address_space(3))) void lvoid_t;   // LDS pointer
 constexpr int kC = 128;       // channels per token row
 constexpr int kBlk = 128;     // rows per block of the padded row space (one QKV workgroup)
 constexpr int kUnit = 256;    // tiles are padded to whole units of this many rows
-constexpr int kBN = 64;       // keys per attention iteration
 constexpr int kThreads = 256;
 constexpr float kLazy = 8.0f; // log2 headroom before the running softmax max is moved
-static_assert(kUnit % kBlk == 0 && kUnit % kBN == 0, "tile padding covers whole blocks");
+static_assert(kUnit % kBlk == 0, "tile padding covers whole blocks");
+constexpr int kNG = TDP_ATTN_NG;
+
+// Shape of the attention core for one head dim.
+template <int D>
+struct CoreShape {
+  static constexpr int kBN = TDP_ATTN_BN ? TDP_ATTN_BN : (D >= 128 ? 128 : 64);   // keys per iteration
+  static constexpr int kKT = kBN / 32;                                            // 32-key MFMA tiles
+  static constexpr int kWaves = TDP_ATTN_WAVES ? TDP_ATTN_WAVES : (D >= 128 ? 8 : 4);
+  static constexpr int kRowsWG = kWaves * 32 * kNG;   // query rows per workgroup
+  static_assert(kBN == 64 || kBN == 128, "64- or 128-key blocks");
+  static_assert(kUnit % kBN == 0, "tile padding covers whole key blocks");
+  static_assert(kUnit % kRowsWG == 0, "a 256-row unit is split over whole workgroups");
+};
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -524,10 +547,10 @@ struct CoreArgs {
   const uint32_t *kmax2;      // [B][heads][T+1] float bits of the largest squared K norm
 };
 
-// LDS staging of one 64-key block, unpadded rows with an XOR swizzle of the
+// LDS staging of one kBN-key block, unpadded rows with an XOR swizzle of the
 // 16-byte chunks inside a row (the layout; the kernel declares the buffers):
-//   K   [64 keys][D]: chunk p of row r holds head-dim chunk p ^ ksw(r)
-//   V^T [D][64 keys]: chunk p of row d holds key chunk p ^ vsw(d)
+//   K   [kBN keys][D]: chunk p of row r holds head-dim chunk p ^ ksw(r)
+//   V^T [D][kBN keys]: chunk p of row d holds key chunk p ^ vsw(d)
 // Both swizzles make the 16 lanes of an LDS read phase hit 16 different
 // 16-byte bank groups.  Blocks arrive by direct global->LDS loads: each
 // 16-byte load of a wave lands at LDS base + 16 * lane, so each lane fetches
@@ -537,13 +560,16 @@ struct CoreSmem {
   static constexpr int kRB = 2 * D;                 // bytes per K row
   static constexpr int kCPR = D / 8;                // 16-byte chunks per K row
   __device__ static int ksw(int r) { return (r / (256 / kRB)) % kCPR; }
-  __device__ static int vsw(int d) { return (d / 2) % 8; }
+  // V^T rows of kBN keys: 128 / kBN rows share one 256-byte bank window
+  static constexpr int kBN = CoreShape<D>::kBN;
+  __device__ static int vsw(int d) { return (d / (128 / kBN)) % (kBN / 8); }
 };
 
 
 template <int D>
 struct DirectStage {
-  static constexpr int kWaves = TDP_ATTN_WAVES;
+  static constexpr int kWaves = CoreShape<D>::kWaves;
+  static constexpr int kBN = CoreShape<D>::kBN;
   static constexpr int kKUnits = kBN * D * 2 / 1024 / kWaves;   // 1 KB loads per wave, K block
   static constexpr int kVUnits = D * kBN * 2 / 1024 / kWaves;   // 1 KB loads per wave, V^T block
   uint32_t koff[kKUnits];                 // byte offset of this lane's chunk in a K block
@@ -594,28 +620,30 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 template <int D>
 struct FragOffsets {
   int32_t k[D / 16];     // K row l32, head-dim chunk 2 st + hh  (+32 D per 32-key tile)
-  int32_t v[2][2];       // V^T row l32, key chunk 4 kt + 2 u + hh (+32*64 per 32-row tile)
+  static constexpr int kBN = CoreShape<D>::kBN, kKT = CoreShape<D>::kKT;
+  int32_t v[kKT][2];     // V^T row l32, key chunk 4 kt + 2 u + hh (+32*kBN per 32-row tile)
   __device__ FragOffsets(int l32, int hh) {
     const int ks = CoreSmem<D>::ksw(l32), vs = CoreSmem<D>::vsw(l32);
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) k[st] = l32 * D + 8 * ((2 * st + hh) ^ ks);
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
       for (int u = 0; u < 2; ++u) v[kt][u] = l32 * kBN + 8 * ((4 * kt + 2 * u + hh) ^ vs);
   }
 };
 
-// S^T[key][query] = K Q^T for one 64-key block and NG groups of 32 queries:
+// S^T[key][query] = K Q^T for one kBN-key block and NG groups of 32 queries:
 // keys on the MFMA rows, so lane l owns query l%32 of each group and, in
 // s[g][kt][v], key 32 kt + 8 (v/4) + 4 hh + v%4.  Each K fragment read from
 // LDS feeds all NG groups.
 template <int D, int NG>
 __device__ __forceinline__ void qk_block(const bf16 *__restrict__ ks,
-                                         const bf16x8 (&qf)[NG][D / 16], f32x16 (&s)[NG][2],
+                                         const bf16x8 (&qf)[NG][D / 16],
+                                         f32x16 (&s)[NG][CoreShape<D>::kKT],
                                          const FragOffsets<D> &fo) {
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < CoreShape<D>::kKT; ++kt) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) s[g][kt] = f32x16{};
 #pragma unroll
@@ -628,22 +656,25 @@ __device__ __forceinline__ void qk_block(const bf16 *__restrict__ ks,
 }
 
 // Largest score of the block for this lane's query (both half-waves).
-__device__ __forceinline__ float block_max(const f32x16 (&s)[2]) {
-  float mx = fmaxf(s[0][0], s[1][0]);
+template <int kKT>
+__device__ __forceinline__ float block_max(const f32x16 (&s)[kKT]) {
+  float mx = s[0][0];
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s[0][v], s[1][v]));
+  for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[kt][v], s[kt][v + 1]));
   return fmaxf(mx, __shfl_xor(mx, 32));
 }
 
 // P = 2^(s - m) (SHIFT) or 2^s rounded to bf16 and packed as the B operands
 // of O^T += V^T P^T; step (kt, u) holds keys 32 kt + 16 u + {4 hh + 0..3,
 // 8 + 4 hh + 0..3} = s[kt][8u .. 8u+7].  Returns the sum of the bf16 values.
-template <bool SHIFT>
-__device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], float m, bf16x8 (&pf)[2][2]) {
+template <bool SHIFT, int kKT>
+__device__ __forceinline__ float exp_pack(const f32x16 (&s)[kKT], float m, bf16x8 (&pf)[kKT][2]) {
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
   float lsum = 0.f;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
 #pragma unroll
     for (int v = 0; v < 16; v += 2) {
       const float p0 = __builtin_amdgcn_exp2f(SHIFT ? s[kt][v] - m : s[kt][v]);
@@ -662,12 +693,13 @@ __device__ __forceinline__ float exp_pack(const f32x16 (&s)[2], float m, bf16x8 
 // feeds all NG groups.
 template <int D, int NG>
 __device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs,
-                                         const bf16x8 (&pf)[NG][2][2], f32x16 (&o)[NG][D / 32],
-                                         const FragOffsets<D> &fo) {
+                                         const bf16x8 (&pf)[NG][CoreShape<D>::kKT][2],
+                                         f32x16 (&o)[NG][D / 32], const FragOffsets<D> &fo) {
+  constexpr int kBN = CoreShape<D>::kBN;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < CoreShape<D>::kKT; ++kt) {
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
         const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vs + 32 * dt * kBN + fo.v[kt][uu]);
@@ -678,48 +710,45 @@ __device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs,
   }
 }
 
-// Keys >= kvalid among this lane's keys of a block (8 i + 4 hh + 0..3).
+// Keys >= kvalid among this lane's keys of a kBN-key block (8 i + 4 hh + 0..3).
+template <int kBN>
 __device__ __forceinline__ int padded_keys(int kvalid, int hh) {
   int n = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) n += min(max(8 * i + 4 * hh + 4 - kvalid, 0), 4);
+  for (int i = 0; i < kBN / 8; ++i) n += min(max(8 * i + 4 * hh + 4 - kvalid, 0), 4);
   return n;
 }
 
-// Query groups of 32 per wave (1 or 2): 2 halves the LDS fragment reads and
-// the K/V staging per flop, at one wave per SIMD.
-#ifndef TDP_ATTN_NG
-#define TDP_ATTN_NG 1
-#endif
 // 1: S of block j+1 is computed while block j is exponentiated (two S sets);
 // 0: each block's S is computed in its own step (one S set; with two query
 // groups the second group's S overlaps the first group's exp).
-// -1: 1 for head_dim 128 with one group, else 0 (measured: at head_dim 64 the
-// second S set costs more occupancy than the overlap gains).
+// -1: 1 for 64-key blocks at head_dim 128 with one group, else 0 (measured:
+// at head_dim 64 the second S set costs more occupancy than the overlap
+// gains; with 128-key blocks it does not fit the registers).
 #ifndef TDP_ATTN_PIPE
 #define TDP_ATTN_PIPE (-1)
 #endif
-constexpr int kNG = TDP_ATTN_NG;
 template <int D>
-constexpr bool kPipeFor = TDP_ATTN_PIPE < 0 ? (D >= 128 && kNG == 1) : TDP_ATTN_PIPE != 0;
-constexpr int kCoreWaves = TDP_ATTN_WAVES;
-constexpr int kCoreRowsWG = kCoreWaves * 32 * kNG;   // query rows per attention workgroup
-static_assert(kUnit % kCoreRowsWG == 0, "a 256-row unit is split over whole workgroups");
+constexpr bool kPipeFor = TDP_ATTN_PIPE < 0 ? (D >= 128 && kNG == 1 && CoreShape<D>::kBN == 64)
+                                            : TDP_ATTN_PIPE != 0;
 
-// One workgroup = kCoreWaves waves x kNG x 32 query rows of one (batch, head,
+// One workgroup = kWaves waves x kNG x 32 query rows of one (batch, head,
 // tile) against all keys of the tile, then the audio keys; a 256-row unit of
-// the padded row space is split over kUnit / kCoreRowsWG workgroups.
+// the padded row space is split over kUnit / kRowsWG workgroups.
 //
-// Per 64-key block j the wave (1) issues the direct loads of K(j+2) and
-// V(j+1) into the LDS buffers freed in block j-1, (2) computes S(j+1) on MFMA
-// while the VALU turns S(j) into bf16 P, (3) accumulates O += V(j) P(j), and
-// (4) waits for its loads and meets the others at the barrier.  K is staged
-// one block ahead of V, so two K and two V buffers suffice.  Without the
-// pipeline (head_dim 64) step j loads K(j+1) and V(j+1) and computes S(j)
-// itself, before its exp.
+// Per kBN-key block j the wave (1) issues the direct loads of K(j+1) and
+// V(j+1) into the LDS buffers of block j-1, (2) computes S(j) on MFMA, turns
+// it into bf16 P on the VALU and accumulates O += V(j) P(j), and (3) waits for
+// its loads and meets the others at the barrier.  With the pipeline (an
+// option for 64-key blocks) step j instead loads K(j+2) and V(j+1) and
+// computes S(j+1) while the VALU works on S(j); K is then staged one block
+// ahead of V.  Either way two K and two V^T buffers suffice.  Head dim 128
+// runs 128-key blocks in 8-wave workgroups (256 queries share each staged
+// block, one workgroup per CU), head dim 64 runs 64-key blocks in 4-wave
+// workgroups.
 //
-// Softmax: first with a static per-query bound (below); if that underflows
-// the whole tile is run again with the exact online softmax.
+// Softmax: shift-free with a static per-query bound when it allows (below),
+// else the exact online softmax for the whole workgroup.
 //
 // Keys past the end of a segment are the zero rows the QKV stage writes into
 // the padding: score exactly 0, V row 0.  They only add the bf16 weight of a
@@ -732,7 +761,11 @@ static_assert(kUnit % kCoreRowsWG == 0, "a 256-row unit is split over whole work
 // walks a contiguous range of work items and the workgroups sharing a tile's
 // K/V run together on one L2.
 template <int D>
-__global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_core_kernel(CoreArgs a) {
+__global__ __launch_bounds__(64 * CoreShape<D>::kWaves, 8 / (CoreShape<D>::kWaves * kNG))
+void attn_core_kernel(CoreArgs a) {
+  constexpr int kBN = CoreShape<D>::kBN;
+  constexpr int kKT = CoreShape<D>::kKT;
+  constexpr int kCoreRowsWG = CoreShape<D>::kRowsWG;
   // Two K and two V^T buffers, as four separate arrays: a direct load into one
   // and fragment reads from another are then provably disjoint, so the
   // compiler does not make the reads wait for the loads.  Every buffer choice
@@ -812,8 +845,8 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
   const int nkb = nkb0 + nkb1;
   if (nkb == 0) return;
   // padded keys this lane holds in the last block of each segment
-  const int nz0 = nkb0 > 0 ? padded_keys(len0 - (nkb0 - 1) * kBN, hh) : 0;
-  const int nz1 = nkb1 > 0 ? padded_keys(a.A - (nkb1 - 1) * kBN, hh) : 0;
+  const int nz0 = nkb0 > 0 ? padded_keys<kBN>(len0 - (nkb0 - 1) * kBN, hh) : 0;
+  const int nz1 = nkb1 > 0 ? padded_keys<kBN>(a.A - (nkb1 - 1) * kBN, hh) : 0;
 
   const DirectStage<D> ds(__builtin_amdgcn_readfirstlane(wave), lane,
                           static_cast<uint32_t>(a.vt_cols));
@@ -864,7 +897,7 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
 
   f32x16 o[NG][kDT];
   float m_run[NG], l_run[NG];
-  f32x16 sa[NG][2], sb[NG][2];   // S of two consecutive blocks (sb unused without kPipe)
+  f32x16 sa[NG][kKT], sb[NG][kKT];   // S of two consecutive blocks (sb unused without kPipe)
 
   // K(0), V(0), K(1) into LDS; S(0), then a barrier so that no wave's load of
   // K(2) into k[0] overtakes another wave's reads of K(0).  The caller has
@@ -887,15 +920,15 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
     }
   };
 
-  // One 64-key block.  EXACT = false: p = 2^s (see above).  EXACT = true: the exact online softmax with a lazily moved
+  // One kBN-key block.  EXACT = false: p = 2^s (see above).  EXACT = true: the exact online softmax with a lazily moved
   // maximum (moved only when a block max exceeds it by more than kLazy, so
   // p <= 2^kLazy; the O rescale is rare and sits on a real branch).  Loads
   // and S(j+1) run unconditionally so they share one basic block with the
   // exp; past the last block they re-read in-range data and the results are
   // dropped.  K(j) and V(j-1) were consumed in block j-1, so their buffers
   // take K(j+2) and V(j+1).  PAR = j % 2.
-  auto step = [&](auto exact_tag, auto par, int j, f32x16 (&scur)[NG][2],
-                  f32x16 (&snext)[NG][2]) __attribute__((always_inline)) {
+  auto step = [&](auto exact_tag, auto par, int j, f32x16 (&scur)[NG][kKT],
+                  f32x16 (&snext)[NG][kKT]) __attribute__((always_inline)) {
     constexpr bool kExact = decltype(exact_tag)::value;
     constexpr int kPar = decltype(par)::value;
     const std::integral_constant<int, kPar> cur{};
@@ -941,7 +974,7 @@ __global__ __launch_bounds__(64 * kCoreWaves, 8 / (kCoreWaves * kNG)) void attn_
       __builtin_amdgcn_s_setprio(0);
 #endif
     }
-    bf16x8 pf[NG][2][2];
+    bf16x8 pf[NG][kKT][2];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const float lsum = exp_pack<kExact>(scur[g], kExact ? m_run[g] : 0.f, pf[g]);
@@ -1234,8 +1267,9 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.max_rows = c.max_rows;
   a.hidden = L.hidden;
   a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
-  const int64_t grid = ceil_div(a.total_units * (kUnit / kCoreRowsWG), 8) * 8;
-  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)), dim3(64 * kCoreWaves), 0,
+  const int64_t grid = ceil_div(a.total_units * (kUnit / CoreShape<D>::kRowsWG), 8) * 8;
+  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)),
+                     dim3(64 * CoreShape<D>::kWaves), 0,
                      stream, a);
 }
 
@@ -1273,7 +1307,8 @@ extern "C" tdp_status tdp_attn_core(const tdp_attn_desc *desc, int32_t n_tiles,
   if (s != TDP_OK) return s;
   const int64_t units = (c.L.npb / (kUnit / kBlk) + static_cast<int64_t>(n_tiles) * c.L.n_aqb) *
                         desc->batch * desc->heads;
-  if (ceil_div(units * (kUnit / kCoreRowsWG), 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
+  const int64_t rows_wg = desc->head_dim == 64 ? CoreShape<64>::kRowsWG : CoreShape<128>::kRowsWG;
+  if (ceil_div(units * (kUnit / rows_wg), 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
   const hipStream_t stream = as_stream(hip_stream);
   if (desc->head_dim == 64) launch_core<64>(c, stream);
   else launch_core<128>(c, stream);
