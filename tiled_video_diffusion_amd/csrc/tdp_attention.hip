@@ -28,10 +28,6 @@
 #ifndef TDP_ATTN_SCHED
 #define TDP_ATTN_SCHED 0
 #endif
-// Wave priority raised while a wave issues its MFMA-heavy part (0 = off).
-#ifndef TDP_ATTN_PRIO
-#define TDP_ATTN_PRIO 0
-#endif
 // Waves (of 32 query rows each) per attention workgroup, 4 or 8, and keys
 // per iteration, 64 or 128; 0 = per head dim (measured best: 8 waves and
 // 128-key blocks at head_dim 128, one workgroup per CU; 4 waves and 64-key
@@ -41,6 +37,12 @@
 #endif
 #ifndef TDP_ATTN_BN
 #define TDP_ATTN_BN 0
+#endif
+// Keys per compute part of a block without the pipeline (32, 64 or 128;
+// 0 = the whole block; measured: parts of 32 or 64 keys, with their lower
+// register use, run within 1% of whole blocks).
+#ifndef TDP_ATTN_SUB
+#define TDP_ATTN_SUB 0
 #endif
 // Query groups of 32 per wave (1 or 2): 2 halves the LDS fragment reads and
 // the K/V staging per flop, at one wave per SIMD.
@@ -69,6 +71,8 @@ struct CoreShape {
   static constexpr int kKT = kBN / 32;                                            // 32-key MFMA tiles
   static constexpr int kWaves = TDP_ATTN_WAVES ? TDP_ATTN_WAVES : (D >= 128 ? 8 : 4);
   static constexpr int kRowsWG = kWaves * 32 * kNG;   // query rows per workgroup
+  // tiles per compute part of a block without the pipeline
+  static constexpr int kSubKT = (TDP_ATTN_SUB && TDP_ATTN_SUB / 32 < kKT) ? TDP_ATTN_SUB / 32 : kKT;
   static_assert(kBN == 64 || kBN == 128, "64- or 128-key blocks");
   static_assert(kUnit % kBN == 0, "tile padding covers whole key blocks");
   static_assert(kUnit % kRowsWG == 0, "a 256-row unit is split over whole workgroups");
@@ -637,20 +641,22 @@ struct FragOffsets {
 // keys on the MFMA rows, so lane l owns query l%32 of each group and, in
 // s[g][kt][v], key 32 kt + 8 (v/4) + 4 hh + v%4.  Each K fragment read from
 // LDS feeds all NG groups.
-template <int D, int NG>
+// Tiles KT0 .. KT0+NKT-1 of the block; s[g][i] holds tile KT0 + i.
+template <int D, int NG, int KT0 = 0, int NKT = CoreShape<D>::kKT>
 __device__ __forceinline__ void qk_block(const bf16 *__restrict__ ks,
-                                         const bf16x8 (&qf)[NG][D / 16],
-                                         f32x16 (&s)[NG][CoreShape<D>::kKT],
+                                         const bf16x8 (&qf)[NG][D / 16], f32x16 (&s)[NG][NKT],
                                          const FragOffsets<D> &fo) {
 #pragma unroll
-  for (int kt = 0; kt < CoreShape<D>::kKT; ++kt) {
+  for (int i = 0; i < NKT; ++i) {
+    constexpr int kt0 = KT0;
+    const int kt = kt0 + i;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) s[g][kt] = f32x16{};
+    for (int g = 0; g < NG; ++g) s[g][i] = f32x16{};
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
       const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(ks + 32 * kt * D + fo.k[st]);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) s[g][kt] = mfma32(kf, qf[g][st], s[g][kt]);
+      for (int g = 0; g < NG; ++g) s[g][i] = mfma32(kf, qf[g][st], s[g][i]);
     }
   }
 }
@@ -691,20 +697,21 @@ __device__ __forceinline__ float exp_pack(const f32x16 (&s)[kKT], float m, bf16x
 // O^T[d][query] += V^T P^T for NG groups.  The V^T chunk a lane reads holds
 // exactly the keys of its P operand, in the same order (see vt_column), and
 // feeds all NG groups.
-template <int D, int NG>
+// Tiles KT0 .. KT0+NKT-1 of the block; pf[g][i] holds tile KT0 + i.
+template <int D, int NG, int KT0 = 0, int NKT = CoreShape<D>::kKT>
 __device__ __forceinline__ void pv_block(const bf16 *__restrict__ vs,
-                                         const bf16x8 (&pf)[NG][CoreShape<D>::kKT][2],
+                                         const bf16x8 (&pf)[NG][NKT][2],
                                          f32x16 (&o)[NG][D / 32], const FragOffsets<D> &fo) {
   constexpr int kBN = CoreShape<D>::kBN;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-    for (int kt = 0; kt < CoreShape<D>::kKT; ++kt) {
+    for (int i = 0; i < NKT; ++i) {
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vs + 32 * dt * kBN + fo.v[kt][uu]);
+        const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(vs + 32 * dt * kBN + fo.v[KT0 + i][uu]);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) o[g][dt] = mfma32(vf, pf[g][kt][uu], o[g][dt]);
+        for (int g = 0; g < NG; ++g) o[g][dt] = mfma32(vf, pf[g][i][uu], o[g][dt]);
       }
     }
   }
@@ -766,6 +773,7 @@ void attn_core_kernel(CoreArgs a) {
   constexpr int kBN = CoreShape<D>::kBN;
   constexpr int kKT = CoreShape<D>::kKT;
   constexpr int kCoreRowsWG = CoreShape<D>::kRowsWG;
+  constexpr int kSubKT = CoreShape<D>::kSubKT;
   // Two K and two V^T buffers, as four separate arrays: a direct load into one
   // and fragment reads from another are then provably disjoint, so the
   // compiler does not make the reads wait for the loads.  Every buffer choice
@@ -845,8 +853,12 @@ void attn_core_kernel(CoreArgs a) {
   const int nkb = nkb0 + nkb1;
   if (nkb == 0) return;
   // padded keys this lane holds in the last block of each segment
-  const int nz0 = nkb0 > 0 ? padded_keys<kBN>(len0 - (nkb0 - 1) * kBN, hh) : 0;
-  const int nz1 = nkb1 > 0 ? padded_keys<kBN>(a.A - (nkb1 - 1) * kBN, hh) : 0;
+  // real keys in the last block of each segment, and the padded keys this
+  // lane holds there
+  const int kvalid0 = nkb0 > 0 ? len0 - (nkb0 - 1) * kBN : kBN;
+  const int kvalid1 = nkb1 > 0 ? a.A - (nkb1 - 1) * kBN : kBN;
+  const int nz0 = nkb0 > 0 ? padded_keys<kBN>(kvalid0, hh) : 0;
+  const int nz1 = nkb1 > 0 ? padded_keys<kBN>(kvalid1, hh) : 0;
 
   const DirectStage<D> ds(__builtin_amdgcn_readfirstlane(wave), lane,
                           static_cast<uint32_t>(a.vt_cols));
@@ -920,31 +932,22 @@ void attn_core_kernel(CoreArgs a) {
     }
   };
 
-  // One kBN-key block.  EXACT = false: p = 2^s (see above).  EXACT = true: the exact online softmax with a lazily moved
-  // maximum (moved only when a block max exceeds it by more than kLazy, so
-  // p <= 2^kLazy; the O rescale is rare and sits on a real branch).  Loads
-  // and S(j+1) run unconditionally so they share one basic block with the
-  // exp; past the last block they re-read in-range data and the results are
-  // dropped.  K(j) and V(j-1) were consumed in block j-1, so their buffers
-  // take K(j+2) and V(j+1).  PAR = j % 2.
-  auto step = [&](auto exact_tag, auto par, int j, f32x16 (&scur)[NG][kKT],
-                  f32x16 (&snext)[NG][kKT]) __attribute__((always_inline)) {
+  // Softmax of one part of a block (N 32-key tiles, scores sc) into bf16 P.
+  // EXACT = false: p = 2^s (see above).  EXACT = true: the exact online
+  // softmax with a lazily moved maximum (moved only when a part's max exceeds
+  // it by more than kLazy, so p <= 2^kLazy; the O rescale is rare and sits on
+  // a real branch).  kvalid: keys of the part below this index are real, the
+  // rest are zero padding (score 0), whose weight the exact path takes off
+  // here; the shift-free path takes p = 1 per padded key off after the loop.
+  auto soft = [&](auto exact_tag, auto &sc, auto &pf, int kvalid) __attribute__((always_inline)) {
     constexpr bool kExact = decltype(exact_tag)::value;
-    constexpr int kPar = decltype(par)::value;
-    const std::integral_constant<int, kPar> cur{};
-    const std::integral_constant<int, 1 - kPar> oth{};
-    if constexpr (!kPipe) {
-      // K(j+1), V(j+1) into the buffers of block j-1, then S(j) from K(j).
-      load_k(j + 1, kbuf(oth));
-      load_v(j + 1, vbuf(oth));
-      qk_block<D, NG>(kbuf(cur), qf, scur, fo);
-    }
+    constexpr int N = sizeof(sc[0]) / sizeof(f32x16);
     if constexpr (kExact) {
       float mb[NG];
       bool grow = false;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        mb[g] = block_max(scur[g]);
+        mb[g] = block_max<N>(sc[g]);
         grow = grow || (mb[g] > m_run[g] + kLazy);
       }
       if (__builtin_expect(__ballot(grow) != 0, 0)) {
@@ -963,31 +966,57 @@ void attn_core_kernel(CoreArgs a) {
         }
       }
     }
-    if constexpr (kPipe) {
-      load_k(j + 2, kbuf(cur));
-      load_v(j + 1, vbuf(oth));
-#if TDP_ATTN_PRIO
-      __builtin_amdgcn_s_setprio(1);
-#endif
-      qk_block<D, NG>(kbuf(oth), qf, snext, fo);
-#if TDP_ATTN_PRIO
-      __builtin_amdgcn_s_setprio(0);
-#endif
-    }
-    bf16x8 pf[NG][kKT][2];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const float lsum = exp_pack<kExact>(scur[g], kExact ? m_run[g] : 0.f, pf[g]);
+      const float lsum = exp_pack<kExact, N>(sc[g], kExact ? m_run[g] : 0.f, pf[g]);
       if constexpr (kExact) {
-        // a padded key scores exactly 0: it added bf16(2^-m) to lsum
-        const int nz = (j == nkb0 - 1) ? nz0 : ((j == nkb - 1 && nkb1 > 0) ? nz1 : 0);
+        const int nz = padded_keys<32 * N>(kvalid, hh);
         const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_run[g])));
         l_run[g] += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
       } else {
-        l_run[g] += lsum;   // padded keys (p = 1 each) are taken off after the loop
+        l_run[g] += lsum;
       }
     }
-    pv_block<D, NG>(vbuf(cur), pf, o, fo);
+  };
+
+  // One kBN-key block j.  Without the pipeline it loads K(j+1) and V(j+1)
+  // into the buffers of block j-1, then works through the block in parts of
+  // kSubKT tiles (QK, softmax, PV per part).  With the pipeline
+  // (64-key blocks) K(j) and V(j-1) were consumed in block j-1, so their
+  // buffers take K(j+2) and V(j+1), and S(j+1) is computed while block j is
+  // exponentiated.  Loads run unconditionally so they share one basic block
+  // with the exp; past the last block they re-read in-range data and the
+  // results are dropped.  PAR = j % 2.
+  auto step = [&](auto exact_tag, auto par, int j, f32x16 (&scur)[NG][kKT],
+                  f32x16 (&snext)[NG][kKT]) __attribute__((always_inline)) {
+    constexpr int kPar = decltype(par)::value;
+    const std::integral_constant<int, kPar> cur{};
+    const std::integral_constant<int, 1 - kPar> oth{};
+    // real keys of this block (the last block of each segment is padded)
+    const int kvalid = (j == nkb0 - 1) ? kvalid0 : ((j == nkb - 1 && nkb1 > 0) ? kvalid1 : kBN);
+    if constexpr (!kPipe) {
+      load_k(j + 1, kbuf(oth));
+      load_v(j + 1, vbuf(oth));
+      auto part = [&](auto part_tag) __attribute__((always_inline)) {
+        constexpr int kT0 = decltype(part_tag)::value * kSubKT;
+        f32x16 sp[NG][kSubKT];
+        qk_block<D, NG, kT0, kSubKT>(kbuf(cur), qf, sp, fo);
+        bf16x8 pf[NG][kSubKT][2];
+        soft(exact_tag, sp, pf, kvalid - 32 * kT0);
+        pv_block<D, NG, kT0, kSubKT>(vbuf(cur), pf, o, fo);
+      };
+      part(std::integral_constant<int, 0>{});
+      if constexpr (kKT / kSubKT > 1) part(std::integral_constant<int, 1>{});
+      if constexpr (kKT / kSubKT > 2) part(std::integral_constant<int, 2>{});
+      if constexpr (kKT / kSubKT > 3) part(std::integral_constant<int, 3>{});
+    } else {
+      load_k(j + 2, kbuf(cur));
+      load_v(j + 1, vbuf(oth));
+      qk_block<D, NG>(kbuf(oth), qf, snext, fo);
+      bf16x8 pf[NG][kKT][2];
+      soft(exact_tag, scur, pf, kvalid);
+      pv_block<D, NG>(vbuf(cur), pf, o, fo);
+    }
     loads_landed_barrier();
   };
 
