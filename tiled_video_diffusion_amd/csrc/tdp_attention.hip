@@ -40,9 +40,15 @@
 #endif
 // Keys per compute part of a block without the pipeline (32, 64 or 128;
 // 0 = the whole block; measured: parts of 32 or 64 keys, with their lower
-// register use, run within 1% of whole blocks).
+// register use, run within 1% of whole blocks).  TDP_ATTN_SUB_HI is the part
+// size of the upper half of a workgroup's waves (0 = 64): the two waves that
+// share a SIMD (wave w and w + kWaves/2) then reach their MFMA-heavy and
+// exp-heavy stretches at different times (measured 2% faster at head_dim 128).
 #ifndef TDP_ATTN_SUB
 #define TDP_ATTN_SUB 0
+#endif
+#ifndef TDP_ATTN_SUB_HI
+#define TDP_ATTN_SUB_HI 0
 #endif
 // Query groups of 32 per wave (1 or 2): 2 halves the LDS fragment reads and
 // the K/V staging per flop, at one wave per SIMD.
@@ -73,6 +79,8 @@ struct CoreShape {
   static constexpr int kRowsWG = kWaves * 32 * kNG;   // query rows per workgroup
   // tiles per compute part of a block without the pipeline
   static constexpr int kSubKT = (TDP_ATTN_SUB && TDP_ATTN_SUB / 32 < kKT) ? TDP_ATTN_SUB / 32 : kKT;
+  static constexpr int kSubHi = (TDP_ATTN_SUB_HI ? TDP_ATTN_SUB_HI : 64) / 32;
+  static constexpr int kSubKTHi = kSubHi < kKT ? kSubHi : kKT;   // ... for the upper half of the waves
   static_assert(kBN == 64 || kBN == 128, "64- or 128-key blocks");
   static_assert(kUnit % kBN == 0, "tile padding covers whole key blocks");
   static_assert(kUnit % kRowsWG == 0, "a 256-row unit is split over whole workgroups");
@@ -987,8 +995,9 @@ void attn_core_kernel(CoreArgs a) {
   // exponentiated.  Loads run unconditionally so they share one basic block
   // with the exp; past the last block they re-read in-range data and the
   // results are dropped.  PAR = j % 2.
-  auto step = [&](auto exact_tag, auto par, int j, f32x16 (&scur)[NG][kKT],
+  auto step = [&](auto exact_tag, auto upper, auto par, int j, f32x16 (&scur)[NG][kKT],
                   f32x16 (&snext)[NG][kKT]) __attribute__((always_inline)) {
+    constexpr int kPK = decltype(upper)::value ? CoreShape<D>::kSubKTHi : kSubKT;
     constexpr int kPar = decltype(par)::value;
     const std::integral_constant<int, kPar> cur{};
     const std::integral_constant<int, 1 - kPar> oth{};
@@ -998,17 +1007,17 @@ void attn_core_kernel(CoreArgs a) {
       load_k(j + 1, kbuf(oth));
       load_v(j + 1, vbuf(oth));
       auto part = [&](auto part_tag) __attribute__((always_inline)) {
-        constexpr int kT0 = decltype(part_tag)::value * kSubKT;
-        f32x16 sp[NG][kSubKT];
-        qk_block<D, NG, kT0, kSubKT>(kbuf(cur), qf, sp, fo);
-        bf16x8 pf[NG][kSubKT][2];
+        constexpr int kT0 = decltype(part_tag)::value * kPK;
+        f32x16 sp[NG][kPK];
+        qk_block<D, NG, kT0, kPK>(kbuf(cur), qf, sp, fo);
+        bf16x8 pf[NG][kPK][2];
         soft(exact_tag, sp, pf, kvalid - 32 * kT0);
-        pv_block<D, NG, kT0, kSubKT>(vbuf(cur), pf, o, fo);
+        pv_block<D, NG, kT0, kPK>(vbuf(cur), pf, o, fo);
       };
       part(std::integral_constant<int, 0>{});
-      if constexpr (kKT / kSubKT > 1) part(std::integral_constant<int, 1>{});
-      if constexpr (kKT / kSubKT > 2) part(std::integral_constant<int, 2>{});
-      if constexpr (kKT / kSubKT > 3) part(std::integral_constant<int, 3>{});
+      if constexpr (kKT / kPK > 1) part(std::integral_constant<int, 1>{});
+      if constexpr (kKT / kPK > 2) part(std::integral_constant<int, 2>{});
+      if constexpr (kKT / kPK > 3) part(std::integral_constant<int, 3>{});
     } else {
       load_k(j + 2, kbuf(cur));
       load_v(j + 1, vbuf(oth));
@@ -1020,17 +1029,26 @@ void attn_core_kernel(CoreArgs a) {
     loads_landed_barrier();
   };
 
-  auto run = [&](auto exact_tag) __attribute__((always_inline)) {
+  auto run_half = [&](auto exact_tag, auto upper) __attribute__((always_inline)) {
     prologue();
     for (int j = 0; j < nkb; j += 2) {
       if constexpr (kPipe) {
-        step(exact_tag, P0{}, j, sa, sb);
-        if (j + 1 < nkb) step(exact_tag, P1{}, j + 1, sb, sa);
+        step(exact_tag, upper, P0{}, j, sa, sb);
+        if (j + 1 < nkb) step(exact_tag, upper, P1{}, j + 1, sb, sa);
       } else {
-        step(exact_tag, P0{}, j, sa, sa);
-        if (j + 1 < nkb) step(exact_tag, P1{}, j + 1, sa, sa);
+        step(exact_tag, upper, P0{}, j, sa, sa);
+        if (j + 1 < nkb) step(exact_tag, upper, P1{}, j + 1, sa, sa);
       }
     }
+  };
+  // The upper half of the waves runs its own copy of the loop (different
+  // part size); both copies pass the same barriers.
+  const bool upper_half = __builtin_amdgcn_readfirstlane(wave) >= CoreShape<D>::kWaves / 2;
+  auto run = [&](auto exact_tag) __attribute__((always_inline)) {
+    if (CoreShape<D>::kSubKTHi != kSubKT && !kPipe && upper_half)
+      run_half(exact_tag, std::true_type{});
+    else
+      run_half(exact_tag, std::false_type{});
   };
   float l_tot[NG];
   bool exact = __syncthreads_or(need_exact);
