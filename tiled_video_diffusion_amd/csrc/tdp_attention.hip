@@ -303,13 +303,21 @@ struct QkvArgs {
   bf16 *q, *k, *vt;
   uint32_t *kmax2;            // [B][heads][T+1] float bits of the largest squared K norm
   int32_t n_tiles;
+  int32_t chunks_per_wg;      // output chunks (of 3 * heads) per workgroup; blockIdx.z picks the range
 };
 
-// One workgroup = 128 token rows (4 waves x 32) of one batch entry, all
-// 3*heads output chunks of head_dim features.  D[feature][token] = W^T X^T on
+// One workgroup = 128 token rows (4 waves x 32) of one batch entry and the
+// output chunks [z c, z c + c) of the 3*heads chunks of head_dim features,
+// z = blockIdx.z, c = chunks_per_wg (small launches split the chunks over
+// more workgroups so the chip fills).  D[feature][token] = W^T X^T on
 // MFMA, so a lane owns one token and groups of 4 consecutive features: RoPE
 // pairs (2i, 2i+1) sit in one lane and cos/sin depend on that lane's token,
 // computed once and reused by every Q and K head.
+#ifndef TDP_QKV_TARGET_WGS
+#define TDP_QKV_TARGET_WGS 1024
+#endif
+constexpr int64_t kQkvTargetWgs = TDP_QKV_TARGET_WGS;
+
 template <typename TX, int D, bool AUDIO>
 __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
   constexpr int kFT = D / 32;            // 32-feature MFMA tiles per head
@@ -375,7 +383,10 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
 #pragma unroll
   for (int st = 0; st < kC / 16; ++st) wro[st] = l32 * kC + 8 * ((2 * st + hh) ^ (l32 % 16));
 
-  if (uwave < 2) load_w(0);
+  const int n_chunks = 3 * a.heads;
+  const int c_begin = static_cast<int>(blockIdx.z) * a.chunks_per_wg;
+  const int c_end = min(c_begin + a.chunks_per_wg, n_chunks);
+  if (uwave < 2) load_w(c_begin);
 
   // X fragments: token `my`, channels 16s + 8hh + 0..7 (B operand of
   // W^T X^T, A operand of X W).
@@ -414,14 +425,13 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  const int n_chunks = 3 * a.heads;
   // The chunk loop is compiled twice: loader waves (W^T direct loads, which
   // the compiler must wait for before LDS reads) and copy waves (global
   // stores only), so copy waves never wait for their stores.  Both copies
   // pass the same barriers.
   auto chunk_loop = [&](auto loader_tag) {
   constexpr bool loader = decltype(loader_tag)::value;
-  for (int chunk = 0; chunk < n_chunks; ++chunk) {
+  for (int chunk = c_begin; chunk < c_end; ++chunk) {
     const int m = chunk / a.heads, h = chunk - m * a.heads;
     const int64_t slab = b * a.heads + h;
     float kss = 0.f;   // squared norm of this lane's (rounded) K row of head h
@@ -507,7 +517,7 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
                   __float_as_uint(kss));
     }
     lds_barrier();                          // sW read, sOut complete
-    if (loader && chunk + 1 < n_chunks) load_w(chunk + 1);
+    if (loader && chunk + 1 < c_end) load_w(chunk + 1);
     // Copy the tile out in 16-byte pieces: consecutive threads, consecutive bytes.
     const int ct = threadIdx.x - 128;      // copy thread of waves 2-3
     if constexpr (loader) {
@@ -1337,6 +1347,19 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
   a.hidden = L.hidden;
   a.log2_theta_step = -std::log2(static_cast<double>(c.d->rope_base)) / (D / 6);
   a.q_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+  const int n_chunks = 3 * c.d->heads;
+  // A launch with fewer than kQkvTargetWgs / 2 workgroups (one per 128 rows)
+  // splits its chunks over blockIdx.z until it has about kQkvTargetWgs
+  // (measured: 0.17 -> 0.07 ms on a 4-tile 8x32x32 latent; the 16-tile
+  // 16x64x64 step, 968 workgroups, runs fastest unsplit).
+  auto split = [&](int64_t wgs) {
+    const int64_t want =
+        wgs * 2 >= kQkvTargetWgs
+            ? 1
+            : std::max<int64_t>(1, std::min<int64_t>(n_chunks, ceil_div(kQkvTargetWgs, wgs)));
+    const int per = static_cast<int>(ceil_div(n_chunks, want));
+    return std::make_pair(per, static_cast<uint32_t>(ceil_div(n_chunks, per)));
+  };
   // tile rows
   a.x = x_tiles;
   a.x_rows = c.n_rows;
@@ -1346,8 +1369,13 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
   a.q = ws_at<bf16>(c.ws, L.off_q);
   a.k = ws_at<bf16>(c.ws, L.off_k);
   a.vt = ws_at<bf16>(c.ws, L.off_vt);
-  hipLaunchKernelGGL((qkv_rope_kernel<TX, D, false>), dim3(static_cast<uint32_t>(L.npb), c.d->batch),
-                     dim3(kThreads), 0, stream, a);
+  {
+    const auto [per, nz] = split(L.npb * c.d->batch);
+    a.chunks_per_wg = per;
+    hipLaunchKernelGGL((qkv_rope_kernel<TX, D, false>),
+                       dim3(static_cast<uint32_t>(L.npb), c.d->batch, nz), dim3(kThreads), 0, stream,
+                       a);
+  }
   if (c.d->n_audio > 0) {
     a.x = x_audio;
     a.x_rows = c.d->n_audio;
@@ -1355,8 +1383,10 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
     a.vt_col0 = L.n_pad;
     a.q = ws_at<bf16>(c.ws, L.off_qa);
     a.k = ws_at<bf16>(c.ws, L.off_ka);
+    const auto [per, nz] = split(L.a_pad / kBlk * c.d->batch);
+    a.chunks_per_wg = per;
     hipLaunchKernelGGL((qkv_rope_kernel<TX, D, true>),
-                       dim3(static_cast<uint32_t>(L.a_pad / kBlk), c.d->batch), dim3(kThreads),
+                       dim3(static_cast<uint32_t>(L.a_pad / kBlk), c.d->batch, nz), dim3(kThreads),
                        0, stream, a);
   }
 }
