@@ -23,11 +23,6 @@
 
 #include "tdp_common.h"
 
-// Explicit MFMA / LDS / VALU interleaving of the attention inner block
-// (0 = the compiler's own schedule).
-#ifndef TDP_ATTN_SCHED
-#define TDP_ATTN_SCHED 0
-#endif
 // Waves (of 32 query rows each) per attention workgroup, 4 or 8, and keys
 // per iteration, 64 or 128; 0 = per head dim (measured best: 8 waves and
 // 128-key blocks at head_dim 128, one workgroup per CU; 4 waves and 64-key
