@@ -132,6 +132,14 @@ tdp_status tdp_plan_query(const tdp_plan_desc *desc, tdp_plan_sizes *sizes);
 tdp_status tdp_plan(const tdp_plan_desc *desc, const tdp_plan_sizes *sizes,
                     tdp_plan_out *out);
 
+/* Tile counts for a balanced 2D (height x width) grid of n tiles, one per
+ * rank of a group ("Usage": the full-resolution stage asks for such a split of
+ * the group size; the page does not define it).  Writes the factor pair
+ * h * w = n with h <= w and w - h smallest: h is the largest divisor of n not
+ * above sqrt(n).  Host only; both outputs are caller-owned.
+ * Errors: TDP_ERR_NULL (an output is NULL), TDP_ERR_ARG (n < 1). */
+tdp_status tdp_balanced_tile_split(int32_t n, int32_t *h_tiles, int32_t *w_tiles);
+
 /* ------------------------------------------------------------------------ */
 /* Gather (device)                                                           */
 /* ------------------------------------------------------------------------ */

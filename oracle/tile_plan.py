@@ -252,3 +252,25 @@ def plan(grid, tiling, cond_pos=None, normalize_positions: bool = True,
                 tile_n_gen=np.array(n_gen, dtype=np.int32), row_src=row_src,
                 row_weight=row_weight, row_pos=row_pos, cond_keep_count=k,
                 dst_row_begin=dst_row_begin, dst_rows=dst_rows)
+
+
+def balanced_tile_split(n: int) -> tuple:
+    """(h_tiles, w_tiles) for ``n`` tiles on a 2D height x width grid.
+
+    TDP page, "Usage": the full-resolution stage asks a ``balanced_tile_split``
+    helper for a balanced 2D spatial (height x width) grid with one tile per
+    rank of the group; the page does not define it.  Reading used: the factor
+    pair h * w = n with h <= w and w - h as small as possible, i.e. h is the
+    largest divisor of n not above sqrt(n) (width gets the larger count, as
+    video latents are wider than tall).  Walks h down from floor(sqrt(n)).
+    """
+    if n < 1:
+        raise PlanError("n must be >= 1")
+    h = int(np.floor(np.sqrt(n)))
+    while h * h > n:
+        h -= 1
+    while (h + 1) * (h + 1) <= n:
+        h += 1
+    while n % h:
+        h -= 1
+    return h, n // h

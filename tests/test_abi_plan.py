@@ -208,3 +208,14 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(tdp, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError):
         tdp.tdp_plan_query((2, 4, 4), ((1, 0), (1, 0), (1, 0)))
+
+
+def test_balanced_split_matches_oracle():
+    for n in range(1, 5001):
+        assert tdp.tdp_balanced_tile_split(n) == oracle.balanced_tile_split(n), n
+    L = tdp.lib()
+    h, w = ctypes.c_int32(), ctypes.c_int32()
+    for n in [0, -1, -100]:
+        assert L.tdp_balanced_tile_split(n, ctypes.byref(h), ctypes.byref(w)) == -2   # TDP_ERR_ARG
+    assert L.tdp_balanced_tile_split(4, None, ctypes.byref(w)) == -1                  # TDP_ERR_NULL
+    assert L.tdp_balanced_tile_split(4, ctypes.byref(h), None) == -1

@@ -144,3 +144,20 @@ def test_blend_row_mixup_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "blend_tiles", bad)
     with pytest.raises(AssertionError):
         tblend.test_identity_reconstructs_latent("tiny_2x16x16")
+
+
+def test_unbalanced_split_is_caught(monkeypatch):
+    # taking the smallest divisor above 1 instead of the one nearest sqrt(n)
+    def split(n):
+        h = next((d for d in range(2, n + 1) if n % d == 0), 1)
+        return (min(h, n // h), max(h, n // h))
+    monkeypatch.setattr(oracle, "balanced_tile_split", split)
+    with pytest.raises(AssertionError):
+        tplan.test_balanced_split_brute_force()
+
+
+def test_transposed_split_is_caught(monkeypatch):
+    orig = oplan.balanced_tile_split
+    monkeypatch.setattr(oracle, "balanced_tile_split", lambda n: orig(n)[::-1])
+    with pytest.raises(AssertionError):
+        tplan.test_balanced_split_special_cases()

@@ -286,3 +286,32 @@ def test_inverse_map_lists_rows_in_tile_order():
         assert np.all(p.row_src[rows] == n)
         assert np.all(np.diff(tile_of_row[rows]) > 0)
     assert sorted(p.dst_rows.tolist()) == list(range(p.n_rows))
+
+
+# --------------------------------------------------------------------------
+# balanced 2D split of a group ("Usage": balanced_tile_split)
+# --------------------------------------------------------------------------
+
+def _balanced_brute(n):
+    # every factor pair with h <= w; the balanced one has the smallest gap
+    pairs = [(h, n // h) for h in range(1, n + 1) if n % h == 0 and h <= n // h]
+    return min(pairs, key=lambda p: p[1] - p[0])
+
+
+def test_balanced_split_brute_force():
+    for n in range(1, 1025):
+        assert oracle.balanced_tile_split(n) == _balanced_brute(n), n
+
+
+def test_balanced_split_special_cases():
+    # primes have only the trivial split; squares split evenly
+    for p in [2, 3, 5, 7, 11, 13, 97, 1009]:
+        assert oracle.balanced_tile_split(p) == (1, p)
+    for r in range(1, 40):
+        assert oracle.balanced_tile_split(r * r) == (r, r)
+    # the spatial tile grids of the 4-, 16- and 60-tile workloads
+    assert oracle.balanced_tile_split(4) == (2, 2)
+    assert oracle.balanced_tile_split(16) == (4, 4)
+    assert oracle.balanced_tile_split(60) == (6, 10)
+    with pytest.raises(oracle.PlanError):
+        oracle.balanced_tile_split(0)

@@ -258,4 +258,16 @@ tdp_status tdp_plan(const tdp_plan_desc *desc, const tdp_plan_sizes *sizes,
   return TDP_OK;
 }
 
+tdp_status tdp_balanced_tile_split(int32_t n, int32_t *h_tiles, int32_t *w_tiles) {
+  if (!h_tiles || !w_tiles) return TDP_ERR_NULL;
+  if (n < 1) return TDP_ERR_ARG;
+  // largest h with h * h <= n, then down to the first divisor
+  int64_t h = 1;
+  while ((h + 1) * (h + 1) <= n) ++h;
+  while (n % h != 0) --h;
+  *h_tiles = static_cast<int32_t>(h);
+  *w_tiles = static_cast<int32_t>(n / h);
+  return TDP_OK;
+}
+
 }  // extern "C"

@@ -65,6 +65,7 @@ _SIGS = {
     "tdp_status_string": (C.c_char_p, [_I32]),
     "tdp_plan_query": (_I32, [C.POINTER(PlanDesc), C.POINTER(PlanSizes)]),
     "tdp_plan": (_I32, [C.POINTER(PlanDesc), C.POINTER(PlanSizes), C.POINTER(PlanOut)]),
+    "tdp_balanced_tile_split": (_I32, [_I32, C.POINTER(_I32), C.POINTER(_I32)]),
     "tdp_gather_tiles": (_I32, [_P, _I32, _I32, _I64, _I32, _P, _I64, _P, _P]),
     "tdp_tile_attention_workspace": (_I32, [C.POINTER(AttnDesc), _I32, _I64, C.POINTER(_SZ)]),
     "tdp_tile_attention": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P, _P,
@@ -173,6 +174,13 @@ def _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank):
     d.world_size = int(world_size)
     d.rank = int(rank)
     return d, keep
+
+
+def tdp_balanced_tile_split(n):
+    """(h_tiles, w_tiles) of a balanced 2D grid of ``n`` tiles."""
+    h, w = _I32(), _I32()
+    _check(lib().tdp_balanced_tile_split(int(n), C.byref(h), C.byref(w)), "tdp_balanced_tile_split")
+    return h.value, w.value
 
 
 def tdp_plan_query(grid, tiling, cond_pos=None, normalize_positions=True, world_size=1,
