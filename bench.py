@@ -20,6 +20,11 @@ with overlap 8, 32 heads x 128, bf16).  Prints ONE JSON line.
                per launch over mean launch time, against 8 TB/s
   cpu_baseline the CPU oracle (float64 NumPy) on a bounded sample of the same
                step, scaled to a whole step by attention flops
+  shares       (--shares W) how the step would split over W GPUs: each rank's
+               round-robin share (its real shape) timed alone on this GPU, the
+               critical path (slowest rank), and each tile timed alone, from
+               which the longest-processing-time assignment's critical path
+               follows; the exchange between ranks is not modeled
 """
 from __future__ import annotations
 
@@ -146,6 +151,52 @@ def cpu_baseline(inp, plan, budget_s: float = 15.0) -> dict:
                        f"estimated {est:.1f} s per step")}
 
 
+def shares(inp, world_size: int, reps: int = 5) -> dict:
+    """Round-robin shares of `world_size` ranks, each timed alone on this GPU."""
+    import numpy as np
+    import torch
+    from tiled_video_diffusion_amd.step import TdpStep
+
+    stream = torch.cuda.current_stream()
+
+    def time_share(world, rank):
+        st = TdpStep(inp, world_size=world, rank=rank)
+        for _ in range(2):
+            st.run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            st.run()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        tiles = [int(t) for t in st.plan.tile_id]
+        n_total = st.plan.n_tiles_total
+        del st
+        torch.cuda.empty_cache()
+        return ms, tiles, n_total
+
+    rr = [time_share(world_size, r) for r in range(world_size)]
+    n_tiles = rr[0][2]
+    per_tile = [time_share(n_tiles, t)[0] for t in range(n_tiles)]
+    # longest processing time first: each tile to the least loaded rank
+    loads = [0.0] * world_size
+    for t in sorted(range(n_tiles), key=lambda t: -per_tile[t]):
+        r = int(np.argmin(loads))
+        loads[r] += per_tile[t]
+    rr_from_tiles = [sum(per_tile[t] for t in tiles) for _, tiles, _ in rr]
+    return {"world_size": world_size, "assignment": "round robin (tile t -> rank t mod W)",
+            "ms_per_rank": [m for m, _, _ in rr], "tiles_per_rank": [t for _, t, _ in rr],
+            "critical_ms": max(m for m, _, _ in rr),
+            "per_tile_ms": per_tile,
+            "critical_ms_from_tile_times": {"round_robin": max(rr_from_tiles),
+                                            "longest_first": max(loads)},
+            "note": "shares run one after another on one GPU; the all_reduce (or halo "
+                    "exchange) between ranks is not included"}
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -259,10 +310,14 @@ def run(args) -> dict:
         "blend_stress": bs,
     }
     if args.calibrate_copy_mib:
-        del step
+        step = None
         torch.cuda.empty_cache()
         calibrate_copy(args.calibrate_copy_mib)
         out["calibrate_copy_mib"] = args.calibrate_copy_mib
+    if args.shares:
+        step = None
+        torch.cuda.empty_cache()
+        out["shares"] = shares(inp, args.shares)
     if not args.skip_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, p, args.cpu_budget)
     return out
@@ -278,6 +333,9 @@ def main():
                     help="seconds of oracle denoiser work in the CPU baseline sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-blend-stress", action="store_true")
+    ap.add_argument("--shares", type=int, default=0,
+                    help="also time each rank's round-robin share for this many ranks "
+                         "(one after another on this GPU)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the run, a fill and a negation of this many MiB (for scaling "
                          "HBM byte counters)")
