@@ -30,7 +30,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "Inputs", "make_inputs",
-           "round_to_bf16", "draw_cond_pos"]
+           "round_to_bf16", "draw_cond_pos", "BlockWorkload", "BLOCK_WORKLOADS",
+           "BlockInputs", "make_block_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -171,3 +172,97 @@ def make_inputs(wl: Workload | str, seed: Optional[int] = None) -> Inputs:
             if wl.latent_dtype == "bf16":
                 xa = round_to_bf16(xa)
     return Inputs(wl, x, cond, wq, wk, wv, wo, xa)
+
+
+
+# ---------------------------------------------------------------------------
+# The per-tile transformer block (the "full transformer" every rank runs)
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class BlockWorkload:
+    """A TDP step whose tile denoiser is L transformer blocks of width
+    D = heads * head_dim with text cross-attention and timestep modulation."""
+    name: str
+    base: str              # geometry, channels, heads and dtype from this workload
+    layers: int
+    n_text: int            # text tokens per batch entry, width D
+    time_dim: int = 256    # timestep embedding width
+    ffn_mult: int = 4
+    heads: Optional[int] = None        # override the base workload's heads
+    head_dim: Optional[int] = None
+
+    def base_workload(self) -> Workload:
+        wl = WORKLOADS[self.base]
+        kw = {}
+        if self.heads is not None:
+            kw["heads"] = self.heads
+        if self.head_dim is not None:
+            kw["head_dim"] = self.head_dim
+        if kw:
+            wl = dataclasses.replace(wl, name=self.name, **kw)
+        return wl
+
+
+BLOCK_WORKLOADS = {
+    # two blocks on the 4-tile 2x16x16 latent, D = 128: the oracle runs all of it
+    "block_tiny": BlockWorkload("block_tiny", base="tiny_2x16x16", layers=2, n_text=16),
+    # one block, head_dim 128, D = 256, bf16 latent with conditioning
+    "block_d128": BlockWorkload("block_d128", base="d64_8x32x32", layers=1, n_text=24,
+                                heads=2, head_dim=128),
+    # one block at the 16-tile step's width (32 heads x 128 = 4096), 128 text tokens
+    "block_t16": BlockWorkload("block_t16", base="t16_16x64x64", layers=1, n_text=128),
+}
+
+
+@dataclasses.dataclass
+class BlockInputs:
+    workload: BlockWorkload
+    base: Inputs                      # latent, conditioning positions (no attention weights used)
+    w_in: np.ndarray                  # [C][D]
+    w_out: np.ndarray                 # [D][C]
+    wt1: np.ndarray                   # [time_dim][D]
+    wt2: np.ndarray                   # [D][6 D]
+    layers: list                      # per layer: dict of wq wk wv wo cq ck cv co w1 w2 table
+    text: np.ndarray                  # [B][n_text][D]
+    tau: np.ndarray                   # [B] timesteps
+
+
+def make_block_inputs(bw: BlockWorkload | str) -> BlockInputs:
+    """Seeded inputs of a block workload.
+
+    The latent and conditioning positions are those of ``make_inputs`` on the
+    base workload.  The block's arrays come from a second generator,
+    ``default_rng(seed + 1000)``, in this order: w_in [C][D]; w_out [D][C];
+    wt1 [time_dim][D]; wt2 [D][6D]; then per layer wq, wk, wv, wo, cq, ck, cv,
+    co [D][D], w1 [D][ffn D], w2 [ffn D][D], table [6][D]; text [B][n_text][D];
+    tau [B].  Matrices are N(0, 1/sqrt(fan_in)), table N(0, 0.1), text
+    N(0, 1), tau U(0, 1000).  Everything but tau is rounded once to bf16.
+    """
+    if isinstance(bw, str):
+        bw = BLOCK_WORKLOADS[bw]
+    wl = bw.base_workload()
+    base = make_inputs(wl)
+    rng = np.random.default_rng(wl.seed + 1000)
+    C, D, B = wl.channels, wl.hidden, wl.batch
+    F = bw.ffn_mult * D
+
+    def mat(fan_in, fan_out):
+        a = rng.standard_normal((fan_in, fan_out), dtype=np.float32)
+        return round_to_bf16(a * np.float32(1.0 / np.sqrt(fan_in)))
+
+    w_in = mat(C, D)
+    w_out = mat(D, C)
+    wt1 = mat(bw.time_dim, D)
+    wt2 = mat(D, 6 * D)
+    layers = []
+    for _ in range(bw.layers):
+        lay = {k: mat(D, D) for k in ("wq", "wk", "wv", "wo", "cq", "ck", "cv", "co")}
+        lay["w1"] = mat(D, F)
+        lay["w2"] = mat(F, D)
+        lay["table"] = round_to_bf16(rng.standard_normal((6, D), dtype=np.float32)
+                                     * np.float32(0.1))
+        layers.append(lay)
+    text = round_to_bf16(rng.standard_normal((B, bw.n_text, D), dtype=np.float32))
+    tau = rng.uniform(0.0, 1000.0, size=B).astype(np.float32)
+    return BlockInputs(bw, base, w_in, w_out, wt1, wt2, layers, text, tau)

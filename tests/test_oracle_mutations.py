@@ -161,3 +161,71 @@ def test_transposed_split_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "balanced_tile_split", lambda n: orig(n)[::-1])
     with pytest.raises(AssertionError):
         tplan.test_balanced_split_special_cases()
+
+
+# ---- the per-tile transformer block ----
+
+import dataclasses as _dc  # noqa: E402
+
+import oracle.block as oblock  # noqa: E402
+import tests.test_oracle_block as tblock  # noqa: E402
+
+
+def _mutated_block(monkeypatch, **changes):
+    """Replace block_forward by a copy with one planted change."""
+    def block(x, pos, text, mod, lay, heads, head_dim):
+        x = np.asarray(x, dtype=np.float64)
+        shift_a, scale_a, gate_a, shift_f, scale_f, gate_f = mod
+        one = 0.0 if changes.get("no_one_plus") else 1.0
+        h = oblock.rms_norm(x) * (one + scale_a) + shift_a
+        a, _ = oracle.tile_forward(h, pos, None, lay.wq, lay.wk, lay.wv, lay.wo, heads, head_dim)
+        x = x + gate_a * a
+        c = oblock.cross_attn(oblock.rms_norm(x), text, lay.cq, lay.ck, lay.cv, lay.co, heads,
+                              head_dim)
+        x = c if changes.get("no_cross_residual") else x + c
+        h = oblock.rms_norm(x) * (one + scale_f) + shift_f
+        f = oblock.ffn(h, lay.w1, lay.w2)
+        return x + (f if changes.get("ungated_ffn") else gate_f * f)
+    monkeypatch.setattr(oblock, "block_forward", block)
+
+
+def test_scale_without_one_is_caught(monkeypatch):
+    _mutated_block(monkeypatch, no_one_plus=True)
+    with pytest.raises(AssertionError):
+        tblock.test_block_self_attention_branch_is_the_hot_path_layer()
+
+
+def test_missing_cross_residual_is_caught(monkeypatch):
+    _mutated_block(monkeypatch, no_cross_residual=True)
+    with pytest.raises(AssertionError):
+        tblock.test_block_with_closed_gates_is_identity()
+
+
+def test_ungated_ffn_is_caught(monkeypatch):
+    _mutated_block(monkeypatch, ungated_ffn=True)
+    with pytest.raises(AssertionError):
+        tblock.test_block_with_closed_gates_is_identity()
+
+
+def test_gelu_without_cubic_term_is_caught(monkeypatch):
+    monkeypatch.setattr(oblock, "gelu_tanh",
+                        lambda u: 0.5 * np.asarray(u) * (1 + np.tanh(np.sqrt(2 / np.pi) * np.asarray(u))))
+    with pytest.raises(AssertionError):
+        tblock.test_gelu_tanh_against_erf_gelu_and_odd_part()
+
+
+def test_cross_attn_scale_by_d_is_caught(monkeypatch):
+    orig = oblock.cross_attn
+    monkeypatch.setattr(oblock, "cross_attn",
+                        lambda h, t, wq, wk, wv, wo, heads, d: orig(h, t, wq / np.sqrt(d), wk, wv, wo,
+                                                                    heads, d))
+    with pytest.raises(AssertionError):
+        tblock.test_cross_attn_brute_force()
+
+
+def test_rms_eps_outside_root_is_caught(monkeypatch):
+    monkeypatch.setattr(oblock, "rms_norm",
+                        lambda x, eps=oblock.RMS_EPS: np.asarray(x) / (
+                            np.sqrt(np.mean(np.asarray(x) ** 2, axis=-1, keepdims=True)) + eps))
+    with pytest.raises(AssertionError):
+        tblock.test_rms_norm_closed_forms()
