@@ -22,6 +22,7 @@
 #include <type_traits>
 
 #include "tdp_common.h"
+#include "tdp_internal.h"
 
 // Waves (of 32 query rows each) per attention workgroup, 4 or 8, and keys
 // per iteration, 64 or 128; 0 = per head dim (measured best: 8 waves and
@@ -1109,150 +1110,6 @@ void attn_core_kernel(CoreArgs a) {
 // out_proj
 // ---------------------------------------------------------------------------
 
-template <typename TY>
-__device__ inline void store_y(TY *p, float v);
-template <>
-__device__ inline void store_y<float>(float *p, float v) { *p = v; }
-template <>
-__device__ inline void store_y<bf16>(bf16 *p, float v) { *p = static_cast<bf16>(v); }
-
-// Y[M][128] = O Wo.  O is head-major: row R of segment s = R / L (a batch
-// entry of the tile rows, or a (tile, batch) pair of the audio rows) holds
-// its head-h features at ((s * heads + h) * L + R % L) * D, so the 64-wide k
-// chunk (head h, half of its D) of 256 consecutive rows is one contiguous
-// stretch of memory.  One workgroup = 256 rows (8 waves x 32), all 128
-// outputs.  Each k chunk of O (32 KB) and of Wo^T (16 KB) goes global -> LDS
-// by direct loads, one 128-byte row segment per 8 lanes, into a 3-stage
-// ring, so a chunk has two chunk-times to arrive while the MFMAs work on the
-// one before.  LDS rows are 128 bytes, 16-byte piece p of row r at slot
-// p ^ ((r / 2) % 8): the 16 lanes of a fragment read phase (16 consecutive
-// rows, one piece) hit 16 distinct slots of a 256-byte bank window.
-constexpr int kOsWaves = 8;
-constexpr int kOsThreads = 64 * kOsWaves;
-constexpr int kOsRows = 32 * kOsWaves;
-constexpr int kOsK = 64;                                  // k per chunk
-constexpr int kOsOLoads = kOsRows * kOsK * 2 / 1024 / kOsWaves;   // 1 KB O loads per wave
-constexpr int kOsWLoads = kC * kOsK * 2 / 1024 / kOsWaves;        // 1 KB Wo^T loads per wave
-
-__device__ __forceinline__ int os_slot(int r, int piece) { return piece ^ ((r >> 1) & 7); }
-
-template <typename TY, int D>
-__global__ __launch_bounds__(kOsThreads, 1) void out_proj_kernel(
-    const bf16 *__restrict__ o, const bf16 *__restrict__ wot, TY *__restrict__ y, int64_t M,
-    int64_t L, int32_t heads) {
-  static_assert(D % kOsK == 0, "whole k chunks per head");
-  const int32_t hidden = heads * D;
-  __shared__ __attribute__((aligned(16))) bf16 sA0[kOsRows * kOsK], sA1[kOsRows * kOsK],
-      sA2[kOsRows * kOsK];
-  __shared__ __attribute__((aligned(16))) bf16 sB0[kC * kOsK], sB1[kC * kOsK], sB2[kC * kOsK];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int uwave = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kOsRows;
-
-  // Per-lane byte offsets of the direct loads (k chunk 0); LDS position
-  // (r, slot) holds piece slot ^ ((r / 2) % 8) of row r.  Rows past M re-read
-  // row M - 1 (their results are not stored).
-  uint64_t aoff[kOsOLoads];
-  uint32_t boff[kOsWLoads];
-#pragma unroll
-  for (int i = 0; i < kOsOLoads; ++i) {
-    const int pos = (i * kOsWaves + uwave) * 64 + lane;   // 16-byte position in the tile
-    const int r = pos / 8, slot = pos % 8;
-    const int64_t gr = min(row0 + r, M - 1);
-    const int64_t seg = gr / L;
-    aoff[i] = static_cast<uint64_t>((seg * heads * L + (gr - seg * L)) * D * 2 +
-                                    16 * os_slot(r, slot));
-  }
-#pragma unroll
-  for (int i = 0; i < kOsWLoads; ++i) {
-    const int pos = (i * kOsWaves + uwave) * 64 + lane;
-    const int r = pos / 8, slot = pos % 8;
-    boff[i] = static_cast<uint32_t>(r * hidden * 2 + 16 * os_slot(r, slot));
-  }
-  const char *abase = reinterpret_cast<const char *>(o);
-  const char *bbase = reinterpret_cast<const char *>(wot);
-  auto load_chunk = [&](int c, bf16 *sa, bf16 *sb) __attribute__((always_inline)) {
-    const int64_t kb = static_cast<int64_t>(c) * kOsK * 2;   // Wo^T: k = 64 c
-    constexpr int kPerHead = D / kOsK;
-    const int h = c / kPerHead;
-    const int64_t ab = (static_cast<int64_t>(h) * L * D + (c - h * kPerHead) * kOsK) * 2;
-#pragma unroll
-    for (int i = 0; i < kOsOLoads; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(abase + ab + aoff[i]),
-                                       (lvoid_t *)(sa + (i * kOsWaves + uwave) * 512), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < kOsWLoads; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(bbase + kb + boff[i]),
-                                       (lvoid_t *)(sb + (i * kOsWaves + uwave) * 512), 16, 0, 0);
-  };
-  // fragment offsets (elements): A row wave*32 + l32, B row 32 ct + l32;
-  // piece 2 ks + hh
-  const int ar = wave * 32 + l32;
-  int32_t afo[kOsK / 16], bfo[4][kOsK / 16];
-#pragma unroll
-  for (int ks = 0; ks < kOsK / 16; ++ks) {
-    afo[ks] = ar * kOsK + 8 * os_slot(ar, 2 * ks + hh);
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const int br = 32 * ct + l32;
-      bfo[ct][ks] = br * kOsK + 8 * os_slot(br, 2 * ks + hh);
-    }
-  }
-  f32x16 acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-  auto compute = [&](const bf16 *sa, const bf16 *sb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < kOsK / 16; ++ks) {
-      const bf16x8 af = *reinterpret_cast<const bf16x8 *>(sa + afo[ks]);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sb + bfo[ct][ks]);
-        acc[ct] = mfma32(af, bfr, acc[ct]);
-      }
-    }
-  };
-  constexpr int kPer = kOsOLoads + kOsWLoads;   // loads per wave per chunk
-  static_assert(kPer == 6, "vmcnt below counts 6 loads per chunk");
-  const int nc = hidden / kOsK;
-  load_chunk(0, sA0, sB0);
-  if (nc > 1) load_chunk(1, sA1, sB1);
-  if (nc > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  // Step c: load chunk c+2 into the ring slot of chunk c-1, compute chunk c,
-  // wait for chunk c+1, barrier.  Loads past the last chunk re-read chunk
-  // nc-1 (in range; never used) so every step waits on the same count.
-  auto step = [&](int c, bf16 *ln_a, bf16 *ln_b, const bf16 *ca, const bf16 *cb)
-      __attribute__((always_inline)) {
-    load_chunk(min(c + 2, nc - 1), ln_a, ln_b);
-    compute(ca, cb);
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    __syncthreads();
-  };
-  int c = 0;
-  for (; c + 3 <= nc; c += 3) {
-    step(c, sA2, sB2, sA0, sB0);
-    step(c + 1, sA0, sB0, sA1, sB1);
-    step(c + 2, sA1, sB1, sA2, sB2);
-  }
-  if (c < nc) step(c, sA2, sB2, sA0, sB0);
-  if (c + 1 < nc) step(c + 1, sA0, sB0, sA1, sB1);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // acc[ct][v]: row 8 (v/4) + 4 hh + v%4 of the wave's 32, column 32 ct + l32
-  const int64_t base = row0 + wave * 32;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
-    if (r < M) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) store_y<TY>(y + r * kC + 32 * ct + l32, acc[ct][v]);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -1479,28 +1336,26 @@ extern "C" tdp_status tdp_attn_out_proj(const tdp_attn_desc *desc, int32_t n_til
   const bf16 *wot = ws_at<bf16>(workspace, L.off_wot);
   const int64_t M = static_cast<int64_t>(desc->batch) * n_rows;
   const int64_t Ma = static_cast<int64_t>(n_tiles) * desc->batch * desc->n_audio;
-  const bf16 *o = ws_at<bf16>(workspace, L.off_o);
-  const bf16 *oa = ws_at<bf16>(workspace, L.off_oa);
-  if (ceil_div(M, kOsRows) > INT32_MAX || ceil_div(Ma, kOsRows) > INT32_MAX) return TDP_ERR_ARG;
-  auto launch = [&](auto d_tag) {
-    constexpr int D = decltype(d_tag)::value;
-    const dim3 grid(static_cast<uint32_t>(ceil_div(M, kOsRows)));
-    if (desc->y_dtype == TDP_F32)
-      hipLaunchKernelGGL((out_proj_kernel<float, D>), grid, dim3(kOsThreads), 0, stream, o, wot,
-                         static_cast<float *>(y_tiles), M, n_rows, desc->heads);
-    else
-      hipLaunchKernelGGL((out_proj_kernel<bf16, D>), grid, dim3(kOsThreads), 0, stream, o, wot,
-                         static_cast<bf16 *>(y_tiles), M, n_rows, desc->heads);
-    tdp_status st = launch_status();
-    if (st != TDP_OK || Ma == 0) return st;
-    hipLaunchKernelGGL((out_proj_kernel<float, D>),
-                       dim3(static_cast<uint32_t>(ceil_div(Ma, kOsRows))), dim3(kOsThreads), 0,
-                       stream, oa, wot, y_audio_tiles, Ma, static_cast<int64_t>(desc->n_audio),
-                       desc->heads);
-    return launch_status();
-  };
-  if (desc->head_dim == 128) return launch(std::integral_constant<int, 128>{});
-  return launch(std::integral_constant<int, 64>{});
+  // Y = O Wo with O head-major (see the attention core's stores)
+  GemmDesc g;
+  g.a = ws_at<bf16>(workspace, L.off_o);
+  g.a_seg_rows = n_rows;
+  g.a_heads = desc->heads;
+  g.a_head_dim = desc->head_dim;
+  g.bt = wot;
+  g.ldb = L.hidden;
+  g.M = M;
+  g.N = kC;
+  g.K = L.hidden;
+  g.c = y_tiles;
+  g.ldc = kC;
+  s = gemm(desc->y_dtype == TDP_F32 ? kEpiF32 : kEpiBf16, g, stream);
+  if (s != TDP_OK || Ma == 0) return s;
+  g.a = ws_at<bf16>(workspace, L.off_oa);
+  g.a_seg_rows = desc->n_audio;
+  g.M = Ma;
+  g.c = y_audio_tiles;
+  return gemm(kEpiF32, g, stream);
 }
 
 extern "C" tdp_status tdp_tile_attention(const tdp_attn_desc *desc, int32_t n_tiles,
