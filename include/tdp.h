@@ -275,6 +275,78 @@ tdp_status tdp_audio_accumulate(const float *y_audio_tiles, int32_t n_tiles_loca
                                 int32_t C, float *y_audio, int32_t accumulate,
                                 void *hip_stream);
 
+/* ------------------------------------------------------------------------ */
+/* Per-tile transformer block (device)                                       */
+/* ------------------------------------------------------------------------ */
+
+/* The TDP page ("What it is") has every rank run the full transformer on its
+ * tiles and describes no part of it.  This library's reading is L blocks of
+ *   h = rms(x)(1 + scale_a) + shift_a;  x += gate_a * SelfAttn(h)
+ *   h = rms(x);                         x += CrossAttn(h, text)
+ *   h = rms(x)(1 + scale_f) + shift_f;  x += gate_f * FFN(h)
+ * around x_0 = X W_in and y = rms(x_L) W_out, per tile and batch entry, with
+ *  rms(x) = x / sqrt(mean(x^2) + 1e-6) (no weight);
+ *  (shift_a, scale_a, gate_a, shift_f, scale_f, gate_f) = table_l +
+ *    silu(emb(tau_b) Wt1) Wt2 split into six D-vectors, emb(tau) =
+ *    [cos(tau w_i), sin(tau w_i)], w_i = 10000^(-i/(time_dim/2));
+ *  SelfAttn = the tdp_tile_attention layer at width D = heads * head_dim
+ *    (3D RoPE on row_pos, softmax(Q K^T / sqrt(d)) V, no bias);
+ *  CrossAttn: queries from the tile rows, keys and values from the batch
+ *    entry's n_text text tokens (width D), no rotation, no mask;
+ *  FFN(h) = gelu_tanh(h W1) W2, width 4D.  No biases.
+ * The residual stream is float32, matrix operands bf16. */
+typedef struct {
+  int32_t batch, C;            /* C must be 128 */
+  int32_t heads, head_dim;     /* head_dim 64 or 128; D = heads * head_dim, a multiple of 128 */
+  int32_t n_text, layers;      /* n_text >= 1, layers >= 0 */
+  int32_t time_dim;            /* timestep embedding width, a multiple of 64 (256) */
+  int32_t x_dtype, y_dtype;    /* tdp_dtype of x_tiles and y_tiles */
+  float rope_base;             /* 10000 */
+} tdp_block_desc;
+
+/* One block's weights: device pointers, bf16 matrices stored [out][in]
+ * row-major (the transpose of x W), 16-byte aligned. */
+typedef struct {
+  const void *wqkv;            /* [3D][D]: rows of Wq^T, then Wk^T, then Wv^T */
+  const void *wo;              /* [D][D] */
+  const void *cq;              /* [D][D]  cross-attention query */
+  const void *ckv;             /* [2D][D] cross-attention key rows, then value rows */
+  const void *co;              /* [D][D] */
+  const void *w1;              /* [4D][D] */
+  const void *w2;              /* [D][4D] */
+  const float *table;          /* [6][D] float32 modulation table */
+} tdp_block_layer;
+
+typedef struct {
+  const void *w_in;            /* [D][C] */
+  const void *w_out;           /* [C][D] */
+  const void *wt1;             /* [D][time_dim] */
+  const void *wt2;             /* [6D][D] */
+  const tdp_block_layer *layers;   /* host array of `layers` entries */
+} tdp_block_weights;
+
+/* Workspace bytes of tdp_block_forward.  Errors: TDP_ERR_NULL, TDP_ERR_ARG,
+ * TDP_ERR_UNSUPPORTED (C, head_dim, D or dtypes outside the above). */
+tdp_status tdp_block_workspace(const tdp_block_desc *desc, int32_t n_tiles, int64_t n_rows,
+                               size_t *bytes);
+
+/* y_tiles = the per-tile transformer of x_tiles, for every tile of a rank's
+ * plan (the tile arguments are those of tdp_tile_attention).
+ *  x_tiles:  device [batch][n_rows][C], x_dtype.
+ *  row_pos:  device [n_rows][3][2] float32 (tdp_plan's normalized positions).
+ *  text:     device [batch][n_text][D] bf16.
+ *  tau:      device [batch] float32 timesteps.
+ *  y_tiles:  device [batch][n_rows][C], y_dtype.
+ * Asynchronous on hip_stream; the library allocates nothing.  Errors:
+ * TDP_ERR_NULL, TDP_ERR_ARG, TDP_ERR_UNSUPPORTED, TDP_ERR_BUFFER (workspace
+ * too small), TDP_ERR_ALIGN, TDP_ERR_HIP. */
+tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_tiles,
+                             const int64_t *tile_row_begin, int32_t max_tile_rows,
+                             int64_t n_rows, const void *x_tiles, const float *row_pos,
+                             const void *text, const float *tau, const tdp_block_weights *weights,
+                             void *y_tiles, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

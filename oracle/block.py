@@ -126,12 +126,19 @@ class Model:
 
 
 def block_forward(x: np.ndarray, pos: np.ndarray, text: np.ndarray, mod: np.ndarray,
-                  lay: Layer, heads: int, head_dim: int) -> np.ndarray:
-    """One block on one tile's residual stream x [n][D]; mod [6][D]."""
+                  lay: Layer, heads: int, head_dim: int, query_rows=None) -> np.ndarray:
+    """One block on one tile's residual stream x [n][D]; mod [6][D].
+
+    ``query_rows`` restricts the rows returned (all rows still give keys and
+    values to the self-attention); default all rows.
+    """
     x = np.asarray(x, dtype=F64)
     shift_a, scale_a, gate_a, shift_f, scale_f, gate_f = mod
     h = rms_norm(x) * (1.0 + scale_a) + shift_a
-    a, _ = tile_forward(h, pos, None, lay.wq, lay.wk, lay.wv, lay.wo, heads, head_dim)
+    a, _ = tile_forward(h, pos, None, lay.wq, lay.wk, lay.wv, lay.wo, heads, head_dim,
+                        query_rows=query_rows)
+    if query_rows is not None:
+        x = x[np.asarray(query_rows)]
     x = x + gate_a * a
     x = x + cross_attn(rms_norm(x), text, lay.cq, lay.ck, lay.cv, lay.co, heads, head_dim)
     h = rms_norm(x) * (1.0 + scale_f) + shift_f
@@ -139,12 +146,19 @@ def block_forward(x: np.ndarray, pos: np.ndarray, text: np.ndarray, mod: np.ndar
 
 
 def tile_transformer(x_tile: np.ndarray, pos: np.ndarray, text: np.ndarray, tau: float,
-                     model: Model) -> np.ndarray:
-    """The per-tile transformer for one batch entry: [n][C] -> [n][C]."""
+                     model: Model, query_rows=None) -> np.ndarray:
+    """The per-tile transformer for one batch entry: [n][C] -> [n][C].
+
+    ``query_rows`` (models of at most one layer) evaluates only those rows.
+    """
     x = np.asarray(x_tile, dtype=F64) @ np.asarray(model.w_in, dtype=F64)
+    if query_rows is not None and len(model.layers) > 1:
+        raise ValueError("query_rows needs every row of the earlier layers")
     for lay in model.layers:
         mod = modulation(tau, model.wt1, model.wt2, lay.table)
-        x = block_forward(x, pos, text, mod, lay, model.heads, model.head_dim)
+        x = block_forward(x, pos, text, mod, lay, model.heads, model.head_dim, query_rows)
+    if query_rows is not None and not model.layers:
+        x = x[np.asarray(query_rows)]
     return rms_norm(x) @ np.asarray(model.w_out, dtype=F64)
 
 

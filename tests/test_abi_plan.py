@@ -219,3 +219,24 @@ def test_balanced_split_matches_oracle():
         assert L.tdp_balanced_tile_split(n, ctypes.byref(h), ctypes.byref(w)) == -2   # TDP_ERR_ARG
     assert L.tdp_balanced_tile_split(4, None, ctypes.byref(w)) == -1                  # TDP_ERR_NULL
     assert L.tdp_balanced_tile_split(4, ctypes.byref(h), None) == -1
+
+
+def test_block_validation():
+    ok = dict(batch=1, C_=128, heads=2, head_dim=64, n_text=16, layers=2,
+              x_dtype=tdp.TDP_F32, y_dtype=tdp.TDP_F32)
+    assert tdp.tdp_block_workspace(tdp.block_desc(**ok), 4, 520) > 0
+    bad = [(dict(C_=64), -4), (dict(head_dim=96), -4), (dict(heads=3), -4),   # D = 192
+           (dict(n_text=0), -2), (dict(layers=-1), -2), (dict(batch=0), -2),
+           (dict(x_dtype=7), -4)]
+    L = tdp.lib()
+    n = ctypes.c_size_t()
+    for kw, code in bad:
+        d = tdp.block_desc(**{**ok, **kw})
+        assert L.tdp_block_workspace(ctypes.byref(d), 4, 520, ctypes.byref(n)) == code, kw
+    d = tdp.block_desc(**ok, time_dim=100)
+    assert L.tdp_block_workspace(ctypes.byref(d), 4, 520, ctypes.byref(n)) == -2
+    # missing pointers fail before any launch
+    w = tdp.BlockWeights()
+    d = tdp.block_desc(**ok)
+    assert L.tdp_block_forward(ctypes.byref(d), 4, None, 130, 520, None, None, None, None,
+                               ctypes.byref(w), None, None, 0, None) == -1

@@ -226,3 +226,17 @@ def test_block_step_is_shift_invariant():
     a = ob.block_step(binp, normalize_positions=True).y_global
     b = ob.block_step(binp, normalize_positions=False).y_global
     assert np.max(np.abs(a - b)) <= 1e-9 * np.max(np.abs(a))
+
+
+def test_query_rows_match_full_evaluation():
+    bw = dataclasses.replace(ti.BLOCK_WORKLOADS["block_tiny"], layers=1)
+    binp = ti.make_block_inputs(bw)
+    p = oracle.plan(binp.base.workload.grid, binp.base.workload.tiling, binp.base.cond_pos)
+    x = oracle.gather_tiles(binp.base.x_global, p)[0]
+    r0, r1 = int(p.tile_row_begin[1]), int(p.tile_row_begin[2])
+    model = ob.model_from_inputs(binp)
+    full = ob.tile_transformer(x[r0:r1], p.row_pos[r0:r1], binp.text[0], float(binp.tau[0]), model)
+    rows = np.array([0, 3, 17, r1 - r0 - 1])
+    part = ob.tile_transformer(x[r0:r1], p.row_pos[r0:r1], binp.text[0], float(binp.tau[0]), model,
+                               query_rows=rows)
+    assert np.allclose(part, full[rows], rtol=1e-12, atol=1e-12)

@@ -552,6 +552,153 @@ __global__ __launch_bounds__(kThreads, 2) void qkv_rope_kernel(QkvArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// rows_to_heads: row-major Q / K / V columns into the core's layouts
+// ---------------------------------------------------------------------------
+
+// For callers that compute the projections with a general GEMM (the per-tile
+// transformer block).  The source holds, per row, head h's features of Q, K
+// and V at columns q_col + h D, k_col + h D and v_col + h D (a part is absent
+// when its column is negative).  The arithmetic after the projection is that
+// of the QKV stage above: RoPE of Q and K from the row's normalized interval
+// midpoints (when `rope`), Q times log2(e)/sqrt(D), one bf16 rounding, the
+// largest squared K row norm per (batch, head, tile), V^T with vt_column's
+// order, zeros in padded rows.
+struct HeadsArgs {
+  const bf16 *src;             // [B][src_rows][ld]
+  int64_t ld, src_rows;
+  int32_t q_col, k_col, v_col;
+  const float *row_pos;        // [n_rows][3][2], tile rows only
+  int32_t rope;
+  float log2_theta_step, q_scale;
+  bf16 *q, *k, *vt;            // the core's layouts (text rows: the second segment's)
+  int64_t n_pad, vt_cols, vt_col0;
+  uint32_t *kmax2;
+  int32_t n_tiles, heads;
+  const int32_t *blk_tile, *blk_q0, *pad_begin;
+  const int64_t *trb;
+  int64_t n_rows;
+  int32_t max_rows;
+};
+
+// One workgroup = 128 rows of the padded row space of one batch entry (tile
+// rows: one block of the block table; TEXT: one 128-row block of the text
+// rows); thread = (row, half of the head dims).
+template <int D, bool TEXT>
+__global__ __launch_bounds__(256) void rows_to_heads_kernel(HeadsArgs a) {
+  constexpr int kHalf = D / 2;        // head dims per thread
+  constexpr int kPairs = D / 4;       // rotation pairs per thread
+  constexpr int kRow = D + 8;         // staged V row (bf16)
+  __shared__ __attribute__((aligned(16))) bf16 sV[kBlk * kRow];
+  const int r = threadIdx.x >> 1, half = threadIdx.x & 1;
+  const int lane = threadIdx.x & 63;
+  const int64_t b = blockIdx.y, pb = blockIdx.x;
+  int64_t src0 = 0, pad_row0 = 0;
+  int32_t nvalid = 0, tile = a.n_tiles;
+  if (TEXT) {
+    src0 = pb * kBlk;
+    pad_row0 = pb * kBlk;
+    nvalid = static_cast<int32_t>(min(static_cast<int64_t>(kBlk), a.src_rows - src0));
+  } else {
+    tile = a.blk_tile[pb];
+    if (tile < 0) return;
+    const int32_t q0 = a.blk_q0[pb];
+    int64_t r0;
+    int32_t len;
+    tile_rows(a.trb, tile, a.n_rows, a.max_rows, &r0, &len);
+    src0 = r0 + q0;
+    pad_row0 = static_cast<int64_t>(a.pad_begin[tile]) * kBlk + q0;
+    nvalid = len - q0;
+  }
+  const bool valid = r < nvalid;
+  const bf16 *row = a.src + (b * a.src_rows + src0 + (valid ? r : 0)) * a.ld;
+
+  float rc[kPairs], rs[kPairs];
+#pragma unroll
+  for (int i = 0; i < kPairs; ++i) { rc[i] = 1.f; rs[i] = 0.f; }
+  if (!TEXT && a.rope && valid) {
+    constexpr int p = D / 6;
+    const float *pp = a.row_pos + (src0 + r) * 6;
+    const float mid[3] = {0.5f * (pp[0] + pp[1]), 0.5f * (pp[2] + pp[3]), 0.5f * (pp[4] + pp[5])};
+#pragma unroll
+    for (int i = 0; i < kPairs; ++i) {
+      const int j = half * kPairs + i;
+      const int ax = j / p;
+      if (ax < 3) {
+        const float theta = exp2f(static_cast<float>(j - ax * p) * a.log2_theta_step);
+        const float mv = ax == 0 ? mid[0] : (ax == 1 ? mid[1] : mid[2]);
+        sincosf(mv * theta, &rs[i], &rc[i]);
+      }
+    }
+  }
+  // one part of one head of this thread's row: rotate (Q, K), scale (Q), round
+  auto rotated = [&](int col, float scale, bool rot, bf16x8 (&out)[kHalf / 8], float *kss) {
+#pragma unroll
+    for (int c = 0; c < kHalf / 8; ++c) {
+      const bf16x8 in = valid ? *reinterpret_cast<const bf16x8 *>(row + col + half * kHalf + 8 * c)
+                              : bf16x8{};
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const int i = 4 * c + e / 2;
+        float x0 = static_cast<float>(in[e]), x1 = static_cast<float>(in[e + 1]);
+        if (rot) {
+          const float y0 = x0 * rc[i] - x1 * rs[i];
+          const float y1 = x0 * rs[i] + x1 * rc[i];
+          x0 = y0;
+          x1 = y1;
+        }
+        out[c][e] = static_cast<bf16>(x0 * scale);
+        out[c][e + 1] = static_cast<bf16>(x1 * scale);
+        if (kss) {
+          const float r0 = static_cast<float>(out[c][e]), r1 = static_cast<float>(out[c][e + 1]);
+          *kss = fmaf(r0, r0, fmaf(r1, r1, *kss));
+        }
+      }
+    }
+  };
+  for (int h = 0; h < a.heads; ++h) {
+    const int64_t slab = b * a.heads + h;
+    bf16x8 out[kHalf / 8];
+    if (a.q_col >= 0) {
+      rotated(a.q_col + h * D, a.q_scale, !TEXT && a.rope, out, nullptr);
+      bf16 *dst = a.q + (slab * a.n_pad + pad_row0 + r) * D + half * kHalf;
+#pragma unroll
+      for (int c = 0; c < kHalf / 8; ++c) *reinterpret_cast<bf16x8 *>(dst + 8 * c) = out[c];
+    }
+    if (a.k_col >= 0) {
+      float kss = 0.f;
+      rotated(a.k_col + h * D, 1.f, !TEXT && a.rope, out, &kss);
+      bf16 *dst = a.k + (slab * a.n_pad + pad_row0 + r) * D + half * kHalf;
+#pragma unroll
+      for (int c = 0; c < kHalf / 8; ++c) *reinterpret_cast<bf16x8 *>(dst + 8 * c) = out[c];
+      kss += __shfl_xor(kss, 1);
+#pragma unroll
+      for (int off = 2; off < 64; off <<= 1) kss = fmaxf(kss, __shfl_xor(kss, off));
+      if (lane == 0)
+        atomicMax(a.kmax2 + slab * (a.n_tiles + 1) + tile, __float_as_uint(kss));
+    }
+    if (a.v_col >= 0) {
+      rotated(a.v_col + h * D, 1.f, false, out, nullptr);
+#pragma unroll
+      for (int c = 0; c < kHalf / 8; ++c)
+        *reinterpret_cast<bf16x8 *>(sV + r * kRow + half * kHalf + 8 * c) = out[c];
+      __syncthreads();
+      // V^T row d, columns 8 c8 .. 8 c8 + 7 of the block: key vt_column(col)
+      bf16 *vdst = a.vt + slab * D * a.vt_cols + a.vt_col0 + pad_row0;
+#pragma unroll
+      for (int i = 0; i < D * (kBlk / 8) / 256; ++i) {
+        const int piece = threadIdx.x + 256 * i;
+        const int d = piece / (kBlk / 8), c8 = piece % (kBlk / 8);
+        bf16x8 v8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = sV[vt_column(8 * c8 + e) * kRow + d];
+        *reinterpret_cast<bf16x8 *>(vdst + d * a.vt_cols + 8 * c8) = v8;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // core
 // ---------------------------------------------------------------------------
 
@@ -563,6 +710,7 @@ struct CoreArgs {
   int64_t n_units, n_pad, a_pad, vt_cols, n_rows, units_per_bh, total_units;
   int32_t T, heads, batch, A, n_aqb, max_rows, hidden;
   const uint32_t *kmax2;      // [B][heads][T+1] float bits of the largest squared K norm
+  int32_t tile_keys;           // 0: attend the second key segment only (cross-attention)
 };
 
 // LDS staging of one kBN-key block, unpadded rows with an XOR swizzle of the
@@ -862,7 +1010,7 @@ void attn_core_kernel(CoreArgs a) {
   const bf16 *vseg0 = a.vt + bh * D * a.vt_cols + pad0;
   const bf16 *kseg1 = a.ka + bh * a.a_pad * D;
   const bf16 *vseg1 = a.vt + bh * D * a.vt_cols + a.n_pad;
-  const int nkb0 = static_cast<int>(ceil_div(len0, kBN));
+  const int nkb0 = a.tile_keys ? static_cast<int>(ceil_div(len0, kBN)) : 0;
   const int nkb1 = static_cast<int>(ceil_div(a.A, kBN));
   const int nkb = nkb0 + nkb1;
   if (nkb == 0) return;
@@ -1244,7 +1392,8 @@ void launch_qkv(const Call &c, const void *x_tiles, const float *row_pos, const 
 }
 
 template <int D>
-void launch_core(const Call &c, hipStream_t stream) {
+void launch_core(const Call &c, hipStream_t stream, bool tile_keys = true,
+                 bool audio_queries = true) {
   const Layout &L = c.L;
   CoreArgs a{};
   a.q = ws_at<bf16>(c.ws, L.off_q);
@@ -1263,13 +1412,14 @@ void launch_core(const Call &c, hipStream_t stream) {
   a.a_pad = L.a_pad;
   a.vt_cols = L.vt_cols;
   a.n_rows = c.n_rows;
-  a.units_per_bh = a.n_units + static_cast<int64_t>(c.n_tiles) * L.n_aqb;
+  a.units_per_bh = a.n_units + (audio_queries ? static_cast<int64_t>(c.n_tiles) * L.n_aqb : 0);
   a.total_units = a.units_per_bh * c.d->batch * c.d->heads;
   a.T = c.n_tiles;
   a.heads = c.d->heads;
   a.batch = c.d->batch;
   a.A = c.d->n_audio;
-  a.n_aqb = L.n_aqb;
+  a.n_aqb = audio_queries ? L.n_aqb : 0;
+  a.tile_keys = tile_keys ? 1 : 0;
   a.max_rows = c.max_rows;
   a.hidden = L.hidden;
   a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
@@ -1384,3 +1534,91 @@ extern "C" tdp_status tdp_tile_attention(const tdp_attn_desc *desc, int32_t n_ti
   return tdp_attn_out_proj(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, y_tiles,
                            y_audio_tiles, workspace, workspace_bytes, hip_stream);
 }
+
+// ---------------------------------------------------------------------------
+// internal entry points for the per-tile transformer block
+// ---------------------------------------------------------------------------
+
+namespace tdp {
+
+tdp_status attn_tables(const tdp_attn_desc *desc, int32_t n_tiles, const int64_t *trb,
+                       int32_t max_rows, int64_t n_rows, void *ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  Call c{desc, n_tiles, trb, max_rows, n_rows, ws, ws_bytes, {}};
+  const tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  const Layout &L = c.L;
+  hipLaunchKernelGGL(block_table_kernel, dim3(1), dim3(1024), 0, stream, trb, n_tiles, n_rows,
+                     max_rows, L.npb, ws_at<int32_t>(ws, L.off_pad_begin),
+                     ws_at<int32_t>(ws, L.off_blk_tile), ws_at<int32_t>(ws, L.off_blk_q0),
+                     ws_at<uint32_t>(ws, L.off_kmax),
+                     static_cast<int64_t>(desc->batch) * desc->heads * (n_tiles + 1));
+  return launch_status();
+}
+
+tdp_status attn_rows_to_heads(const tdp_attn_desc *desc, int32_t n_tiles, const int64_t *trb,
+                              int32_t max_rows, int64_t n_rows, const bf16 *src, int64_t ld,
+                              int32_t q_col, int32_t k_col, int32_t v_col, const float *row_pos,
+                              bool text, const bf16 *text_src, int64_t text_ld, void *ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  Call c{desc, n_tiles, trb, max_rows, n_rows, ws, ws_bytes, {}};
+  const tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  const Layout &L = c.L;
+  const int D = desc->head_dim;
+  HeadsArgs a{};
+  a.src = text ? text_src : src;
+  a.ld = text ? text_ld : ld;
+  a.src_rows = text ? desc->n_audio : n_rows;
+  if (!a.src || a.ld % 8 != 0 || (text && desc->n_audio < 1)) return TDP_ERR_ARG;
+  a.q_col = q_col;
+  a.k_col = k_col;
+  a.v_col = v_col;
+  a.row_pos = row_pos;
+  a.rope = (!text && row_pos) ? 1 : 0;
+  a.log2_theta_step = static_cast<float>(-std::log2(static_cast<double>(desc->rope_base)) / (D / 6));
+  a.q_scale = static_cast<float>(1.4426950408889634 / std::sqrt(static_cast<double>(D)));
+  a.q = ws_at<bf16>(ws, text ? L.off_qa : L.off_q);
+  a.k = ws_at<bf16>(ws, text ? L.off_ka : L.off_k);
+  a.vt = ws_at<bf16>(ws, L.off_vt);
+  a.n_pad = text ? L.a_pad : L.n_pad;
+  a.vt_cols = L.vt_cols;
+  a.vt_col0 = text ? L.n_pad : 0;
+  a.kmax2 = ws_at<uint32_t>(ws, L.off_kmax);
+  a.n_tiles = n_tiles;
+  a.heads = desc->heads;
+  a.blk_tile = ws_at<int32_t>(ws, L.off_blk_tile);
+  a.blk_q0 = ws_at<int32_t>(ws, L.off_blk_q0);
+  a.pad_begin = ws_at<int32_t>(ws, L.off_pad_begin);
+  a.trb = trb;
+  a.n_rows = n_rows;
+  a.max_rows = max_rows;
+  const dim3 grid(static_cast<uint32_t>(text ? L.a_pad / kBlk : L.npb), desc->batch);
+  if (D == 128) {
+    if (text) hipLaunchKernelGGL((rows_to_heads_kernel<128, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((rows_to_heads_kernel<128, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (text) hipLaunchKernelGGL((rows_to_heads_kernel<64, true>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((rows_to_heads_kernel<64, false>), grid, dim3(256), 0, stream, a);
+  }
+  return launch_status();
+}
+
+tdp_status attn_core_run(const tdp_attn_desc *desc, int32_t n_tiles, const int64_t *trb,
+                         int32_t max_rows, int64_t n_rows, void *ws, size_t ws_bytes,
+                         bool tile_keys, hipStream_t stream) {
+  Call c{desc, n_tiles, trb, max_rows, n_rows, ws, ws_bytes, {}};
+  const tdp_status s = check_call(&c);
+  if (s != TDP_OK) return s;
+  if (desc->head_dim == 64) launch_core<64>(c, stream, tile_keys, tile_keys);
+  else launch_core<128>(c, stream, tile_keys, tile_keys);
+  return launch_status();
+}
+
+const bf16 *attn_output(const tdp_attn_desc *desc, int32_t n_tiles, int64_t n_rows, void *ws) {
+  Layout L;
+  if (make_layout(desc, n_tiles, n_rows, &L) != TDP_OK) return nullptr;
+  return ws_at<bf16>(ws, L.off_o);
+}
+
+}  // namespace tdp

@@ -1,0 +1,289 @@
+// The per-tile transformer block for gfx950: the "full transformer" every rank
+// runs on its tiles (TDP page, "What it is"), built as L blocks of
+//
+//   h = rms(x) (1 + scale_a) + shift_a;  x += gate_a * SelfAttn(h)
+//   h = rms(x);                          x += CrossAttn(h, text)
+//   h = rms(x) (1 + scale_f) + shift_f;  x += gate_f * FFN(h)
+//
+// around x_0 = X W_in and y = rms(x_L) W_out.  The page does not describe the
+// transformer; the layout above (one shared timestep modulation, text
+// cross-attention, tanh-GELU FFN of width 4D) is the reading this library
+// uses.  Every matrix product runs on gemm() (tdp_gemm.hip) with its
+// epilogue fused (GELU, SiLU, gated residual add); self- and cross-attention
+// run on the attention core; RMSNorm with the modulation is one row kernel.
+// The residual stream x is float32; GEMM operands are bf16.
+#include <cmath>
+
+#include "tdp_internal.h"
+
+namespace tdp {
+namespace {
+
+constexpr int kRowsPerWg = 4;   // rows (one per wave) per RMSNorm workgroup
+constexpr float kRmsEps = 1e-6f;
+
+// h[m][:] = bf16(rms(x[m][:]) * (1 + scale) + shift), one wave per row; shift
+// and scale = e[b][row r of 6] + table[r] for the row's batch entry b (both
+// absent: plain RMSNorm).
+__global__ __launch_bounds__(64 * kRowsPerWg) void rms_mod_kernel(
+    const float *__restrict__ x, int64_t M, int32_t D, int64_t rows_per_batch,
+    const float *__restrict__ e, const float *__restrict__ table, int32_t shift_row,
+    bf16 *__restrict__ h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 6);
+  if (m >= M) return;
+  const float *xr = x + m * D;
+  float ss = 0.f;
+  for (int j = lane; j < D; j += 64) ss = fmaf(xr[j], xr[j], ss);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + kRmsEps);
+  const int64_t b = m / rows_per_batch;
+  const float *es = e ? e + (b * 6 + shift_row) * D : nullptr;
+  const float *ts = table ? table + static_cast<int64_t>(shift_row) * D : nullptr;
+  bf16 *hr = h + m * D;
+  for (int j = lane; j < D; j += 64) {
+    float v = xr[j] * rs;
+    if (es || ts) {
+      const float shift = (es ? es[j] : 0.f) + (ts ? ts[j] : 0.f);
+      const float scale = (es ? es[D + j] : 0.f) + (ts ? ts[D + j] : 0.f);
+      v = v * (1.0f + scale) + shift;
+    }
+    hr[j] = static_cast<bf16>(v);
+  }
+}
+
+// emb[b][i] = cos(tau_b w_i), emb[b][half + i] = sin(tau_b w_i),
+// w_i = 10000^(-i / half), rounded to bf16.
+__global__ void time_embed_kernel(const float *__restrict__ tau, int32_t B, int32_t dim,
+                                  bf16 *__restrict__ emb) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int half = dim / 2;
+  if (i >= B * half) return;
+  const int b = i / half, k = i - b * half;
+  const float w = exp2f(-static_cast<float>(k) / static_cast<float>(half) * 13.287712379549449f);
+  float s, c;
+  sincosf(tau[b] * w, &s, &c);
+  emb[b * dim + k] = static_cast<bf16>(c);
+  emb[b * dim + half + k] = static_cast<bf16>(s);
+}
+
+__global__ void to_bf16_kernel(const float *__restrict__ src, int64_t n, bf16 *__restrict__ dst) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = static_cast<bf16>(src[i]);
+}
+
+size_t a256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct BlockLayout {
+  tdp_attn_desc self{}, cross{};
+  size_t off_self = 0, off_cross = 0, off_x = 0, off_h = 0, off_big = 0, off_xin = 0;
+  size_t off_emb = 0, off_e1 = 0, off_e = 0, off_ckv = 0, total = 0;
+  size_t self_bytes = 0, cross_bytes = 0;
+  int64_t D = 0, M = 0;
+};
+
+tdp_status make_block_layout(const tdp_block_desc *d, int32_t n_tiles, int64_t n_rows,
+                             BlockLayout *L) {
+  if (!d) return TDP_ERR_NULL;
+  if (d->batch < 1 || d->heads < 1 || d->n_text < 1 || d->layers < 0 || d->time_dim < 64 ||
+      d->time_dim % 64 != 0 || n_rows < 1 || n_tiles < 1)
+    return TDP_ERR_ARG;
+  if (d->C != 128 || (d->head_dim != 64 && d->head_dim != 128)) return TDP_ERR_UNSUPPORTED;
+  const int64_t D = static_cast<int64_t>(d->heads) * d->head_dim;
+  if (D % 128 != 0 || D > (1 << 16)) return TDP_ERR_UNSUPPORTED;
+  if ((d->x_dtype != TDP_F32 && d->x_dtype != TDP_BF16) ||
+      (d->y_dtype != TDP_F32 && d->y_dtype != TDP_BF16))
+    return TDP_ERR_UNSUPPORTED;
+  L->D = D;
+  L->M = static_cast<int64_t>(d->batch) * n_rows;
+  L->self = tdp_attn_desc{d->batch, 128, d->heads, d->head_dim, 0, TDP_BF16, TDP_BF16,
+                          d->rope_base};
+  L->cross = L->self;
+  L->cross.n_audio = d->n_text;
+  tdp_status s = tdp_tile_attention_workspace(&L->self, n_tiles, n_rows, &L->self_bytes);
+  if (s != TDP_OK) return s;
+  s = tdp_tile_attention_workspace(&L->cross, n_tiles, n_rows, &L->cross_bytes);
+  if (s != TDP_OK) return s;
+  const size_t M = L->M, B = d->batch;
+  size_t off = 0;
+  auto take = [&off](size_t bytes) { const size_t o = off; off = a256(off + bytes); return o; };
+  L->off_self = take(L->self_bytes);
+  L->off_cross = take(L->cross_bytes);
+  L->off_x = take(M * D * 4);
+  L->off_h = take(M * D * 2);
+  L->off_big = take(M * 4 * D * 2);
+  L->off_xin = take(M * 128 * 2);
+  L->off_emb = take(B * d->time_dim * 2);
+  L->off_e1 = take(B * D * 2);
+  L->off_e = take(B * 6 * D * 4);
+  L->off_ckv = take(B * static_cast<size_t>(d->n_text) * 2 * D * 2);
+  L->total = off;
+  return TDP_OK;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(ws) + off); }
+
+}  // namespace
+}  // namespace tdp
+
+using namespace tdp;
+
+extern "C" tdp_status tdp_block_workspace(const tdp_block_desc *desc, int32_t n_tiles,
+                                          int64_t n_rows, size_t *bytes) {
+  if (!bytes) return TDP_ERR_NULL;
+  BlockLayout L;
+  const tdp_status s = make_block_layout(desc, n_tiles, n_rows, &L);
+  if (s != TDP_OK) return s;
+  *bytes = L.total;
+  return TDP_OK;
+}
+
+extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_tiles,
+                                        const int64_t *tile_row_begin, int32_t max_tile_rows,
+                                        int64_t n_rows, const void *x_tiles,
+                                        const float *row_pos, const void *text, const float *tau,
+                                        const tdp_block_weights *w, void *y_tiles,
+                                        void *workspace, size_t workspace_bytes,
+                                        void *hip_stream) {
+  BlockLayout L;
+  tdp_status s = make_block_layout(desc, n_tiles, n_rows, &L);
+  if (s != TDP_OK) return s;
+  if (!tile_row_begin || !x_tiles || !row_pos || !text || !tau || !w || !y_tiles || !workspace ||
+      !w->w_in || !w->w_out || !w->wt1 || !w->wt2 || (desc->layers > 0 && !w->layers))
+    return TDP_ERR_NULL;
+  for (int l = 0; l < desc->layers; ++l) {
+    const tdp_block_layer &y = w->layers[l];
+    if (!y.wqkv || !y.wo || !y.cq || !y.ckv || !y.co || !y.w1 || !y.w2 || !y.table)
+      return TDP_ERR_NULL;
+  }
+  if (max_tile_rows < 1 || max_tile_rows > n_rows) return TDP_ERR_ARG;
+  if (workspace_bytes < L.total) return TDP_ERR_BUFFER;
+  if (!aligned16(workspace) || !aligned16(x_tiles) || !aligned16(text) || !aligned16(y_tiles))
+    return TDP_ERR_ALIGN;
+  const hipStream_t stream = as_stream(hip_stream);
+  const int64_t D = L.D, M = L.M, B = desc->batch, NT = desc->n_text;
+  void *ws_self = at<char>(workspace, L.off_self);
+  void *ws_cross = at<char>(workspace, L.off_cross);
+  float *x = at<float>(workspace, L.off_x);
+  bf16 *h = at<bf16>(workspace, L.off_h);
+  bf16 *big = at<bf16>(workspace, L.off_big);
+  bf16 *e1 = at<bf16>(workspace, L.off_e1);
+  float *E = at<float>(workspace, L.off_e);
+  bf16 *ckv = at<bf16>(workspace, L.off_ckv);
+  auto rms = [&](const float *table, int shift_row) {
+    hipLaunchKernelGGL(rms_mod_kernel, dim3(static_cast<uint32_t>((M + kRowsPerWg - 1) / kRowsPerWg)),
+                       dim3(64 * kRowsPerWg), 0, stream, x, M, static_cast<int32_t>(D), n_rows,
+                       table ? E : nullptr, table, shift_row, h);
+    return launch_status();
+  };
+  auto mm = [&](int epi, const bf16 *a, int64_t lda, int64_t m, const void *bt, int32_t n,
+                int32_t k, void *c, int64_t ldc, const float *g0 = nullptr,
+                const float *g1 = nullptr) {
+    GemmDesc g;
+    g.a = a;
+    g.lda = lda;
+    g.bt = static_cast<const bf16 *>(bt);
+    g.ldb = k;
+    g.M = m;
+    g.N = n;
+    g.K = k;
+    g.c = c;
+    g.ldc = ldc;
+    g.g0 = g0;
+    g.g0_stride = 6 * D;
+    g.g1 = g1;
+    g.rows_per_batch = n_rows;
+    return gemm(epi, g, stream);
+  };
+  auto proj_o = [&](const tdp_attn_desc *ad, void *aws, const void *wo, int epi,
+                    const float *g0, const float *g1) {
+    GemmDesc g;
+    g.a = attn_output(ad, n_tiles, n_rows, aws);
+    g.a_seg_rows = n_rows;
+    g.a_heads = desc->heads;
+    g.a_head_dim = desc->head_dim;
+    g.bt = static_cast<const bf16 *>(wo);
+    g.ldb = D;
+    g.M = M;
+    g.N = static_cast<int32_t>(D);
+    g.K = static_cast<int32_t>(D);
+    g.c = x;
+    g.ldc = D;
+    g.g0 = g0;
+    g.g0_stride = 6 * D;
+    g.g1 = g1;
+    g.rows_per_batch = n_rows;
+    return gemm(epi, g, stream);
+  };
+#define TDP_TRY(expr)               \
+  do {                              \
+    const tdp_status st_ = (expr);  \
+    if (st_ != TDP_OK) return st_;  \
+  } while (0)
+
+  TDP_TRY(attn_tables(&L.self, n_tiles, tile_row_begin, max_tile_rows, n_rows, ws_self,
+                      L.self_bytes, stream));
+  TDP_TRY(attn_tables(&L.cross, n_tiles, tile_row_begin, max_tile_rows, n_rows, ws_cross,
+                      L.cross_bytes, stream));
+  // x_0 = X W_in
+  const bf16 *xin = static_cast<const bf16 *>(x_tiles);
+  if (desc->x_dtype == TDP_F32) {
+    bf16 *xb = at<bf16>(workspace, L.off_xin);
+    const int64_t n = M * 128;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<const float *>(x_tiles), n, xb);
+    TDP_TRY(launch_status());
+    xin = xb;
+  }
+  TDP_TRY(mm(kEpiF32, xin, 128, M, w->w_in, static_cast<int32_t>(D), 128, x, D));
+  // timestep modulation E[b] = silu(emb(tau_b) Wt1) Wt2, shared by the layers
+  bf16 *emb = at<bf16>(workspace, L.off_emb);
+  hipLaunchKernelGGL(time_embed_kernel,
+                     dim3(static_cast<uint32_t>((B * desc->time_dim / 2 + 255) / 256)), dim3(256),
+                     0, stream, tau, static_cast<int32_t>(B), desc->time_dim, emb);
+  TDP_TRY(launch_status());
+  TDP_TRY(mm(kEpiSiluBf16, emb, desc->time_dim, B, w->wt1, static_cast<int32_t>(D), desc->time_dim,
+             e1, D));
+  TDP_TRY(mm(kEpiF32, e1, D, B, w->wt2, static_cast<int32_t>(6 * D), static_cast<int32_t>(D), E,
+             6 * D));
+  for (int l = 0; l < desc->layers; ++l) {
+    const tdp_block_layer &y = w->layers[l];
+    // self-attention, gated
+    TDP_TRY(rms(y.table, 0));
+    TDP_TRY(mm(kEpiBf16, h, D, M, y.wqkv, static_cast<int32_t>(3 * D), static_cast<int32_t>(D),
+               big, 3 * D));
+    TDP_TRY(attn_rows_to_heads(&L.self, n_tiles, tile_row_begin, max_tile_rows, n_rows, big,
+                               3 * D, 0, static_cast<int32_t>(D), static_cast<int32_t>(2 * D),
+                               row_pos, false, nullptr, 0, ws_self, L.self_bytes, stream));
+    TDP_TRY(attn_core_run(&L.self, n_tiles, tile_row_begin, max_tile_rows, n_rows, ws_self,
+                          L.self_bytes, true, stream));
+    TDP_TRY(proj_o(&L.self, ws_self, y.wo, kEpiResidGate, E + 2 * D, y.table + 2 * D));
+    // cross-attention over the text tokens
+    TDP_TRY(rms(nullptr, 0));
+    TDP_TRY(mm(kEpiBf16, h, D, M, y.cq, static_cast<int32_t>(D), static_cast<int32_t>(D), big, D));
+    TDP_TRY(attn_rows_to_heads(&L.cross, n_tiles, tile_row_begin, max_tile_rows, n_rows, big, D, 0,
+                               -1, -1, nullptr, false, nullptr, 0, ws_cross, L.cross_bytes,
+                               stream));
+    TDP_TRY(mm(kEpiBf16, static_cast<const bf16 *>(text), D, B * NT, y.ckv,
+               static_cast<int32_t>(2 * D), static_cast<int32_t>(D), ckv, 2 * D));
+    TDP_TRY(attn_rows_to_heads(&L.cross, n_tiles, tile_row_begin, max_tile_rows, n_rows, nullptr,
+                               0, -1, 0, static_cast<int32_t>(D), nullptr, true, ckv, 2 * D,
+                               ws_cross, L.cross_bytes, stream));
+    TDP_TRY(attn_core_run(&L.cross, n_tiles, tile_row_begin, max_tile_rows, n_rows, ws_cross,
+                          L.cross_bytes, false, stream));
+    TDP_TRY(proj_o(&L.cross, ws_cross, y.co, kEpiResid, nullptr, nullptr));
+    // FFN, gated
+    TDP_TRY(rms(y.table, 3));
+    TDP_TRY(mm(kEpiGeluBf16, h, D, M, y.w1, static_cast<int32_t>(4 * D), static_cast<int32_t>(D),
+               big, 4 * D));
+    TDP_TRY(mm(kEpiResidGate, big, 4 * D, M, y.w2, static_cast<int32_t>(D),
+               static_cast<int32_t>(4 * D), x, D, E + 5 * D, y.table + 5 * D));
+  }
+  // y = rms(x_L) W_out
+  TDP_TRY(rms(nullptr, 0));
+  return mm(desc->y_dtype == TDP_F32 ? kEpiF32 : kEpiBf16, h, D, M, w->w_out, 128,
+            static_cast<int32_t>(D), y_tiles, 128);
+#undef TDP_TRY
+}

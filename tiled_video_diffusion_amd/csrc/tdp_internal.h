@@ -45,4 +45,28 @@ struct GemmDesc {
 // requirements, TDP_ERR_HIP for a failed launch.
 tdp_status gemm(int epi, const GemmDesc &d, hipStream_t stream);
 
+// The attention core driven from row-major projections (the transformer
+// block).  `desc` and the tile arguments are those of the tdp_attn_* calls;
+// the workspace is sized by tdp_tile_attention_workspace.
+// Block table of the padded row space, K-norm maxima cleared.
+tdp_status attn_tables(const tdp_attn_desc *desc, int32_t n_tiles, const int64_t *trb,
+                       int32_t max_rows, int64_t n_rows, void *ws, size_t ws_bytes,
+                       hipStream_t stream);
+// Tile rows of src ([B][n_rows][ld]; Q, K, V of head h at columns
+// {q,k,v}_col + h * head_dim, negative = absent) into the core's layouts, with
+// RoPE when row_pos is given; or (text) rows of text_src ([B][n_audio][text_ld])
+// into the second key segment (K and V only, no rotation).
+tdp_status attn_rows_to_heads(const tdp_attn_desc *desc, int32_t n_tiles, const int64_t *trb,
+                              int32_t max_rows, int64_t n_rows, const bf16 *src, int64_t ld,
+                              int32_t q_col, int32_t k_col, int32_t v_col, const float *row_pos,
+                              bool text, const bf16 *text_src, int64_t text_ld, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
+// The core over the tile's keys then the second segment's (tile_keys), or the
+// second segment's only (cross-attention; no queries from that segment).
+tdp_status attn_core_run(const tdp_attn_desc *desc, int32_t n_tiles, const int64_t *trb,
+                         int32_t max_rows, int64_t n_rows, void *ws, size_t ws_bytes,
+                         bool tile_keys, hipStream_t stream);
+// The core's output O, head-major [B][heads][n_rows][head_dim] (nullptr for a bad desc).
+const bf16 *attn_output(const tdp_attn_desc *desc, int32_t n_tiles, int64_t n_rows, void *ws);
+
 }  // namespace tdp

@@ -126,3 +126,68 @@ class TdpStep:
             self.attention(stream)
         self.blend(accumulate, stream)
         self.audio(accumulate, stream)
+
+
+class BlockStep:
+    """One rank's share of a TDP step whose tile denoiser is the per-tile
+    transformer block (``tdp_block_forward``); gather and blend as in TdpStep."""
+
+    def __init__(self, binputs, normalize_positions: bool = True, world_size: int = 1,
+                 rank: int = 0, device: str = "cuda:0"):
+        inp = binputs.base
+        wl = inp.workload
+        bw = binputs.workload
+        self.s = TdpStep(inp, normalize_positions, world_size, rank, device, identity=True)
+        s = self.s
+        dev = s.device
+        p = s.plan
+        self.plan = p
+        s.y_tiles = torch.empty_like(s.x_tiles)
+        bf = torch.bfloat16
+
+        def t(a):             # [in][out] -> the library's [out][in]
+            return _dev(np.ascontiguousarray(np.asarray(a).T), dev, bf)
+
+        self.w_in, self.w_out = t(binputs.w_in), t(binputs.w_out)
+        self.wt1, self.wt2 = t(binputs.wt1), t(binputs.wt2)
+        self.layers = []
+        for lay in binputs.layers:
+            self.layers.append({
+                "wqkv": _dev(np.concatenate([np.asarray(lay[k]).T for k in ("wq", "wk", "wv")]),
+                             dev, bf),
+                "wo": t(lay["wo"]), "cq": t(lay["cq"]),
+                "ckv": _dev(np.concatenate([np.asarray(lay[k]).T for k in ("ck", "cv")]), dev, bf),
+                "co": t(lay["co"]), "w1": t(lay["w1"]), "w2": t(lay["w2"]),
+                "table": _dev(lay["table"], dev, torch.float32)})
+        self.weights = tdp.block_weights(self.w_in, self.w_out, self.wt1, self.wt2, self.layers)
+        self.text = _dev(binputs.text, dev, bf)
+        self.tau = _dev(binputs.tau, dev, torch.float32)
+        self.desc = tdp.block_desc(wl.batch, wl.channels, wl.heads, wl.head_dim, bw.n_text,
+                                   bw.layers, s.code, s.code, bw.time_dim)
+        self.ws_bytes = tdp.tdp_block_workspace(self.desc, p.n_tiles_local, p.n_rows)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+
+    @property
+    def y_tiles(self):
+        return self.s.y_tiles
+
+    @property
+    def y_global(self):
+        return self.s.y_global
+
+    def gather(self, stream=None):
+        self.s.gather(stream)
+
+    def block(self, stream=None):
+        p = self.plan
+        tdp.tdp_block_forward(self.desc, p.n_tiles_local, self.s.tile_row_begin, p.max_tile_rows,
+                              p.n_rows, self.s.x_tiles, self.s.row_pos, self.text, self.tau,
+                              self.weights, self.s.y_tiles, self.workspace, self.ws_bytes, stream)
+
+    def blend(self, accumulate: bool = False, stream=None):
+        self.s.blend(accumulate, stream)
+
+    def run(self, accumulate: bool = False, stream=None):
+        self.gather(stream)
+        self.block(stream)
+        self.blend(accumulate, stream)

@@ -60,6 +60,22 @@ class AttnDesc(C.Structure):
                 ("y_dtype", C.c_int32), ("rope_base", C.c_float)]
 
 
+class BlockDesc(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("C", C.c_int32), ("heads", C.c_int32),
+                ("head_dim", C.c_int32), ("n_text", C.c_int32), ("layers", C.c_int32),
+                ("time_dim", C.c_int32), ("x_dtype", C.c_int32), ("y_dtype", C.c_int32),
+                ("rope_base", C.c_float)]
+
+
+class BlockLayer(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("wqkv", "wo", "cq", "ckv", "co", "w1", "w2", "table")]
+
+
+class BlockWeights(C.Structure):
+    _fields_ = [("w_in", C.c_void_p), ("w_out", C.c_void_p), ("wt1", C.c_void_p),
+                ("wt2", C.c_void_p), ("layers", C.POINTER(BlockLayer))]
+
+
 _P, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
 _SIGS = {
     "tdp_status_string": (C.c_char_p, [_I32]),
@@ -79,6 +95,9 @@ _SIGS = {
                                  _P]),
     "tdp_blend_accumulate": (_I32, [_P, _I32, _I32, _I64, _I32, _P, _P, _P, _I64, _P, _I32, _P]),
     "tdp_audio_accumulate": (_I32, [_P, _I32, _I32, _I32, _I32, _I32, _P, _I32, _P]),
+    "tdp_block_workspace": (_I32, [C.POINTER(BlockDesc), _I32, _I64, C.POINTER(_SZ)]),
+    "tdp_block_forward": (_I32, [C.POINTER(BlockDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P,
+                                 C.POINTER(BlockWeights), _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -312,3 +331,37 @@ def tdp_audio_accumulate(y_audio_tiles, n_tiles_local, n_tiles_total, batch, n_a
     _check(lib().tdp_audio_accumulate(_ptr(y_audio_tiles), n_tiles_local, n_tiles_total, batch,
                                       n_audio, C_, _ptr(y_audio), int(accumulate),
                                       _stream(stream)), "tdp_audio_accumulate")
+
+
+def block_desc(batch, C_, heads, head_dim, n_text, layers, x_dtype, y_dtype, time_dim=256,
+               rope_base=10000.0) -> BlockDesc:
+    return BlockDesc(batch, C_, heads, head_dim, n_text, layers, time_dim, x_dtype, y_dtype,
+                     rope_base)
+
+
+def block_weights(w_in, w_out, wt1, wt2, layers) -> BlockWeights:
+    """``layers``: list of dicts of device tensors keyed like tdp_block_layer."""
+    arr = (BlockLayer * max(1, len(layers)))()
+    for i, lay in enumerate(layers):
+        arr[i] = BlockLayer(*(_ptr(lay[k]) for k in ("wqkv", "wo", "cq", "ckv", "co", "w1", "w2",
+                                                      "table")))
+    w = BlockWeights(_ptr(w_in), _ptr(w_out), _ptr(wt1), _ptr(wt2),
+                     C.cast(arr, C.POINTER(BlockLayer)))
+    w._keep = arr          # the host array must outlive the call
+    return w
+
+
+def tdp_block_workspace(desc: BlockDesc, n_tiles, n_rows) -> int:
+    n = C.c_size_t()
+    _check(lib().tdp_block_workspace(C.byref(desc), n_tiles, n_rows, C.byref(n)),
+           "tdp_block_workspace")
+    return n.value
+
+
+def tdp_block_forward(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_tiles, row_pos,
+                      text, tau, weights: BlockWeights, y_tiles, workspace, workspace_bytes,
+                      stream=None) -> None:
+    _check(lib().tdp_block_forward(
+        C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows, n_rows, _ptr(x_tiles),
+        _ptr(row_pos), _ptr(text), _ptr(tau), C.byref(weights), _ptr(y_tiles), _ptr(workspace),
+        workspace_bytes, _stream(stream)), "tdp_block_forward")
