@@ -25,6 +25,10 @@ with overlap 8, 32 heads x 128, bf16).  Prints ONE JSON line.
                critical path (slowest rank), and each tile timed alone, from
                which the longest-processing-time assignment's critical path
                follows; the exchange between ranks is not modeled
+  block        (--block NAME) the step with the per-tile transformer block as
+               the tile denoiser (a block workload of tdp_inputs): wall time per
+               step, algorithmic flops (GEMMs, self- and cross-attention) per
+               step over that time, against the dense bf16 MFMA peak
 """
 from __future__ import annotations
 
@@ -197,6 +201,59 @@ def shares(inp, world_size: int, reps: int = 5) -> dict:
                     "exchange) between ranks is not included"}
 
 
+def block_flops(plan, bw, wl) -> dict:
+    """Algorithmic flops of one block step (multiply-add = 2 flops)."""
+    import numpy as np
+    D, B, C = wl.hidden, wl.batch, wl.channels
+    M = B * plan.n_rows
+    nt = np.diff(plan.tile_row_begin).astype(np.float64)
+    L = bw.layers
+    gemm = (2.0 * M * C * D * 2                                       # proj_in, proj_out
+            + 2.0 * B * (bw.time_dim * D + 6.0 * D * D)               # timestep MLP
+            + L * (28.0 * M * D * D + 4.0 * B * bw.n_text * D * D))   # QKV, O, cross Q/KV/O, FFN
+    self_attn = L * 4.0 * D * B * float(np.sum(nt * nt))
+    cross_attn = L * 4.0 * D * M * bw.n_text
+    return {"gemm": gemm, "self_attention": self_attn, "cross_attention": cross_attn,
+            "total": gemm + self_attn + cross_attn}
+
+
+def block_bench(name: str, steps: int, warmup: int) -> dict:
+    """The step with the per-tile transformer block as tile denoiser."""
+    import numpy as np
+    import torch
+
+    import tdp_inputs as ti
+    from tiled_video_diffusion_amd.step import BlockStep
+
+    binp = ti.make_block_inputs(name)
+    bw, wl = binp.workload, binp.base.workload
+    st = BlockStep(binp)
+    for _ in range(warmup):
+        st.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        st.gather()
+        a.record(stream)
+        st.block()
+        b.record(stream)
+        st.blend()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    ms_block = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    fl = block_flops(st.plan, bw, wl)
+    ach = fl["total"] / (ms_block * 1e-3) / 1e12
+    return {"workload": name, "layers": bw.layers, "width": wl.hidden, "n_text": bw.n_text,
+            "tiles": st.plan.n_tiles_total, "rows": st.plan.n_rows,
+            "ms_per_step": ms_step, "block_ms": ms_block,
+            "latent_tokens_per_s": wl.batch * wl.n_gen / (ms_step * 1e-3),
+            "flops_per_step": fl, "achieved_tflops": ach, "peak_tflops": PEAK_BF16_TFLOPS,
+            "frac": ach / PEAK_BF16_TFLOPS}
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -314,6 +371,10 @@ def run(args) -> dict:
         torch.cuda.empty_cache()
         calibrate_copy(args.calibrate_copy_mib)
         out["calibrate_copy_mib"] = args.calibrate_copy_mib
+    if args.block:
+        step = None
+        torch.cuda.empty_cache()
+        out["block"] = block_bench(args.block, max(2, args.steps // 4), 1)
     if args.shares:
         step = None
         torch.cuda.empty_cache()
@@ -333,6 +394,9 @@ def main():
                     help="seconds of oracle denoiser work in the CPU baseline sample")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-blend-stress", action="store_true")
+    ap.add_argument("--block", default="",
+                    help="also time the step with the per-tile transformer block (a block "
+                         "workload name, e.g. block_t16)")
     ap.add_argument("--shares", type=int, default=0,
                     help="also time each rank's round-robin share for this many ranks "
                          "(one after another on this GPU)")

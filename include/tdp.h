@@ -305,7 +305,8 @@ typedef struct {
 } tdp_block_desc;
 
 /* One block's weights: device pointers, bf16 matrices stored [out][in]
- * row-major (the transpose of x W), 16-byte aligned. */
+ * row-major (the transpose of x W); every pointer 16-byte aligned
+ * (TDP_ERR_ALIGN otherwise). */
 typedef struct {
   const void *wqkv;            /* [3D][D]: rows of Wq^T, then Wk^T, then Wv^T */
   const void *wo;              /* [D][D] */

@@ -24,7 +24,9 @@ constexpr float kRmsEps = 1e-6f;
 
 // h[m][:] = bf16(rms(x[m][:]) * (1 + scale) + shift), one wave per row; shift
 // and scale = e[b][row r of 6] + table[r] for the row's batch entry b (both
-// absent: plain RMSNorm).
+// absent: plain RMSNorm).  VEC: D a multiple of 256, each lane moves 16-byte
+// pieces (4 floats) of the row.
+template <bool VEC>
 __global__ __launch_bounds__(64 * kRowsPerWg) void rms_mod_kernel(
     const float *__restrict__ x, int64_t M, int32_t D, int64_t rows_per_batch,
     const float *__restrict__ e, const float *__restrict__ table, int32_t shift_row,
@@ -33,23 +35,49 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void rms_mod_kernel(
   const int64_t m = static_cast<int64_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 6);
   if (m >= M) return;
   const float *xr = x + m * D;
-  float ss = 0.f;
-  for (int j = lane; j < D; j += 64) ss = fmaf(xr[j], xr[j], ss);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-  const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + kRmsEps);
   const int64_t b = m / rows_per_batch;
   const float *es = e ? e + (b * 6 + shift_row) * D : nullptr;
   const float *ts = table ? table + static_cast<int64_t>(shift_row) * D : nullptr;
   bf16 *hr = h + m * D;
-  for (int j = lane; j < D; j += 64) {
-    float v = xr[j] * rs;
-    if (es || ts) {
-      const float shift = (es ? es[j] : 0.f) + (ts ? ts[j] : 0.f);
-      const float scale = (es ? es[D + j] : 0.f) + (ts ? ts[D + j] : 0.f);
-      v = v * (1.0f + scale) + shift;
+  float ss = 0.f;
+  if constexpr (VEC) {
+    for (int j = 4 * lane; j < D; j += 256) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + j);
+      ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], ss))));
     }
-    hr[j] = static_cast<bf16>(v);
+  } else {
+    for (int j = lane; j < D; j += 64) ss = fmaf(xr[j], xr[j], ss);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + kRmsEps);
+  if constexpr (VEC) {
+    for (int j = 4 * lane; j < D; j += 256) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + j);
+      f32x4 shift = {0.f, 0.f, 0.f, 0.f}, scale = {0.f, 0.f, 0.f, 0.f};
+      if (es) {
+        shift += *reinterpret_cast<const f32x4 *>(es + j);
+        scale += *reinterpret_cast<const f32x4 *>(es + D + j);
+      }
+      if (ts) {
+        shift += *reinterpret_cast<const f32x4 *>(ts + j);
+        scale += *reinterpret_cast<const f32x4 *>(ts + D + j);
+      }
+      bf16x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = static_cast<bf16>((v[q] * rs) * (1.0f + scale[q]) + shift[q]);
+      *reinterpret_cast<bf16x4 *>(hr + j) = o;
+    }
+  } else {
+    for (int j = lane; j < D; j += 64) {
+      float v = xr[j] * rs;
+      if (es || ts) {
+        const float shift = (es ? es[j] : 0.f) + (ts ? ts[j] : 0.f);
+        const float scale = (es ? es[D + j] : 0.f) + (ts ? ts[D + j] : 0.f);
+        v = v * (1.0f + scale) + shift;
+      }
+      hr[j] = static_cast<bf16>(v);
+    }
   }
 }
 
@@ -157,7 +185,12 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
     const tdp_block_layer &y = w->layers[l];
     if (!y.wqkv || !y.wo || !y.cq || !y.ckv || !y.co || !y.w1 || !y.w2 || !y.table)
       return TDP_ERR_NULL;
+    if (!aligned16(y.wqkv) || !aligned16(y.wo) || !aligned16(y.cq) || !aligned16(y.ckv) ||
+        !aligned16(y.co) || !aligned16(y.w1) || !aligned16(y.w2) || !aligned16(y.table))
+      return TDP_ERR_ALIGN;
   }
+  if (!aligned16(w->w_in) || !aligned16(w->w_out) || !aligned16(w->wt1) || !aligned16(w->wt2))
+    return TDP_ERR_ALIGN;
   if (max_tile_rows < 1 || max_tile_rows > n_rows) return TDP_ERR_ARG;
   if (workspace_bytes < L.total) return TDP_ERR_BUFFER;
   if (!aligned16(workspace) || !aligned16(x_tiles) || !aligned16(text) || !aligned16(y_tiles))
@@ -173,9 +206,13 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
   float *E = at<float>(workspace, L.off_e);
   bf16 *ckv = at<bf16>(workspace, L.off_ckv);
   auto rms = [&](const float *table, int shift_row) {
-    hipLaunchKernelGGL(rms_mod_kernel, dim3(static_cast<uint32_t>((M + kRowsPerWg - 1) / kRowsPerWg)),
-                       dim3(64 * kRowsPerWg), 0, stream, x, M, static_cast<int32_t>(D), n_rows,
-                       table ? E : nullptr, table, shift_row, h);
+    const dim3 grid(static_cast<uint32_t>((M + kRowsPerWg - 1) / kRowsPerWg));
+    if (D % 256 == 0)
+      hipLaunchKernelGGL(rms_mod_kernel<true>, grid, dim3(64 * kRowsPerWg), 0, stream, x, M,
+                         static_cast<int32_t>(D), n_rows, table ? E : nullptr, table, shift_row, h);
+    else
+      hipLaunchKernelGGL(rms_mod_kernel<false>, grid, dim3(64 * kRowsPerWg), 0, stream, x, M,
+                         static_cast<int32_t>(D), n_rows, table ? E : nullptr, table, shift_row, h);
     return launch_status();
   };
   auto mm = [&](int epi, const bf16 *a, int64_t lda, int64_t m, const void *bt, int32_t n,

@@ -200,8 +200,170 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// Wide form for large GEMMs: one workgroup = 256 rows x 256
+// columns, 8 waves as 4 (rows) x 2 (columns), each wave 64 x 128 (2 x 4
+// MFMA tiles).  A fragment read from LDS feeds 4 MFMAs and a B^T fragment 2
+// (0.75 reads per MFMA against 1.25 above), and the operand bytes per MFMA
+// drop by a third.  64-wide k chunks of A and B^T (32 KB each) in two LDS
+// stages.
+constexpr int kWRows = 256, kWCols = 256;
+constexpr int kWALoads = kWRows * kGK * 2 / 1024 / kGWaves;   // 4
+constexpr int kWBLoads = kWCols * kGK * 2 / 1024 / kGWaves;   // 4
+
+template <int EPI, int HD>
+__global__ __launch_bounds__(kGThreads, 1) void gemm_wide_kernel(GemmArgs g) {
+  static_assert(HD % kGK == 0, "whole k chunks per head");
+  __shared__ __attribute__((aligned(16))) bf16 sA0[kWRows * kGK], sA1[kWRows * kGK];
+  __shared__ __attribute__((aligned(16))) bf16 sB0[kWCols * kGK], sB1[kWCols * kGK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave & 3, wn = wave >> 2;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kWRows;
+  const int64_t col0 = static_cast<int64_t>(blockIdx.y) * kWCols;
+  const int64_t M = g.M;
+  uint64_t aoff[kWALoads], boff[kWBLoads];
+#pragma unroll
+  for (int i = 0; i < kWALoads; ++i) {
+    const int pos = (i * kGWaves + uwave) * 64 + lane;
+    const int r = pos / 8, slot = pos % 8;
+    const int64_t gr = min(row0 + r, M - 1);
+    int64_t el;
+    if constexpr (HD > 0) {
+      const int64_t L = g.a_seg_rows;
+      const int64_t seg = gr / L;
+      el = (seg * g.a_heads * L + (gr - seg * L)) * HD;
+    } else {
+      el = gr * g.lda;
+    }
+    aoff[i] = static_cast<uint64_t>(el * 2 + 16 * g_slot(r, slot));
+  }
+#pragma unroll
+  for (int i = 0; i < kWBLoads; ++i) {
+    const int pos = (i * kGWaves + uwave) * 64 + lane;
+    const int r = pos / 8, slot = pos % 8;
+    boff[i] = static_cast<uint64_t>((col0 + r) * g.ldb * 2 + 16 * g_slot(r, slot));
+  }
+  const char *abase = reinterpret_cast<const char *>(g.a);
+  const char *bbase = reinterpret_cast<const char *>(g.bt);
+  auto load_chunk = [&](int c, bf16 *sa, bf16 *sb) __attribute__((always_inline)) {
+    const int64_t kb = static_cast<int64_t>(c) * kGK * 2;
+    int64_t ab = kb;
+    if constexpr (HD > 0) {
+      constexpr int kPerHead = HD / kGK;
+      const int h = c / kPerHead;
+      ab = (static_cast<int64_t>(h) * g.a_seg_rows * HD + (c - h * kPerHead) * kGK) * 2;
+    }
+#pragma unroll
+    for (int i = 0; i < kWALoads; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(abase + ab + aoff[i]),
+                                       (lvoid_t *)(sa + (i * kGWaves + uwave) * 512), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kWBLoads; ++i)
+      __builtin_amdgcn_global_load_lds((gvoid_t *)(bbase + kb + boff[i]),
+                                       (lvoid_t *)(sb + (i * kGWaves + uwave) * 512), 16, 0, 0);
+  };
+  int32_t afo[2][kGK / 16], bfo[4][kGK / 16];
+#pragma unroll
+  for (int ks = 0; ks < kGK / 16; ++ks) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int ar = 64 * wm + 32 * mt + l32;
+      afo[mt][ks] = ar * kGK + 8 * g_slot(ar, 2 * ks + hh);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const int br = 128 * wn + 32 * ct + l32;
+      bfo[ct][ks] = br * kGK + 8 * g_slot(br, 2 * ks + hh);
+    }
+  }
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x16{};
+  auto compute = [&](const bf16 *sa, const bf16 *sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(sa + afo[0][ks]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(sa + afo[1][ks]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const bf16x8 bfr = *reinterpret_cast<const bf16x8 *>(sb + bfo[ct][ks]);
+        acc[0][ct] = mfma32(a0, bfr, acc[0][ct]);
+        acc[1][ct] = mfma32(a1, bfr, acc[1][ct]);
+      }
+    }
+  };
+  const int nc = g.K / kGK;
+  load_chunk(0, sA0, sB0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // Step c: load chunk c+1 into the other stage (last read in step c-1),
+  // compute chunk c, wait for the loads, barrier.
+  int c = 0;
+  for (; c + 2 <= nc; c += 2) {
+    load_chunk(c + 1, sA1, sB1);
+    compute(sA0, sB0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (c + 2 < nc) load_chunk(c + 2, sA0, sB0);
+    compute(sA1, sB1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  if (c < nc) compute(sA0, sB0);
+
+  // acc[mt][ct][v]: row 64 wm + 32 mt + 8 (v/4) + 4 hh + v%4, column
+  // 128 wn + 32 ct + l32
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int64_t base = row0 + 64 * wm + 32 * mt;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
+      if (r >= M) continue;
+      float gb[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (EPI == kEpiResidGate) {
+        const int64_t b = r / g.rows_per_batch;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int64_t n = col0 + 128 * wn + 32 * ct + l32;
+          gb[ct] = (g.g0 ? g.g0[b * g.g0_stride + n] : 0.f) + (g.g1 ? g.g1[n] : 0.f);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int64_t idx = r * g.ldc + col0 + 128 * wn + 32 * ct + l32;
+        const float x = acc[mt][ct][v];
+        if constexpr (EPI == kEpiBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(x);
+        if constexpr (EPI == kEpiF32) static_cast<float *>(g.c)[idx] = x;
+        if constexpr (EPI == kEpiGeluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(gelu_tanh(x));
+        if constexpr (EPI == kEpiSiluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(silu(x));
+        if constexpr (EPI == kEpiResid) static_cast<float *>(g.c)[idx] += x;
+        if constexpr (EPI == kEpiResidGate) static_cast<float *>(g.c)[idx] += gb[ct] * x;
+      }
+    }
+  }
+}
+
+#ifndef TDP_GEMM_WIDE
+#define TDP_GEMM_WIDE 1
+#endif
+
 template <int EPI>
 tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) {
+  // the wide form for a multiple of 256 columns and enough rows
+  if (TDP_GEMM_WIDE && a.N % kWCols == 0 && a.M >= 8 * kWRows) {
+    const dim3 wgrid(static_cast<uint32_t>(cdiv(a.M, kWRows)), static_cast<uint32_t>(a.N / kWCols));
+    if (hd == 0)
+      hipLaunchKernelGGL((gemm_wide_kernel<EPI, 0>), wgrid, dim3(kGThreads), 0, stream, a);
+    else if (hd == 64)
+      hipLaunchKernelGGL((gemm_wide_kernel<EPI, 64>), wgrid, dim3(kGThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_wide_kernel<EPI, 128>), wgrid, dim3(kGThreads), 0, stream, a);
+    return launch_status();
+  }
   if (hd == 0)
     hipLaunchKernelGGL((gemm_kernel<EPI, 0>), grid, dim3(kGThreads), 0, stream, a);
   else if (hd == 64)
