@@ -207,6 +207,14 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
 // drop by a third.  64-wide k chunks of A and B^T (32 KB each) in two LDS
 // stages.
 constexpr int kWRows = 256, kWCols = 256;
+// Tile order of the wide form: consecutive workgroup ids go to the 8 XCDs in
+// turn; the id is remapped so each XCD walks a contiguous range of tiles,
+// taken TDP_GEMM_GROUP_M row blocks at a time down a column of tiles (the
+// workgroups that run together on one XCD then share their A and B^T tiles
+// in its L2).  0: the plain order, row blocks first.
+#ifndef TDP_GEMM_GROUP_M
+#define TDP_GEMM_GROUP_M 4
+#endif
 constexpr int kWALoads = kWRows * kGK * 2 / 1024 / kGWaves;   // 4
 constexpr int kWBLoads = kWCols * kGK * 2 / 1024 / kGWaves;   // 4
 
@@ -219,9 +227,27 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_wide_kernel(GemmArgs g) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int uwave = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave & 3, wn = wave >> 2;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kWRows;
-  const int64_t col0 = static_cast<int64_t>(blockIdx.y) * kWCols;
   const int64_t M = g.M;
+  const int64_t nm = cdiv(M, kWRows), nn = g.N / kWCols;
+  int64_t tm, tn;
+  if constexpr (TDP_GEMM_GROUP_M > 0) {
+    const int64_t G = gridDim.x;   // a multiple of 8, >= nm * nn
+    const int64_t bid = blockIdx.x;
+    const int64_t lid = (bid % 8) * (G / 8) + bid / 8;
+    if (lid >= nm * nn) return;
+    const int64_t per_group = static_cast<int64_t>(TDP_GEMM_GROUP_M) * nn;
+    const int64_t grp = lid / per_group;
+    const int64_t first_m = grp * TDP_GEMM_GROUP_M;
+    const int64_t gm = min(static_cast<int64_t>(TDP_GEMM_GROUP_M), nm - first_m);
+    const int64_t in = lid - grp * per_group;
+    tm = first_m + in % gm;
+    tn = in / gm;
+  } else {
+    tm = blockIdx.x;
+    tn = blockIdx.y;
+  }
+  const int64_t row0 = tm * kWRows;
+  const int64_t col0 = tn * kWCols;
   uint64_t aoff[kWALoads], boff[kWBLoads];
 #pragma unroll
   for (int i = 0; i < kWALoads; ++i) {
@@ -355,7 +381,10 @@ template <int EPI>
 tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) {
   // the wide form for a multiple of 256 columns and enough rows
   if (TDP_GEMM_WIDE && a.N % kWCols == 0 && a.M >= 8 * kWRows) {
-    const dim3 wgrid(static_cast<uint32_t>(cdiv(a.M, kWRows)), static_cast<uint32_t>(a.N / kWCols));
+    const int64_t nm = cdiv(a.M, kWRows), nn = a.N / kWCols;
+    const dim3 wgrid = TDP_GEMM_GROUP_M > 0
+                           ? dim3(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8))
+                           : dim3(static_cast<uint32_t>(nm), static_cast<uint32_t>(nn));
     if (hd == 0)
       hipLaunchKernelGGL((gemm_wide_kernel<EPI, 0>), wgrid, dim3(kGThreads), 0, stream, a);
     else if (hd == 64)
