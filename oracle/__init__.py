@@ -17,6 +17,10 @@ step, in plain NumPy:
   blend.py      gather of tile rows and the weighted blend into the global
               latent that stands in for the multi-GPU all_reduce (float64)
   tdp_step.py   one whole step built from the three
+  block.py      the per-tile transformer block (norms, timestep modulation,
+              self- and cross-attention, FFN) and a step that uses it
+  upscale.py    the upscale loop: re-noise, TDP velocity and Euler update per
+              step, seam spread of the tiles
 
 Where the pages are silent, the readings used are stated in each function's
 docstring.  Pins (tests that tie each function to something other than
@@ -31,3 +35,5 @@ from .tile_plan import (Plan, plan, dim_boxes, dim_weights, PlanError,  # noqa: 
 from .denoise import rope_angles, apply_rope, tile_forward  # noqa: F401
 from .blend import gather_tiles, blend_tiles, audio_mean  # noqa: F401
 from .tdp_step import step  # noqa: F401
+from .upscale import (linear_sigmas, renoise, euler_step, seam_spread,  # noqa: F401
+                      upscale_loop)

@@ -31,6 +31,7 @@ import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "Inputs", "make_inputs",
            "round_to_bf16", "draw_cond_pos", "BlockWorkload", "BLOCK_WORKLOADS",
+           "UpscaleWorkload", "UPSCALE_WORKLOADS", "UpscaleInputs", "make_upscale_inputs",
            "BlockInputs", "make_block_inputs"]
 
 
@@ -266,3 +267,47 @@ def make_block_inputs(bw: BlockWorkload | str) -> BlockInputs:
     text = round_to_bf16(rng.standard_normal((B, bw.n_text, D), dtype=np.float32))
     tau = rng.uniform(0.0, 1000.0, size=B).astype(np.float32)
     return BlockInputs(bw, base, w_in, w_out, wt1, wt2, layers, text, tau)
+
+
+# ---------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class UpscaleWorkload:
+    """The TDP upscale loop: a block workload's latent, taken as the clean
+    stage-1 result at the target grid, re-noised to ``sigma0`` and denoised in
+    ``n_steps`` steps."""
+    name: str
+    block: str             # a BLOCK_WORKLOADS name
+    sigma0: float
+    n_steps: int
+
+
+UPSCALE_WORKLOADS = {
+    # three steps from sigma 0.5 on the 4-tile 2x16x16 latent (with negative-time
+    # conditioning): the oracle runs all of it
+    "upscale_tiny": UpscaleWorkload("upscale_tiny", block="block_tiny", sigma0=0.5, n_steps=3),
+    # two steps from sigma 0.3, D = 256
+    "upscale_d128": UpscaleWorkload("upscale_d128", block="block_d128", sigma0=0.3, n_steps=2),
+    # four steps from sigma 0.3 on the 16-tile step at D = 4096
+    "upscale_t16": UpscaleWorkload("upscale_t16", block="block_t16", sigma0=0.3, n_steps=4),
+}
+
+
+@dataclasses.dataclass
+class UpscaleInputs:
+    workload: UpscaleWorkload
+    block: BlockInputs                # weights, text; block.base.x_global is the stage-1 latent
+    noise: np.ndarray                 # [B][N][C] float32, the re-injected noise
+
+
+def make_upscale_inputs(uw: UpscaleWorkload | str) -> UpscaleInputs:
+    """Seeded inputs of an upscale workload: the block workload's inputs and
+    the noise, N(0, 1) float32 ``[B][N][C]`` from ``default_rng(seed + 2000)``
+    (N generated tokens; conditioning rows get no noise)."""
+    if isinstance(uw, str):
+        uw = UPSCALE_WORKLOADS[uw]
+    binp = make_block_inputs(uw.block)
+    wl = binp.base.workload
+    rng = np.random.default_rng(wl.seed + 2000)
+    noise = rng.standard_normal((wl.batch, wl.n_gen, wl.channels), dtype=np.float32)
+    return UpscaleInputs(uw, binp, noise)

@@ -229,3 +229,59 @@ def test_rms_eps_outside_root_is_caught(monkeypatch):
                             np.sqrt(np.mean(np.asarray(x) ** 2, axis=-1, keepdims=True)) + eps))
     with pytest.raises(AssertionError):
         tblock.test_rms_norm_closed_forms()
+
+
+# --------------------------------------------------------------------------
+# the upscale loop
+# --------------------------------------------------------------------------
+
+import oracle.upscale as oup  # noqa: E402
+import tests.test_oracle_upscale as tup  # noqa: E402
+
+_SIGMAS = oup.linear_sigmas(0.8, 3)
+
+
+def test_euler_sign_error_is_caught(monkeypatch):
+    def step(x, v, sigma, sigma_next, n_gen):
+        out = np.array(x, dtype=np.float64, copy=True)
+        out[:, :n_gen] += (np.float64(sigma) - np.float64(sigma_next)) * v[:, :n_gen]
+        return out
+    monkeypatch.setattr(oup, "euler_step", step)
+    with pytest.raises(AssertionError):
+        tup.test_straight_path_is_followed_exactly(_SIGMAS)
+
+
+def test_renoise_without_signal_decay_is_caught(monkeypatch):
+    def renoise(x1, noise, sigma0, n_gen):
+        x = np.array(x1, dtype=np.float64, copy=True)
+        x[:, :n_gen] += np.float64(sigma0) * noise
+        return x
+    monkeypatch.setattr(oup, "renoise", renoise)
+    with pytest.raises(AssertionError):
+        tup.test_straight_path_is_followed_exactly(_SIGMAS)
+
+
+def test_euler_on_conditioning_rows_is_caught(monkeypatch):
+    def step(x, v, sigma, sigma_next, n_gen):
+        return np.asarray(x, dtype=np.float64) + (np.float64(sigma_next) - np.float64(sigma)) * v
+    monkeypatch.setattr(oup, "euler_step", step)
+    with pytest.raises(AssertionError):
+        tup.test_straight_path_is_followed_exactly(_SIGMAS)
+
+
+def test_unweighted_seam_spread_is_caught(monkeypatch):
+    def seam(y_tiles, p, n_gen):
+        q = _dc.replace(p, row_weight=np.ones_like(p.row_weight))
+        return _ORIG_SEAM(y_tiles, q, n_gen)
+    monkeypatch.setattr(oup, "seam_spread", seam)
+    with pytest.raises(AssertionError):
+        tup.test_seam_spread_two_tile_closed_form()
+
+
+def test_timestep_without_scale_is_caught(monkeypatch):
+    monkeypatch.setattr(oup, "TAU_PER_SIGMA", 1.0)
+    with pytest.raises(AssertionError):
+        tup.test_one_step_is_the_block_step()
+
+
+_ORIG_SEAM = oup.seam_spread
