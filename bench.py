@@ -29,6 +29,12 @@ with overlap 8, 32 heads x 128, bf16).  Prints ONE JSON line.
                the tile denoiser (a block workload of tdp_inputs): wall time per
                step, algorithmic flops (GEMMs, self- and cross-attention) per
                step over that time, against the dense bf16 MFMA peak
+  loop         (--loop NAME) the upscale loop (an upscale workload of
+               tdp_inputs): re-noise, then per step gather -> transformer ->
+               blend fused with the Euler update; wall time per step, each
+               step's seam spread, and the fused blend/Euler kernel alone on the
+               workload's plan against 8 TB/s (algorithmic bytes: tile rows,
+               the latent read and written, the inverse map)
 """
 from __future__ import annotations
 
@@ -254,6 +260,77 @@ def block_bench(name: str, steps: int, warmup: int) -> dict:
             "frac": ach / PEAK_BF16_TFLOPS}
 
 
+def blend_euler_bytes(plan, n_gen, batch, C) -> int:
+    """Algorithmic bytes of one tdp_blend_euler launch (float32 tile rows)."""
+    return (batch * plan.n_rows * C * 4 + 2 * batch * n_gen * C * 4
+            + plan.n_rows * (4 + 4) + (n_gen + 1) * 8)
+
+
+def loop_bench(name: str, reps: int, warmup: int) -> dict:
+    """The upscale loop, and its fused blend/Euler kernel alone."""
+    import numpy as np
+    import torch
+
+    import tdp_inputs as ti
+    from tiled_video_diffusion_amd import tdp
+    from tiled_video_diffusion_amd.step import UpscaleLoop
+
+    up = ti.make_upscale_inputs(name)
+    wl = up.block.base.workload
+    lp = UpscaleLoop(up)
+    for _ in range(warmup):
+        lp.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        lp.run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms_loop = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    seam = lp.seam.cpu().numpy()
+    # the fused blend/Euler kernel alone, float32 tile rows of this plan, seam on
+    p = lp.bs.plan
+    B, C, N = wl.batch, wl.channels, wl.n_gen
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    y = torch.randn((B, p.n_rows, C), generator=g, device="cuda:0", dtype=torch.float32)
+    x = lp.x.clone()
+    ws_bytes = tdp.tdp_blend_euler_workspace(B, N, C)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    seam_d = torch.zeros(3, dtype=torch.float64, device="cuda:0")
+    s = lp.bs.s
+    n_launch = 50
+
+    def launch():
+        tdp.tdp_blend_euler(y, tdp.TDP_F32, B, p.n_rows, C, s.dst_row_begin, s.dst_rows,
+                            s.row_weight, N, x, lp.n_dst, 0.3, 0.225, seam_d, ws, ws_bytes,
+                            stream)
+
+    for _ in range(3):
+        launch()
+    ke = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_launch)]
+    for a, b in ke:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ke]))
+    nbytes = blend_euler_bytes(p, N, B, C)
+    gbs = nbytes / (k_ms * 1e-3) / 1e9
+    return {"workload": name, "block": up.workload.block, "sigma0": up.workload.sigma0,
+            "n_steps": lp.n_steps, "ms_per_loop": ms_loop,
+            "ms_per_step": ms_loop / max(lp.n_steps, 1),
+            "latent_tokens_per_s_per_step": B * N / (ms_loop / max(lp.n_steps, 1) * 1e-3),
+            "seam_relative_spread": [float(v) for v in seam[:lp.n_steps, 2]],
+            "seam_note": "synthetic weights: the spread shows the metric, not a quality",
+            "blend_euler": {"ms_per_launch": k_ms, "bytes_per_launch": nbytes,
+                            "achieved": gbs, "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                            "frac": gbs / PEAK_HBM_GBS, "with_seam": True}}
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -375,6 +452,10 @@ def run(args) -> dict:
         step = None
         torch.cuda.empty_cache()
         out["block"] = block_bench(args.block, max(2, args.steps // 4), 1)
+    if args.loop:
+        step = None
+        torch.cuda.empty_cache()
+        out["loop"] = loop_bench(args.loop, max(2, args.steps // 8), 1)
     if args.shares:
         step = None
         torch.cuda.empty_cache()
@@ -397,6 +478,9 @@ def main():
     ap.add_argument("--block", default="",
                     help="also time the step with the per-tile transformer block (a block "
                          "workload name, e.g. block_t16)")
+    ap.add_argument("--loop", default="",
+                    help="also time the upscale loop (an upscale workload name, e.g. "
+                         "upscale_t16)")
     ap.add_argument("--shares", type=int, default=0,
                     help="also time each rank's round-robin share for this many ranks "
                          "(one after another on this GPU)")

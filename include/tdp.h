@@ -348,6 +348,96 @@ tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_tiles,
                              void *y_tiles, void *workspace, size_t workspace_bytes,
                              void *hip_stream);
 
+/* ------------------------------------------------------------------------ */
+
+/* The upscale loop.  TDP page, "When to use it" (the note on stages): TDP is
+ * the upscale stage, run on a first stage's full-frame result; it re-injects
+ * noise up to a first sigma, then denoises, and its tiles drift apart more as
+ * that sigma grows; conditioning on the stage-1 result at negative time
+ * indices keeps them together.  The page names no sampler.  This library's
+ * reading is the flow-matching form:
+ *  - a latent at noise level sigma in [0, 1] is (1 - sigma) x0 + sigma eps;
+ *  - the blend of the tile outputs is the velocity v (eps - x0);
+ *  - one step from sigma_i to sigma_{i+1}: x += (sigma_{i+1} - sigma_i) v,
+ *    on the generated rows only; conditioning rows keep their clean tokens;
+ *  - the transformer's timestep is tau = 1000 sigma;
+ *  - seam spread of a step: over the batch entries and the generated tokens
+ *    that two or more of the given rows cover, S2 = sum_r w_r |y_r - v|^2 and
+ *    S0 = sum |v|^2; reported as {S2, S0, sqrt(S2 / S0)} (0 when S0 = 0). */
+
+/* sigmas[i] = sigma0 (1 - i / n_steps), i = 0..n_steps, computed in double and
+ * rounded once to float; sigmas[0] = sigma0 when n_steps = 0.  Host array of
+ * n_steps + 1 floats, caller-owned.  Errors: TDP_ERR_NULL, TDP_ERR_ARG
+ * (n_steps < 0, sigma0 outside [0, 1]). */
+tdp_status tdp_linear_sigmas(float sigma0, int32_t n_steps, float *sigmas);
+
+/* x[b][n] = (1 - sigma0) x_stage1[b][n] + sigma0 noise[b][n] for generated
+ * rows n < n_gen, x_stage1[b][n] for the conditioning rows [n_gen, n_dst_rows).
+ *  x_stage1, x: device [batch][n_dst_rows][C] float32 (x may be x_stage1).
+ *  noise:       device [batch][n_gen][C] float32.
+ * C a multiple of 4; buffers 16-byte aligned.  Asynchronous on hip_stream.
+ * Errors: TDP_ERR_ARG, TDP_ERR_NULL, TDP_ERR_ALIGN, TDP_ERR_HIP. */
+tdp_status tdp_renoise(const float *x_stage1, const float *noise, int32_t batch, int64_t n_gen,
+                       int64_t n_dst_rows, int32_t C, float sigma0, float *x,
+                       void *hip_stream);
+
+/* Workspace bytes tdp_blend_euler needs when it reports the seam spread. */
+tdp_status tdp_blend_euler_workspace(int32_t batch, int64_t n_gen, int32_t C, size_t *bytes);
+
+/* One Euler step on the blended tile outputs: for every generated token
+ * n < n_gen, v = the tdp_blend_accumulate sum of its rows (same order), and
+ * x[b][n] += (sigma_next - sigma) v; rows [n_gen, n_dst_rows) of x are not
+ * touched.  The blended v is not stored.
+ *  y_tiles:   device [batch][n_rows][C] (dtype), the tile outputs.
+ *  dst_row_begin / dst_rows / row_weight: tdp_plan's inverse map and weights
+ *             on the device.
+ *  x:         device [batch][n_dst_rows][C] float32, updated in place.
+ *  seam:      device double[3] receiving {S2, S0, sqrt(S2 / S0)} of this step,
+ *             or NULL; then workspace may be NULL.
+ *  workspace: device, tdp_blend_euler_workspace bytes (partial sums).
+ * Asynchronous on hip_stream.  Errors: TDP_ERR_ARG, TDP_ERR_UNSUPPORTED,
+ * TDP_ERR_NULL, TDP_ERR_BUFFER, TDP_ERR_ALIGN, TDP_ERR_HIP. */
+tdp_status tdp_blend_euler(const void *y_tiles, int32_t dtype, int32_t batch, int64_t n_rows,
+                           int32_t C, const int64_t *dst_row_begin, const int32_t *dst_rows,
+                           const float *row_weight, int64_t n_gen, float *x, int64_t n_dst_rows,
+                           float sigma, float sigma_next, double *seam, void *workspace,
+                           size_t workspace_bytes, void *hip_stream);
+
+/* A rank's plan (tdp_plan's arrays) copied to the device, for the loop. */
+typedef struct {
+  int32_t n_tiles, max_tile_rows;
+  int64_t n_rows;              /* tile rows of all local tiles */
+  int64_t n_gen;               /* N = F * H * W generated tokens */
+  int64_t n_dst_rows;          /* N + M */
+  const int64_t *tile_row_begin;   /* [n_tiles + 1] */
+  const int32_t *row_src;          /* [n_rows] */
+  const float *row_weight;         /* [n_rows] */
+  const float *row_pos;            /* [n_rows][3][2] */
+  const int64_t *dst_row_begin;    /* [n_dst_rows + 1] */
+  const int32_t *dst_rows;         /* [n_rows] */
+} tdp_plan_dev;
+
+/* Workspace bytes of tdp_upscale_loop (the block's workspace, float32 tile
+ * buffers, partial sums).  desc->x_dtype and y_dtype must be TDP_F32
+ * (TDP_ERR_UNSUPPORTED otherwise). */
+tdp_status tdp_upscale_workspace(const tdp_block_desc *desc, const tdp_plan_dev *plan,
+                                 size_t *bytes);
+
+/* n_steps steps of the upscale loop on x, the re-noised latent (tdp_renoise):
+ * for i = 0 .. n_steps - 1, tau = 1000 sigmas[i]; x_tiles = gather(x);
+ * y_tiles = tdp_block_forward(x_tiles, tau); tdp_blend_euler(y_tiles, sigmas[i],
+ * sigmas[i + 1]).
+ *  sigmas: host float[n_steps + 1], each in [0, 1] (tdp_linear_sigmas).
+ *  x:      device [batch][n_dst_rows][C] float32, in place; holds the result.
+ *  seam:   device double[n_steps][3] (per step, as tdp_blend_euler) or NULL.
+ *  text, weights: as tdp_block_forward.
+ * Asynchronous on hip_stream; the library allocates nothing.  Errors: those
+ * of tdp_block_forward, TDP_ERR_ARG (a sigma outside [0, 1]). */
+tdp_status tdp_upscale_loop(const tdp_block_desc *desc, const tdp_plan_dev *plan,
+                            const tdp_block_weights *weights, const void *text,
+                            const float *sigmas, int32_t n_steps, float *x, double *seam,
+                            void *workspace, size_t workspace_bytes, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -240,3 +240,50 @@ def test_block_validation():
     d = tdp.block_desc(**ok)
     assert L.tdp_block_forward(ctypes.byref(d), 4, None, 130, 520, None, None, None, None,
                                ctypes.byref(w), None, None, 0, None) == -1
+
+
+@pytest.mark.parametrize("sigma0,n_steps", [(0.3, 3), (1.0, 4), (0.5, 1), (0.7, 0), (0.123, 7),
+                                            (0.0, 2)])
+def test_linear_sigmas_match_oracle_bitwise(sigma0, n_steps):
+    import oracle.upscale as ou
+    assert np.array_equal(tdp.tdp_linear_sigmas(sigma0, n_steps), ou.linear_sigmas(sigma0, n_steps))
+
+
+def test_upscale_validation():
+    L = tdp.lib()
+    n = ctypes.c_size_t()
+    out = (ctypes.c_float * 4)()
+    assert L.tdp_linear_sigmas(1.5, 3, out) == -2
+    assert L.tdp_linear_sigmas(0.5, -1, out) == -2
+    assert L.tdp_linear_sigmas(float("nan"), 3, out) == -2
+    assert L.tdp_linear_sigmas(0.5, 3, None) == -1
+    # re-noise: sigma outside [0, 1], missing buffers, C not a multiple of 4
+    assert L.tdp_renoise(None, None, 1, 8, 10, 128, 1.5, None, None) == -2
+    assert L.tdp_renoise(None, None, 1, 8, 10, 128, 0.5, None, None) == -1
+    assert L.tdp_renoise(None, None, 1, 8, 10, 126, 0.5, None, None) == -2
+    assert L.tdp_renoise(None, None, 1, 11, 10, 128, 0.5, None, None) == -2   # n_gen > n_dst
+    # blend_euler: workspace sizes and argument checks
+    assert tdp.tdp_blend_euler_workspace(1, 512, 128) >= 64 * 8
+    assert L.tdp_blend_euler_workspace(0, 512, 128, ctypes.byref(n)) == -2
+    assert L.tdp_blend_euler(None, 5, 1, 10, 128, None, None, None, 8, None, 10, 0.5, 0.25, None,
+                             None, 0, None) == -4
+    assert L.tdp_blend_euler(None, 0, 1, 10, 128, None, None, None, 11, None, 10, 0.5, 0.25,
+                             None, None, 0, None) == -2
+    assert L.tdp_blend_euler(None, 0, 1, 10, 128, None, None, None, 8, None, 10, 0.5, 0.25,
+                             None, None, 0, None) == -1
+    # the loop: float32 state only, plan sizes checked before any launch
+    d = tdp.block_desc(1, 128, 2, 64, 16, 2, tdp.TDP_F32, tdp.TDP_F32)
+    p = tdp.plan_dev(4, 130, 520, 512, 520, None, None, None, None, None, None)
+    assert tdp.tdp_upscale_workspace(d, p) > tdp.tdp_block_workspace(d, 4, 520)
+    d_bf = tdp.block_desc(1, 128, 2, 64, 16, 2, tdp.TDP_BF16, tdp.TDP_F32)
+    assert L.tdp_upscale_workspace(ctypes.byref(d_bf), ctypes.byref(p), ctypes.byref(n)) == -4
+    for bad in [dict(n_gen=0), dict(n_dst_rows=500), dict(max_tile_rows=600), dict(n_tiles=0)]:
+        q = tdp.plan_dev(**{**dict(n_tiles=4, max_tile_rows=130, n_rows=520, n_gen=512,
+                                   n_dst_rows=520, tile_row_begin=None, row_src=None,
+                                   row_weight=None, row_pos=None, dst_row_begin=None,
+                                   dst_rows=None), **bad})
+        assert L.tdp_upscale_workspace(ctypes.byref(d), ctypes.byref(q), ctypes.byref(n)) == -2, bad
+    w = tdp.BlockWeights()
+    sig = (ctypes.c_float * 4)(0.5, 0.3, 0.1, 0.0)
+    assert L.tdp_upscale_loop(ctypes.byref(d), ctypes.byref(p), ctypes.byref(w), None, sig, 3,
+                              None, None, None, 0, None) == -1

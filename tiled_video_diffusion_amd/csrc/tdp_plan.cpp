@@ -270,4 +270,20 @@ tdp_status tdp_balanced_tile_split(int32_t n, int32_t *h_tiles, int32_t *w_tiles
   return TDP_OK;
 }
 
+// The upscale loop's schedule (TDP page, "When to use it": the upscale stage
+// starts from a first sigma; the page names no schedule): linear from sigma0
+// to 0 in n_steps steps, each value computed in double and rounded once.
+tdp_status tdp_linear_sigmas(float sigma0, int32_t n_steps, float *sigmas) {
+  if (!sigmas) return TDP_ERR_NULL;
+  if (n_steps < 0 || !(sigma0 >= 0.0f && sigma0 <= 1.0f)) return TDP_ERR_ARG;
+  if (n_steps == 0) {
+    sigmas[0] = sigma0;
+    return TDP_OK;
+  }
+  const double s0 = sigma0;
+  for (int32_t i = 0; i <= n_steps; ++i)
+    sigmas[i] = static_cast<float>(s0 * (1.0 - static_cast<double>(i) / n_steps));
+  return TDP_OK;
+}
+
 }  // extern "C"

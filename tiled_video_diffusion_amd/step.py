@@ -133,7 +133,7 @@ class BlockStep:
     transformer block (``tdp_block_forward``); gather and blend as in TdpStep."""
 
     def __init__(self, binputs, normalize_positions: bool = True, world_size: int = 1,
-                 rank: int = 0, device: str = "cuda:0"):
+                 rank: int = 0, device: str = "cuda:0", workspace: bool = True):
         inp = binputs.base
         wl = inp.workload
         bw = binputs.workload
@@ -165,7 +165,8 @@ class BlockStep:
         self.desc = tdp.block_desc(wl.batch, wl.channels, wl.heads, wl.head_dim, bw.n_text,
                                    bw.layers, s.code, s.code, bw.time_dim)
         self.ws_bytes = tdp.tdp_block_workspace(self.desc, p.n_tiles_local, p.n_rows)
-        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.workspace = (torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+                          if workspace else None)
 
     @property
     def y_tiles(self):
@@ -191,3 +192,49 @@ class BlockStep:
         self.gather(stream)
         self.block(stream)
         self.blend(accumulate, stream)
+
+
+class UpscaleLoop:
+    """The TDP upscale loop on the GPU: re-noise the stage-1 latent to the
+    first sigma (``tdp_renoise``), then ``n_steps`` steps of gather -> per-tile
+    transformer -> blend fused with the Euler update (``tdp_upscale_loop``).
+    The state ``x`` is the float32 global latent ``[B][N+M][C]``; ``seam``
+    receives each step's {S2, S0, sqrt(S2/S0)}.  Weights, text and the plan come
+    from a ``BlockStep`` on the same inputs."""
+
+    def __init__(self, uinputs, device: str = "cuda:0", sigmas=None):
+        binp = uinputs.block
+        self.bs = BlockStep(binp, device=device, workspace=False)
+        bs, s, p = self.bs, self.bs.s, self.bs.plan
+        wl, bw, uw = binp.base.workload, binp.workload, uinputs.workload
+        self.wl = wl
+        self.sigmas = (tdp.tdp_linear_sigmas(uw.sigma0, uw.n_steps) if sigmas is None
+                       else np.ascontiguousarray(sigmas, np.float32))
+        self.n_steps = self.sigmas.size - 1
+        dev = s.device
+        self.n_gen = wl.n_gen
+        self.n_dst = p.n_dst_rows
+        self.x_stage1 = _dev(binp.base.x_global, dev, torch.float32)
+        self.noise = _dev(uinputs.noise, dev, torch.float32)
+        self.x = torch.empty_like(self.x_stage1)
+        self.seam = torch.zeros((max(self.n_steps, 1), 3), dtype=torch.float64, device=dev)
+        self.desc = tdp.block_desc(wl.batch, wl.channels, wl.heads, wl.head_dim, bw.n_text,
+                                   bw.layers, tdp.TDP_F32, tdp.TDP_F32, bw.time_dim)
+        self.plan_dev = tdp.plan_dev(p.n_tiles_local, p.max_tile_rows, p.n_rows, self.n_gen,
+                                     self.n_dst, s.tile_row_begin, s.row_src, s.row_weight,
+                                     s.row_pos, s.dst_row_begin, s.dst_rows)
+        self.ws_bytes = tdp.tdp_upscale_workspace(self.desc, self.plan_dev)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+
+    def renoise(self, stream=None):
+        tdp.tdp_renoise(self.x_stage1, self.noise, self.wl.batch, self.n_gen, self.n_dst,
+                        self.wl.channels, float(self.sigmas[0]), self.x, stream)
+
+    def loop(self, stream=None):
+        tdp.tdp_upscale_loop(self.desc, self.plan_dev, self.bs.weights, self.bs.text, self.sigmas,
+                             self.n_steps, self.x, self.seam, self.workspace, self.ws_bytes,
+                             stream)
+
+    def run(self, stream=None):
+        self.renoise(stream)
+        self.loop(stream)

@@ -76,6 +76,13 @@ class BlockWeights(C.Structure):
                 ("wt2", C.c_void_p), ("layers", C.POINTER(BlockLayer))]
 
 
+class PlanDev(C.Structure):
+    _fields_ = [("n_tiles", C.c_int32), ("max_tile_rows", C.c_int32), ("n_rows", C.c_int64),
+                ("n_gen", C.c_int64), ("n_dst_rows", C.c_int64)] + [
+        (n, C.c_void_p) for n in ("tile_row_begin", "row_src", "row_weight", "row_pos",
+                                  "dst_row_begin", "dst_rows")]
+
+
 _P, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
 _SIGS = {
     "tdp_status_string": (C.c_char_p, [_I32]),
@@ -98,6 +105,14 @@ _SIGS = {
     "tdp_block_workspace": (_I32, [C.POINTER(BlockDesc), _I32, _I64, C.POINTER(_SZ)]),
     "tdp_block_forward": (_I32, [C.POINTER(BlockDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P,
                                  C.POINTER(BlockWeights), _P, _P, _SZ, _P]),
+    "tdp_linear_sigmas": (_I32, [C.c_float, _I32, C.POINTER(C.c_float)]),
+    "tdp_renoise": (_I32, [_P, _P, _I32, _I64, _I64, _I32, C.c_float, _P, _P]),
+    "tdp_blend_euler_workspace": (_I32, [_I32, _I64, _I32, C.POINTER(_SZ)]),
+    "tdp_blend_euler": (_I32, [_P, _I32, _I32, _I64, _I32, _P, _P, _P, _I64, _P, _I64, C.c_float,
+                               C.c_float, _P, _P, _SZ, _P]),
+    "tdp_upscale_workspace": (_I32, [C.POINTER(BlockDesc), C.POINTER(PlanDev), C.POINTER(_SZ)]),
+    "tdp_upscale_loop": (_I32, [C.POINTER(BlockDesc), C.POINTER(PlanDev), C.POINTER(BlockWeights),
+                                _P, C.POINTER(C.c_float), _I32, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -365,3 +380,61 @@ def tdp_block_forward(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_ti
         C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows, n_rows, _ptr(x_tiles),
         _ptr(row_pos), _ptr(text), _ptr(tau), C.byref(weights), _ptr(y_tiles), _ptr(workspace),
         workspace_bytes, _stream(stream)), "tdp_block_forward")
+
+
+# ---------------------------------------------------------------------------
+# upscale loop
+# ---------------------------------------------------------------------------
+
+def tdp_linear_sigmas(sigma0, n_steps) -> np.ndarray:
+    """The linear schedule, float32 ``[n_steps + 1]`` (host)."""
+    out = np.zeros(max(int(n_steps), 0) + 1, np.float32)
+    _check(lib().tdp_linear_sigmas(float(sigma0), int(n_steps),
+                                   out.ctypes.data_as(C.POINTER(C.c_float))), "tdp_linear_sigmas")
+    return out
+
+
+def tdp_renoise(x_stage1, noise, batch, n_gen, n_dst_rows, C_, sigma0, x, stream=None) -> None:
+    _check(lib().tdp_renoise(_ptr(x_stage1), _ptr(noise), batch, n_gen, n_dst_rows, C_,
+                             float(sigma0), _ptr(x), _stream(stream)), "tdp_renoise")
+
+
+def tdp_blend_euler_workspace(batch, n_gen, C_) -> int:
+    n = C.c_size_t()
+    _check(lib().tdp_blend_euler_workspace(batch, n_gen, C_, C.byref(n)),
+           "tdp_blend_euler_workspace")
+    return n.value
+
+
+def tdp_blend_euler(y_tiles, dtype, batch, n_rows, C_, dst_row_begin, dst_rows, row_weight,
+                    n_gen, x, n_dst_rows, sigma, sigma_next, seam, workspace, workspace_bytes,
+                    stream=None) -> None:
+    _check(lib().tdp_blend_euler(_ptr(y_tiles), dtype, batch, n_rows, C_, _ptr(dst_row_begin),
+                                 _ptr(dst_rows), _ptr(row_weight), n_gen, _ptr(x), n_dst_rows,
+                                 float(sigma), float(sigma_next), _ptr(seam), _ptr(workspace),
+                                 workspace_bytes, _stream(stream)), "tdp_blend_euler")
+
+
+def plan_dev(n_tiles, max_tile_rows, n_rows, n_gen, n_dst_rows, tile_row_begin, row_src,
+             row_weight, row_pos, dst_row_begin, dst_rows) -> PlanDev:
+    return PlanDev(n_tiles, max_tile_rows, n_rows, n_gen, n_dst_rows, _ptr(tile_row_begin),
+                   _ptr(row_src), _ptr(row_weight), _ptr(row_pos), _ptr(dst_row_begin),
+                   _ptr(dst_rows))
+
+
+def tdp_upscale_workspace(desc: BlockDesc, plan: PlanDev) -> int:
+    n = C.c_size_t()
+    _check(lib().tdp_upscale_workspace(C.byref(desc), C.byref(plan), C.byref(n)),
+           "tdp_upscale_workspace")
+    return n.value
+
+
+def tdp_upscale_loop(desc, plan: PlanDev, weights: BlockWeights, text, sigmas, n_steps, x, seam,
+                     workspace, workspace_bytes, stream=None) -> None:
+    sig = np.ascontiguousarray(sigmas, dtype=np.float32)
+    if sig.size < int(n_steps) + 1:
+        raise ValueError("sigmas needs n_steps + 1 entries")
+    _check(lib().tdp_upscale_loop(C.byref(desc), C.byref(plan), C.byref(weights), _ptr(text),
+                                  sig.ctypes.data_as(C.POINTER(C.c_float)), int(n_steps), _ptr(x),
+                                  _ptr(seam), _ptr(workspace), workspace_bytes, _stream(stream)),
+           "tdp_upscale_loop")
