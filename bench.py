@@ -272,8 +272,7 @@ def loop_bench(name: str, reps: int, warmup: int) -> dict:
     import torch
 
     import tdp_inputs as ti
-    from tiled_video_diffusion_amd import tdp
-    from tiled_video_diffusion_amd.step import UpscaleLoop
+    from tiled_video_diffusion_amd.step import TdpStep, UpscaleLoop
 
     up = ti.make_upscale_inputs(name)
     wl = up.block.base.workload
@@ -291,44 +290,63 @@ def loop_bench(name: str, reps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     ms_loop = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     seam = lp.seam.cpu().numpy()
-    # the fused blend/Euler kernel alone, float32 tile rows of this plan, seam on
-    p = lp.bs.plan
-    B, C, N = wl.batch, wl.channels, wl.n_gen
+    n_steps = lp.n_steps
+    # the fused blend/Euler kernel alone (float32 tile rows) on this plan and on
+    # the 32x96x160 latent's plan, with and without the seam sums
+    B = wl.batch
+    kern = {"workload_plan": _time_blend_euler(lp.bs.s, B, wl.channels, wl.n_gen, lp.n_dst)}
+    lp = None
+    torch.cuda.empty_cache()
+    big = ti.make_inputs("blend_32x96x160")
+    bst = TdpStep(big, identity=True)
+    kern["blend_32x96x160_plan"] = _time_blend_euler(bst, big.workload.batch,
+                                                     big.workload.channels, big.workload.n_gen,
+                                                     bst.plan.n_dst_rows)
+    return {"workload": name, "block": up.workload.block, "sigma0": up.workload.sigma0,
+            "n_steps": n_steps, "ms_per_loop": ms_loop,
+            "ms_per_step": ms_loop / max(n_steps, 1),
+            "latent_tokens_per_s_per_step": B * wl.n_gen / (ms_loop / max(n_steps, 1) * 1e-3),
+            "seam_relative_spread": [float(v) for v in seam[:n_steps, 2]],
+            "seam_note": "synthetic weights: the spread shows the metric, not a quality",
+            "blend_euler": kern}
+
+
+def _time_blend_euler(s, B, C, N, n_dst, n_launch=50) -> dict:
+    """Mean launch time of tdp_blend_euler on TdpStep ``s``'s plan with random
+    float32 tile rows, with and without the seam sums (HIP events on the
+    launch stream)."""
+    import numpy as np
+    import torch
+
+    from tiled_video_diffusion_amd import tdp
+
+    p = s.plan
+    stream = torch.cuda.current_stream()
     g = torch.Generator(device="cuda:0").manual_seed(0)
     y = torch.randn((B, p.n_rows, C), generator=g, device="cuda:0", dtype=torch.float32)
-    x = lp.x.clone()
+    x = torch.randn((B, n_dst, C), generator=g, device="cuda:0", dtype=torch.float32)
     ws_bytes = tdp.tdp_blend_euler_workspace(B, N, C)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
-    seam_d = torch.zeros(3, dtype=torch.float64, device="cuda:0")
-    s = lp.bs.s
-    n_launch = 50
-
-    def launch():
-        tdp.tdp_blend_euler(y, tdp.TDP_F32, B, p.n_rows, C, s.dst_row_begin, s.dst_rows,
-                            s.row_weight, N, x, lp.n_dst, 0.3, 0.225, seam_d, ws, ws_bytes,
-                            stream)
-
-    for _ in range(3):
-        launch()
-    ke = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_launch)]
-    for a, b in ke:
-        a.record(stream)
-        launch()
-        b.record(stream)
-    torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in ke]))
-    nbytes = blend_euler_bytes(p, N, B, C)
-    gbs = nbytes / (k_ms * 1e-3) / 1e9
-    return {"workload": name, "block": up.workload.block, "sigma0": up.workload.sigma0,
-            "n_steps": lp.n_steps, "ms_per_loop": ms_loop,
-            "ms_per_step": ms_loop / max(lp.n_steps, 1),
-            "latent_tokens_per_s_per_step": B * N / (ms_loop / max(lp.n_steps, 1) * 1e-3),
-            "seam_relative_spread": [float(v) for v in seam[:lp.n_steps, 2]],
-            "seam_note": "synthetic weights: the spread shows the metric, not a quality",
-            "blend_euler": {"ms_per_launch": k_ms, "bytes_per_launch": nbytes,
-                            "achieved": gbs, "unit": "GB/s", "peak": PEAK_HBM_GBS,
-                            "frac": gbs / PEAK_HBM_GBS, "with_seam": True}}
+    seam = torch.zeros(3, dtype=torch.float64, device="cuda:0")
+    out = {"bytes_per_launch": blend_euler_bytes(p, N, B, C), "unit": "GB/s",
+           "peak": PEAK_HBM_GBS}
+    for key, sm in (("with_seam", seam), ("no_seam", None)):
+        def launch():
+            tdp.tdp_blend_euler(y, tdp.TDP_F32, B, p.n_rows, C, s.dst_row_begin, s.dst_rows,
+                                s.row_weight, N, x, n_dst, 0.3, 0.2999, sm, ws, ws_bytes, stream)
+        for _ in range(3):
+            launch()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(n_launch)]
+        for a, b in ev:
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        gbs = out["bytes_per_launch"] / (ms * 1e-3) / 1e9
+        out[key] = {"ms_per_launch": ms, "achieved": gbs, "frac": gbs / PEAK_HBM_GBS}
+    return out
 
 
 def run(args) -> dict:

@@ -45,18 +45,32 @@ __global__ __launch_bounds__(kThreads) void renoise_kernel(const f32x4 *x1, cons
   x[i] = v;
 }
 
-template <typename T>
-__device__ __forceinline__ f32x4 load4(const T *p);
-template <>
-__device__ __forceinline__ f32x4 load4<float>(const float *p) {
-  return *reinterpret_cast<const f32x4 *>(p);
-}
-template <>
-__device__ __forceinline__ f32x4 load4<bf16>(const bf16 *p) {
-  const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
-  return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
-               static_cast<float>(v[3])};
-}
+// Tile rows and the latent are streamed with non-temporal hints when the tile
+// rows are larger than the 256 MB last-level cache (NT = true); smaller ones
+// were just written by the transformer and are read from that cache.
+constexpr int64_t kStreamBytes = int64_t{256} << 20;
+
+template <typename T, bool NT>
+struct Load4;
+template <bool NT>
+struct Load4<float, NT> {
+  __device__ static f32x4 at(const float *p) {
+    const f32x4 *q = reinterpret_cast<const f32x4 *>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+  }
+};
+template <bool NT>
+struct Load4<bf16, NT> {
+  __device__ static f32x4 at(const bf16 *p) {
+    const bf16x4 *q = reinterpret_cast<const bf16x4 *>(p);
+    bf16x4 v;
+    if constexpr (NT) v = __builtin_nontemporal_load(q);
+    else v = *q;
+    return f32x4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+                 static_cast<float>(v[3])};
+  }
+};
 
 __device__ __forceinline__ float sq_dist(f32x4 a, f32x4 b) {
   float t = 0.f;
@@ -78,7 +92,7 @@ __device__ __forceinline__ float sq_dist(f32x4 a, f32x4 b) {
 // Each thread owns 4 channels of one token (C / 4 threads per token); the
 // first four rows of a token are loaded together, more (three-dimensional
 // overlaps) in a loop.  Row ids outside [0, n_rows) are skipped.
-template <typename T>
+template <typename T, bool NT>
 __global__ __launch_bounds__(kThreads) void blend_euler_kernel(
     const T *__restrict__ y_tiles, int64_t n_rows, int32_t C,
     const int64_t *__restrict__ dst_row_begin, const int32_t *__restrict__ dst_rows,
@@ -106,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void blend_euler_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       w[u] = r[u] >= 0 ? row_weight[r[u]] : 0.f;
-      y[u] = r[u] >= 0 ? load4<T>(yb + static_cast<int64_t>(r[u]) * C)
+      y[u] = r[u] >= 0 ? Load4<T, NT>::at(yb + static_cast<int64_t>(r[u]) * C)
                        : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -123,16 +137,19 @@ __global__ __launch_bounds__(kThreads) void blend_euler_kernel(
       const int32_t rr = dst_rows[k];
       if (rr < 0 || rr >= n_rows) continue;
       const float ww = row_weight[rr];
-      const f32x4 yy = load4<T>(yb + static_cast<int64_t>(rr) * C);
+      const f32x4 yy = Load4<T, NT>::at(yb + static_cast<int64_t>(rr) * C);
 #pragma unroll
       for (int c = 0; c < 4; ++c) v[c] = fmaf(ww, yy[c], v[c]);
       ++cnt;
     }
     f32x4 *xp = reinterpret_cast<f32x4 *>(x + (b * n_dst + n) * C + 4 * q);
-    f32x4 xv = *xp;
+    f32x4 xv;
+    if constexpr (NT) xv = __builtin_nontemporal_load(xp);
+    else xv = *xp;
 #pragma unroll
     for (int c = 0; c < 4; ++c) xv[c] = fmaf(dsigma, v[c], xv[c]);
-    *xp = xv;
+    if constexpr (NT) __builtin_nontemporal_store(xv, xp);
+    else *xp = xv;
     if (partial && cnt >= 2) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) s0 = fmaf(v[c], v[c], s0);
@@ -142,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void blend_euler_kernel(
       for (int64_t k = kb + 4; k < ke; ++k) {
         const int32_t rr = dst_rows[k];
         if (rr < 0 || rr >= n_rows) continue;
-        s2 = fmaf(row_weight[rr], sq_dist(load4<T>(yb + static_cast<int64_t>(rr) * C), v), s2);
+        s2 = fmaf(row_weight[rr], sq_dist(Load4<T, NT>::at(yb + static_cast<int64_t>(rr) * C), v), s2);
       }
     }
   }
@@ -171,15 +188,14 @@ __global__ __launch_bounds__(kThreads) void blend_euler_kernel(
   }
 }
 
-// out = {S2, S0, sqrt(S2 / S0) or 0}: the n partial pairs summed in double in
-// a fixed order (one workgroup), so the result does not depend on timing.
-__global__ __launch_bounds__(kThreads) void seam_reduce_kernel(const float2 *__restrict__ partial,
-                                                                int64_t n, double *__restrict__ out) {
-  double a = 0.0, c = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
-    a += static_cast<double>(partial[i].x);
-    c += static_cast<double>(partial[i].y);
-  }
+// The seam sums in two fixed-order passes (the result does not depend on
+// timing): pass 1, workgroup g adds the float2 partials [g * kSeamChunk,
+// (g + 1) * kSeamChunk) in double; pass 2, one workgroup adds pass 1's sums and
+// writes out = {S2, S0, sqrt(S2 / S0) or 0}.
+constexpr int kSeamPerThread = 16;
+constexpr int64_t kSeamChunk = static_cast<int64_t>(kThreads) * kSeamPerThread;
+
+__device__ __forceinline__ void block_sum2(double &a, double &c) {
   __shared__ double red[2][kThreads];
   red[0][threadIdx.x] = a;
   red[1][threadIdx.x] = c;
@@ -191,10 +207,42 @@ __global__ __launch_bounds__(kThreads) void seam_reduce_kernel(const float2 *__r
     }
     __syncthreads();
   }
+  a = red[0][0];
+  c = red[1][0];
+}
+
+__global__ __launch_bounds__(kThreads) void seam_pass1_kernel(const float2 *__restrict__ partial,
+                                                               int64_t n,
+                                                               double2 *__restrict__ sums) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kSeamChunk + threadIdx.x;
+  float2 v[kSeamPerThread];
+#pragma unroll
+  for (int j = 0; j < kSeamPerThread; ++j) {
+    const int64_t i = base + static_cast<int64_t>(j) * kThreads;
+    v[j] = i < n ? partial[i] : make_float2(0.f, 0.f);
+  }
+  double a = 0.0, c = 0.0;
+#pragma unroll
+  for (int j = 0; j < kSeamPerThread; ++j) {
+    a += static_cast<double>(v[j].x);
+    c += static_cast<double>(v[j].y);
+  }
+  block_sum2(a, c);
+  if (threadIdx.x == 0) sums[blockIdx.x] = make_double2(a, c);
+}
+
+__global__ __launch_bounds__(kThreads) void seam_pass2_kernel(const double2 *__restrict__ sums,
+                                                               int64_t n, double *__restrict__ out) {
+  double a = 0.0, c = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
+    a += sums[i].x;
+    c += sums[i].y;
+  }
+  block_sum2(a, c);
   if (threadIdx.x == 0) {
-    out[0] = red[0][0];
-    out[1] = red[1][0];
-    out[2] = red[1][0] > 0.0 ? sqrt(red[0][0] / red[1][0]) : 0.0;
+    out[0] = a;
+    out[1] = c;
+    out[2] = c > 0.0 ? sqrt(a / c) : 0.0;
   }
 }
 
@@ -212,9 +260,17 @@ int64_t blend_euler_blocks(int32_t C, int64_t n_gen) {
 
 size_t a256(size_t v) { return (v + 255) & ~static_cast<size_t>(255); }
 
+// Seam workspace: the workgroup partials, then pass 1's sums.
+int64_t seam_partials(int32_t batch, int64_t n_gen, int32_t C) {
+  return static_cast<int64_t>(batch) * blend_euler_blocks(C, n_gen);
+}
+int64_t seam_pass1_blocks(int64_t n_partials) {
+  return (n_partials + kSeamChunk - 1) / kSeamChunk;
+}
 size_t partial_bytes(int32_t batch, int64_t n_gen, int32_t C) {
-  return a256(static_cast<size_t>(batch) * static_cast<size_t>(blend_euler_blocks(C, n_gen)) *
-              sizeof(float2));
+  const int64_t n = seam_partials(batch, n_gen, C);
+  return a256(static_cast<size_t>(n) * sizeof(float2)) +
+         a256(static_cast<size_t>(seam_pass1_blocks(n)) * sizeof(double2));
 }
 
 tdp_status check_blend_euler(int32_t dtype, int32_t batch, int64_t n_rows, int32_t C,
@@ -233,25 +289,40 @@ tdp_status check_blend_euler(int32_t dtype, int32_t batch, int64_t n_rows, int32
 tdp_status launch_blend_euler(const void *y_tiles, int32_t dtype, int32_t batch, int64_t n_rows,
                               int32_t C, const int64_t *dst_row_begin, const int32_t *dst_rows,
                               const float *row_weight, int64_t n_gen, float *x, int64_t n_dst,
-                              float dsigma, double *seam, float2 *partial, hipStream_t stream) {
+                              float dsigma, double *seam, void *seam_ws, hipStream_t stream) {
   const int64_t nblk = blend_euler_blocks(C, n_gen);
-  if (!seam) partial = nullptr;
+  const int64_t n_part = seam_partials(batch, n_gen, C);
+  float2 *partial = seam ? static_cast<float2 *>(seam_ws) : nullptr;
+  double2 *sums = seam ? reinterpret_cast<double2 *>(
+                             static_cast<char *>(seam_ws) +
+                             a256(static_cast<size_t>(n_part) * sizeof(float2)))
+                       : nullptr;
   if (nblk > 0) {
     const dim3 grid(static_cast<uint32_t>(nblk), batch);
-    if (dtype == TDP_F32)
-      hipLaunchKernelGGL(blend_euler_kernel<float>, grid, dim3(kThreads), 0, stream,
-                         static_cast<const float *>(y_tiles), n_rows, C, dst_row_begin, dst_rows,
-                         row_weight, n_gen, n_dst, x, dsigma, partial);
-    else
-      hipLaunchKernelGGL(blend_euler_kernel<bf16>, grid, dim3(kThreads), 0, stream,
-                         static_cast<const bf16 *>(y_tiles), n_rows, C, dst_row_begin, dst_rows,
-                         row_weight, n_gen, n_dst, x, dsigma, partial);
+    const bool nt = static_cast<int64_t>(batch) * n_rows * C * esize_of(dtype) > kStreamBytes;
+    if (dtype == TDP_F32) {
+      auto k = nt ? blend_euler_kernel<float, true> : blend_euler_kernel<float, false>;
+      hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, stream, static_cast<const float *>(y_tiles),
+                         n_rows, C, dst_row_begin, dst_rows, row_weight, n_gen, n_dst, x, dsigma,
+                         partial);
+    } else {
+      auto k = nt ? blend_euler_kernel<bf16, true> : blend_euler_kernel<bf16, false>;
+      hipLaunchKernelGGL(k, grid, dim3(kThreads), 0, stream, static_cast<const bf16 *>(y_tiles),
+                         n_rows, C, dst_row_begin, dst_rows, row_weight, n_gen, n_dst, x, dsigma,
+                         partial);
+    }
     const tdp_status s = launch_status();
     if (s != TDP_OK) return s;
   }
   if (seam) {
-    hipLaunchKernelGGL(seam_reduce_kernel, dim3(1), dim3(kThreads), 0, stream, partial,
-                       nblk * batch, seam);
+    const int64_t g = seam_pass1_blocks(n_part);
+    if (g > 0) {
+      hipLaunchKernelGGL(seam_pass1_kernel, dim3(static_cast<uint32_t>(g)), dim3(kThreads), 0,
+                         stream, partial, n_part, sums);
+      const tdp_status s = launch_status();
+      if (s != TDP_OK) return s;
+    }
+    hipLaunchKernelGGL(seam_pass2_kernel, dim3(1), dim3(kThreads), 0, stream, sums, g, seam);
     return launch_status();
   }
   return TDP_OK;
@@ -339,8 +410,8 @@ extern "C" tdp_status tdp_blend_euler(const void *y_tiles, int32_t dtype, int32_
   if ((n_gen > 0 && !aligned16(x)) || (n_rows > 0 && n_gen > 0 && !aligned16(y_tiles)))
     return TDP_ERR_ALIGN;
   return launch_blend_euler(y_tiles, dtype, batch, n_rows, C, dst_row_begin, dst_rows,
-                            row_weight, n_gen, x, n_dst_rows, sigma_next - sigma, seam,
-                            static_cast<float2 *>(workspace), as_stream(hip_stream));
+                            row_weight, n_gen, x, n_dst_rows, sigma_next - sigma, seam, workspace,
+                            as_stream(hip_stream));
 }
 
 extern "C" tdp_status tdp_upscale_workspace(const tdp_block_desc *desc,
@@ -376,7 +447,7 @@ extern "C" tdp_status tdp_upscale_loop(const tdp_block_desc *desc, const tdp_pla
   float *xt = reinterpret_cast<float *>(ws + L.off_xt);
   float *yt = reinterpret_cast<float *>(ws + L.off_yt);
   float *tau = reinterpret_cast<float *>(ws + L.off_tau);
-  float2 *partial = reinterpret_cast<float2 *>(ws + L.off_partial);
+  void *seam_ws = ws + L.off_partial;
   const int32_t B = desc->batch, Cc = desc->C;
   for (int32_t i = 0; i < n_steps; ++i) {
     // transformer timestep tau = 1000 sigma_i for every batch entry
@@ -393,7 +464,7 @@ extern "C" tdp_status tdp_upscale_loop(const tdp_block_desc *desc, const tdp_pla
     if ((s = launch_blend_euler(yt, TDP_F32, B, plan->n_rows, Cc, plan->dst_row_begin,
                                 plan->dst_rows, plan->row_weight, plan->n_gen, x,
                                 plan->n_dst_rows, sigmas[i + 1] - sigmas[i],
-                                seam ? seam + 3 * static_cast<int64_t>(i) : nullptr, partial,
+                                seam ? seam + 3 * static_cast<int64_t>(i) : nullptr, seam_ws,
                                 stream)) != TDP_OK)
       return s;
   }
