@@ -9,9 +9,12 @@
 // transformer; the layout above (one shared timestep modulation, text
 // cross-attention, tanh-GELU FFN of width 4D) is the reading this library
 // uses.  Every matrix product runs on gemm() (tdp_gemm.hip) with its
-// epilogue fused (GELU, SiLU, gated residual add); self- and cross-attention
-// run on the attention core; RMSNorm with the modulation is one row kernel.
-// The residual stream x is float32; GEMM operands are bf16.
+// epilogue fused (GELU, SiLU); self- and cross-attention run on the attention
+// core; RMSNorm with the modulation is one row kernel, which also performs
+// the residual add x += gate * branch of the branch that ran before it (the
+// branch's GEMM stores its output in bf16), so no GEMM reads and rewrites the
+// float32 residual stream.  The residual stream x is float32; GEMM operands
+// are bf16.
 #include <cmath>
 
 #include "tdp_internal.h"
@@ -22,31 +25,59 @@ namespace {
 constexpr int kRowsPerWg = 4;   // rows (one per wave) per RMSNorm workgroup
 constexpr float kRmsEps = 1e-6f;
 
-// h[m][:] = bf16(rms(x[m][:]) * (1 + scale) + shift), one wave per row; shift
-// and scale = e[b][row r of 6] + table[r] for the row's batch entry b (both
-// absent: plain RMSNorm).  VEC: D a multiple of 256, each lane moves 16-byte
-// pieces (4 floats) of the row.
+// One wave per row m (batch entry b = m / rows_per_batch):
+//   with y: x[m][:] += g * y[m][:] first (the residual add of the branch that
+//     produced y; g = ge[b][:] + gt[:], either term may be absent, g = 1 when
+//     both are), written back to x;
+//   h[m][:] = bf16(rms(x[m][:]) * (1 + scale) + shift), shift and scale =
+//     e[b][row r of 6] + table[r] for r = shift_row, shift_row + 1 (both
+//     absent: plain RMSNorm).
+// VEC: D a multiple of 256, each lane moves 16-byte pieces (4 floats) of the
+// row.  y and h may be the same buffer: a row's y is read in full before its
+// h is written, by the same wave.
 template <bool VEC>
 __global__ __launch_bounds__(64 * kRowsPerWg) void rms_mod_kernel(
-    const float *__restrict__ x, int64_t M, int32_t D, int64_t rows_per_batch,
+    float *__restrict__ x, int64_t M, int32_t D, int64_t rows_per_batch,
     const float *__restrict__ e, const float *__restrict__ table, int32_t shift_row,
-    bf16 *__restrict__ h) {
+    const bf16 *y, const float *__restrict__ ge, const float *__restrict__ gt, bf16 *h) {
   const int lane = threadIdx.x & 63;
   const int64_t m = static_cast<int64_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 6);
   if (m >= M) return;
-  const float *xr = x + m * D;
+  float *xr = x + m * D;
   const int64_t b = m / rows_per_batch;
   const float *es = e ? e + (b * 6 + shift_row) * D : nullptr;
   const float *ts = table ? table + static_cast<int64_t>(shift_row) * D : nullptr;
+  const float *gs = ge ? ge + b * 6 * D : nullptr;
+  const bf16 *yr = y ? y + m * D : nullptr;
   bf16 *hr = h + m * D;
   float ss = 0.f;
   if constexpr (VEC) {
     for (int j = 4 * lane; j < D; j += 256) {
-      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + j);
+      f32x4 v = *reinterpret_cast<const f32x4 *>(xr + j);
+      if (yr) {
+        const bf16x4 yv = *reinterpret_cast<const bf16x4 *>(yr + j);
+        f32x4 g = {1.f, 1.f, 1.f, 1.f};
+        if (gs || gt) {
+          g = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (gs) g += *reinterpret_cast<const f32x4 *>(gs + j);
+          if (gt) g += *reinterpret_cast<const f32x4 *>(gt + j);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = fmaf(g[q], static_cast<float>(yv[q]), v[q]);
+        *reinterpret_cast<f32x4 *>(xr + j) = v;
+      }
       ss = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], ss))));
     }
   } else {
-    for (int j = lane; j < D; j += 64) ss = fmaf(xr[j], xr[j], ss);
+    for (int j = lane; j < D; j += 64) {
+      float v = xr[j];
+      if (yr) {
+        const float g = (gs || gt) ? (gs ? gs[j] : 0.f) + (gt ? gt[j] : 0.f) : 1.f;
+        v = fmaf(g, static_cast<float>(yr[j]), v);
+        xr[j] = v;
+      }
+      ss = fmaf(v, v, ss);
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
@@ -205,14 +236,21 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
   bf16 *e1 = at<bf16>(workspace, L.off_e1);
   float *E = at<float>(workspace, L.off_e);
   bf16 *ckv = at<bf16>(workspace, L.off_ckv);
-  auto rms = [&](const float *table, int shift_row) {
+  // h = RMSNorm of x with the modulation rows (shift_row, shift_row + 1) of
+  // `table` (and E), after x += gate * y when y is given (y = the branch
+  // output a GEMM just stored in h; gate rows of E and of the table by
+  // pointer, both absent = 1).
+  auto rms = [&](const float *table, int shift_row, const bf16 *y = nullptr,
+                 const float *gate_e = nullptr, const float *gate_t = nullptr) {
     const dim3 grid(static_cast<uint32_t>((M + kRowsPerWg - 1) / kRowsPerWg));
     if (D % 256 == 0)
       hipLaunchKernelGGL(rms_mod_kernel<true>, grid, dim3(64 * kRowsPerWg), 0, stream, x, M,
-                         static_cast<int32_t>(D), n_rows, table ? E : nullptr, table, shift_row, h);
+                         static_cast<int32_t>(D), n_rows, table ? E : nullptr, table, shift_row,
+                         y, gate_e, gate_t, h);
     else
       hipLaunchKernelGGL(rms_mod_kernel<false>, grid, dim3(64 * kRowsPerWg), 0, stream, x, M,
-                         static_cast<int32_t>(D), n_rows, table ? E : nullptr, table, shift_row, h);
+                         static_cast<int32_t>(D), n_rows, table ? E : nullptr, table, shift_row,
+                         y, gate_e, gate_t, h);
     return launch_status();
   };
   auto mm = [&](int epi, const bf16 *a, int64_t lda, int64_t m, const void *bt, int32_t n,
@@ -234,8 +272,7 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
     g.rows_per_batch = n_rows;
     return gemm(epi, g, stream);
   };
-  auto proj_o = [&](const tdp_attn_desc *ad, void *aws, const void *wo, int epi,
-                    const float *g0, const float *g1) {
+  auto proj_o = [&](const tdp_attn_desc *ad, void *aws, const void *wo) {
     GemmDesc g;
     g.a = attn_output(ad, n_tiles, n_rows, aws);
     g.a_seg_rows = n_rows;
@@ -246,13 +283,9 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
     g.M = M;
     g.N = static_cast<int32_t>(D);
     g.K = static_cast<int32_t>(D);
-    g.c = x;
+    g.c = h;
     g.ldc = D;
-    g.g0 = g0;
-    g.g0_stride = 6 * D;
-    g.g1 = g1;
-    g.rows_per_batch = n_rows;
-    return gemm(epi, g, stream);
+    return gemm(kEpiBf16, g, stream);
   };
 #define TDP_TRY(expr)               \
   do {                              \
@@ -285,10 +318,14 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
              e1, D));
   TDP_TRY(mm(kEpiF32, e1, D, B, w->wt2, static_cast<int32_t>(6 * D), static_cast<int32_t>(D), E,
              6 * D));
+  // Each branch's GEMM stores its output in h (bf16); the residual add
+  // x += gate * branch happens in the RMSNorm kernel that reads x next.
+  const bf16 *pend_y = nullptr;                 // branch output waiting in h
+  const float *pend_ge = nullptr, *pend_gt = nullptr;
   for (int l = 0; l < desc->layers; ++l) {
     const tdp_block_layer &y = w->layers[l];
     // self-attention, gated
-    TDP_TRY(rms(y.table, 0));
+    TDP_TRY(rms(y.table, 0, pend_y, pend_ge, pend_gt));
     TDP_TRY(mm(kEpiBf16, h, D, M, y.wqkv, static_cast<int32_t>(3 * D), static_cast<int32_t>(D),
                big, 3 * D));
     TDP_TRY(attn_rows_to_heads(&L.self, n_tiles, tile_row_begin, max_tile_rows, n_rows, big,
@@ -296,9 +333,9 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
                                row_pos, false, nullptr, 0, ws_self, L.self_bytes, stream));
     TDP_TRY(attn_core_run(&L.self, n_tiles, tile_row_begin, max_tile_rows, n_rows, ws_self,
                           L.self_bytes, true, stream));
-    TDP_TRY(proj_o(&L.self, ws_self, y.wo, kEpiResidGate, E + 2 * D, y.table + 2 * D));
-    // cross-attention over the text tokens
-    TDP_TRY(rms(nullptr, 0));
+    TDP_TRY(proj_o(&L.self, ws_self, y.wo));
+    // cross-attention over the text tokens (after x += gate_a * attention)
+    TDP_TRY(rms(nullptr, 0, h, E + 2 * D, y.table + 2 * D));
     TDP_TRY(mm(kEpiBf16, h, D, M, y.cq, static_cast<int32_t>(D), static_cast<int32_t>(D), big, D));
     TDP_TRY(attn_rows_to_heads(&L.cross, n_tiles, tile_row_begin, max_tile_rows, n_rows, big, D, 0,
                                -1, -1, nullptr, false, nullptr, 0, ws_cross, L.cross_bytes,
@@ -310,16 +347,19 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
                                ws_cross, L.cross_bytes, stream));
     TDP_TRY(attn_core_run(&L.cross, n_tiles, tile_row_begin, max_tile_rows, n_rows, ws_cross,
                           L.cross_bytes, false, stream));
-    TDP_TRY(proj_o(&L.cross, ws_cross, y.co, kEpiResid, nullptr, nullptr));
-    // FFN, gated
-    TDP_TRY(rms(y.table, 3));
+    TDP_TRY(proj_o(&L.cross, ws_cross, y.co));
+    // FFN, gated (after x += cross-attention, ungated)
+    TDP_TRY(rms(y.table, 3, h, nullptr, nullptr));
     TDP_TRY(mm(kEpiGeluBf16, h, D, M, y.w1, static_cast<int32_t>(4 * D), static_cast<int32_t>(D),
                big, 4 * D));
-    TDP_TRY(mm(kEpiResidGate, big, 4 * D, M, y.w2, static_cast<int32_t>(D),
-               static_cast<int32_t>(4 * D), x, D, E + 5 * D, y.table + 5 * D));
+    TDP_TRY(mm(kEpiBf16, big, 4 * D, M, y.w2, static_cast<int32_t>(D),
+               static_cast<int32_t>(4 * D), h, D));
+    pend_y = h;
+    pend_ge = E + 5 * D;
+    pend_gt = y.table + 5 * D;
   }
-  // y = rms(x_L) W_out
-  TDP_TRY(rms(nullptr, 0));
+  // y = rms(x_L) W_out (after x += gate_f * FFN of the last block)
+  TDP_TRY(rms(nullptr, 0, pend_y, pend_ge, pend_gt));
   return mm(desc->y_dtype == TDP_F32 ? kEpiF32 : kEpiBf16, h, D, M, w->w_out, 128,
             static_cast<int32_t>(D), y_tiles, 128);
 #undef TDP_TRY

@@ -2,7 +2,10 @@
 //
 // Used by the attention's output projection (A = the head-major attention
 // output) and by the per-tile transformer block (projections, FFN, timestep
-// MLP).  One workgroup = 256 rows (8 waves x 32) and 128 columns; each wave
+// MLP).  Three forms: the narrow one below (N a multiple of 128, small M),
+// the wide one, and the large one (the big products), further down.
+//
+// Narrow form: one workgroup = 256 rows (8 waves x 32) and 128 columns; each wave
 // owns 32 rows x 128 columns (four 32x32 MFMA tiles).  Each 64-wide k chunk
 // of A (32 KB) and of B^T (16 KB) goes global -> LDS by direct loads, one
 // 128-byte row segment per 8 lanes, into a 3-stage ring, so a chunk has two
@@ -32,13 +35,16 @@ __device__ __forceinline__ int g_slot(int r, int piece) { return piece ^ ((r >> 
 
 constexpr float kLog2e = 1.4426950408889634f;
 // tanh-form GELU via 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)), z = sqrt(2/pi) (u + 0.044715 u^3).
+// The quotient uses the hardware reciprocal (about 1 ulp, far below the bf16
+// rounding of the result); for very negative u, exp2 -> inf and the
+// reciprocal -> 0.
 __device__ __forceinline__ float gelu_tanh(float u) {
   const float z = 0.7978845608028654f * (u + 0.044715f * u * u * u);
-  return u / (1.0f + __builtin_amdgcn_exp2f(-2.0f * kLog2e * z));
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.0f * kLog2e * z));
 }
 // u sigmoid(u)
 __device__ __forceinline__ float silu(float u) {
-  return u / (1.0f + __builtin_amdgcn_exp2f(-kLog2e * u));
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * u));
 }
 
 struct GemmArgs {
@@ -373,6 +379,355 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_wide_kernel(GemmArgs g) {
   }
 }
 
+// Large form for the big products: one workgroup = 256 x 256 like the wide
+// form, but 4 waves as 2 x 2, each wave 128 x 128 (4 x 4 MFMA tiles, 256
+// accumulator registers, one wave per SIMD).  Every A and B^T fragment read
+// from LDS feeds 4 MFMAs (0.5 reads per MFMA, against 0.75 in the wide form).
+// The k loop runs over 32-wide chunks (16 KB of A and 16 KB of B^T) in a
+// ring of kBStages LDS stages (K a multiple of 32 kBStages), the direct loads
+// running kBStages - 1 chunks ahead: with one wave per SIMD nothing else hides a load that misses the
+// L2, and one chunk of lead (the two-stage forms) left the MFMAs waiting.
+// LDS rows are 64 bytes, 16-byte piece p of row r at slot p ^ ((r / 4) % 4),
+// so the 16 lanes of a fragment read phase (16 consecutive rows, one piece)
+// cover all 64 banks.  The fragments of the next 16-wide k step are read
+// while the MFMAs of the current one run.
+#ifndef TDP_GEMM_STAGES
+#define TDP_GEMM_STAGES 4
+#endif
+// 1: the chunk body interleaves MFMAs and memory instructions one by one;
+// 0: grouped (reads, then MFMAs, fenced).
+#ifndef TDP_GEMM_INTERLEAVE
+#define TDP_GEMM_INTERLEAVE 1
+#endif
+constexpr int kBStages = TDP_GEMM_STAGES;
+constexpr int kBK = 32;                      // k per chunk
+constexpr int kBWaves = 4;
+constexpr int kBThreads = 64 * kBWaves;
+constexpr int kBLoadsA = kWRows * kBK * 2 / 1024 / kBWaves;   // 4 (1 KB each, per wave)
+constexpr int kBLoadsB = kWCols * kBK * 2 / 1024 / kBWaves;   // 4
+constexpr int kBLoads = kBLoadsA + kBLoadsB;
+static_assert(kBStages >= 2 && kBStages <= 4, "2..4 stages of 32 KB");
+
+// Workgroup barrier ordering LDS only (the direct loads are waited for with
+// an explicit vmcnt before it; a plain __syncthreads would also wait for every
+// load still in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Wait until at most N chunks of direct loads (8 instructions each) are in
+// flight.
+template <int N>
+__device__ __forceinline__ void wait_chunks() {
+  static_assert(N >= 0 && N <= 2, "vmcnt of 0, 8 or 16");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+}
+
+__device__ __forceinline__ int b_slot(int r, int piece) { return piece ^ ((r >> 2) & 3); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of `bytes` bytes at `base` (wave-uniform): raw, stride 0,
+// the gfx9 data-format word.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from descriptor offset voff + soff into LDS: the wave's
+// 64 lanes fill the 1 KB at `lds` (wave-uniform) in lane order.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                           const bf16 *lds) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16 *)lds));
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+               : "memory");
+}
+
+template <int EPI, int HD>
+__global__ __launch_bounds__(kBThreads, 1) void gemm_big_kernel(GemmArgs g) {
+  static_assert(HD % kBK == 0, "whole k chunks per head");
+  __shared__ __attribute__((aligned(16))) bf16 sA[kBStages][kWRows * kBK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[kBStages][kWCols * kBK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t M = g.M;
+  const int64_t nm = cdiv(M, kWRows), nn = g.N / kWCols;
+  int64_t tm, tn;
+  {
+    const int64_t G = gridDim.x;   // a multiple of 8, >= nm * nn
+    const int64_t bid = blockIdx.x;
+    const int64_t lid = (bid % 8) * (G / 8) + bid / 8;
+    if (lid >= nm * nn) return;
+    constexpr int64_t kGroup = TDP_GEMM_GROUP_M > 0 ? TDP_GEMM_GROUP_M : 1;
+    const int64_t per_group = kGroup * nn;
+    const int64_t grp = lid / per_group;
+    const int64_t first_m = grp * kGroup;
+    const int64_t gm = min(kGroup, nm - first_m);
+    const int64_t in = lid - grp * per_group;
+    tm = first_m + in % gm;
+    tn = in / gm;
+  }
+  // The tile indices come out of 64-bit divisions on the vector unit; make
+  // them wave-uniform so the buffer descriptors below sit in scalar registers.
+  const int64_t row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tm))) *
+                       kWRows;
+  const int64_t col0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tn))) *
+                       kWCols;
+  // Direct loads: buffer_load ... lds written as inline assembly, through
+  // buffer descriptors.  The compiler then tracks none of them, so it never
+  // waits for a stage's loads before reading another stage (its alias
+  // tracking of LDS direct loads loses track across a ring of stages and
+  // waits for all of them); the waits are the explicit vmcnt counts before
+  // each barrier.  Each descriptor covers exactly the bytes this workgroup may
+  // read (a load outside it returns zeros instead of faulting); per-lane
+  // offsets are 32-bit within it and a chunk's k offset is the scalar offset.
+  // Rows past M re-read row M - 1 (their results are not stored).
+  const int64_t rows_here = min(static_cast<int64_t>(kWRows), M - row0);
+  const char *abase;
+  uint32_t a_extent;
+  if constexpr (HD > 0) {
+    abase = reinterpret_cast<const char *>(g.a);
+    a_extent = static_cast<uint32_t>(M * g.K * 2);   // host: < 2^32 bytes
+  } else {
+    abase = reinterpret_cast<const char *>(g.a + row0 * g.lda);
+    a_extent = static_cast<uint32_t>(((rows_here - 1) * g.lda + g.K) * 2);
+  }
+  const char *bbase = reinterpret_cast<const char *>(g.bt + col0 * g.ldb);
+  const uint32_t b_extent = static_cast<uint32_t>(((kWCols - 1) * g.ldb + g.K) * 2);
+  const i32x4 arsrc = buffer_rsrc(abase, a_extent);
+  const i32x4 brsrc = buffer_rsrc(bbase, b_extent);
+  uint32_t aoff[kBLoadsA], boff[kBLoadsB];
+#pragma unroll
+  for (int i = 0; i < kBLoadsA; ++i) {
+    const int pos = (i * kBWaves + uwave) * 64 + lane;   // 16-byte position in the stage
+    const int r = pos / 4, slot = pos % 4;
+    const int64_t gr = min(row0 + r, M - 1);
+    int64_t el;
+    if constexpr (HD > 0) {
+      const int64_t L = g.a_seg_rows;
+      const int64_t seg = gr / L;
+      el = (seg * g.a_heads * L + (gr - seg * L)) * HD;
+    } else {
+      el = (gr - row0) * g.lda;
+    }
+    aoff[i] = static_cast<uint32_t>(el * 2 + 16 * b_slot(r, slot));
+  }
+#pragma unroll
+  for (int i = 0; i < kBLoadsB; ++i) {
+    const int pos = (i * kBWaves + uwave) * 64 + lane;
+    const int r = pos / 4, slot = pos % 4;
+    boff[i] = static_cast<uint32_t>(r * g.ldb * 2 + 16 * b_slot(r, slot));
+  }
+  // Scalar offsets of chunk c: {A, B^T}.
+  auto chunk_soff = [&](int c) __attribute__((always_inline)) {
+    const uint32_t kb = static_cast<uint32_t>(c) * kBK * 2;
+    uint32_t ab = kb;
+    if constexpr (HD > 0) {
+      constexpr int kPerHead = HD / kBK;
+      const int h = c / kPerHead;
+      ab = static_cast<uint32_t>((static_cast<int64_t>(h) * g.a_seg_rows * HD +
+                                  (c - h * kPerHead) * kBK) * 2);
+    }
+    return uint2{ab, kb};
+  };
+  // Load i (0..7: four of A, then four of B^T) of a chunk.
+  auto load_one = [&](int i, uint2 so, bf16 *sa, bf16 *sb) __attribute__((always_inline)) {
+    if (i < kBLoadsA) load_lds16(arsrc, aoff[i], so.x, sa + (i * kBWaves + uwave) * 512);
+    else load_lds16(brsrc, boff[i - kBLoadsA], so.y, sb + ((i - kBLoadsA) * kBWaves + uwave) * 512);
+  };
+  auto load_chunk = [&](int c, bf16 *sa, bf16 *sb) __attribute__((always_inline)) {
+    const uint2 so = chunk_soff(c);
+#pragma unroll
+    for (int i = 0; i < kBLoads; ++i) load_one(i, so, sa, sb);
+  };
+  // fragment offsets (elements): A row 128 wm + 32 t + l32, B^T row
+  // 128 wn + 32 t + l32; piece 2 ks + hh
+  int32_t afo[4][2], bfo[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int ar = 128 * wm + 32 * t + l32;
+      afo[t][ks] = ar * kBK + 8 * b_slot(ar, 2 * ks + hh);
+      const int br = 128 * wn + 32 * t + l32;
+      bfo[t][ks] = br * kBK + 8 * b_slot(br, 2 * ks + hh);
+    }
+  }
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x16{};
+  // Two fragment sets: k step ks of a chunk uses set ks.
+  bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+  auto read = [&](const bf16 *sa, const bf16 *sb, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      fa[t] = *reinterpret_cast<const bf16x8 *>(sa + afo[t][ks]);
+      fb[t] = *reinterpret_cast<const bf16x8 *>(sb + bfo[t][ks]);
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], int mt0, int mt1)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = mt0; mt < mt1; ++mt)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = mfma32(fa[mt], fb[ct], acc[mt][ct]);
+  };
+  const int nc = g.K / kBK;
+#define TDP_FENCE() __builtin_amdgcn_sched_barrier(0)
+  // Chunk c in stage (sa, sb); chunk c + kBStages - 1 goes to (la, lb), the
+  // stage chunk c - 1 used; the next chunk is in (na, nb).  The loads go out
+  // first; the reads of step 1 go out before the MFMAs of step 0; the wait for
+  // the next chunk (the newer kBStages - 2 chunks may still be in flight), the
+  // barrier and the next chunk's first reads sit between the two halves of
+  // step 1's MFMAs.  Loads past the last chunk re-load chunk nc - 1 (in range,
+  // never used), so every chunk leaves the same count of loads in flight.
+  auto chunk = [&](int c, const bf16 *sa, const bf16 *sb, bf16 *la, bf16 *lb, const bf16 *na,
+                   const bf16 *nb) __attribute__((always_inline)) {
+#if TDP_GEMM_INTERLEAVE
+    // One MFMA, then one memory instruction, in a fixed order: step 0's 16
+    // MFMAs carry the 8 fragment reads of step 1 and the chunk's 8 direct
+    // loads; step 1's second 8 MFMAs carry the next chunk's 8 first reads.
+    const uint2 so = chunk_soff(min(c + kBStages - 1, nc - 1));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      acc[q / 4][q % 4] = mfma32(fa0[q / 4], fb0[q % 4], acc[q / 4][q % 4]);
+      if (q < 4) fa1[q] = *reinterpret_cast<const bf16x8 *>(sa + afo[q][1]);
+      else if (q < 8) fb1[q - 4] = *reinterpret_cast<const bf16x8 *>(sb + bfo[q - 4][1]);
+      else load_one(q - 8, so, la, lb);
+      TDP_FENCE();
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      acc[q / 4][q % 4] = mfma32(fa1[q / 4], fb1[q % 4], acc[q / 4][q % 4]);
+      TDP_FENCE();
+    }
+    wait_chunks<kBStages - 2>();
+    lds_barrier();
+    TDP_FENCE();
+#pragma unroll
+    for (int q = 8; q < 16; ++q) {
+      if (q < 12) fa0[q - 8] = *reinterpret_cast<const bf16x8 *>(na + afo[q - 8][0]);
+      else fb0[q - 12] = *reinterpret_cast<const bf16x8 *>(nb + bfo[q - 12][0]);
+      acc[q / 4][q % 4] = mfma32(fa1[q / 4], fb1[q % 4], acc[q / 4][q % 4]);
+      TDP_FENCE();
+    }
+    return;
+#endif
+    load_chunk(min(c + kBStages - 1, nc - 1), la, lb);
+    TDP_FENCE();
+    read(sa, sb, 1, fa1, fb1);
+    TDP_FENCE();
+    mfmas(fa0, fb0, 0, 4);
+    TDP_FENCE();
+    mfmas(fa1, fb1, 0, 2);
+    TDP_FENCE();
+    wait_chunks<kBStages - 2>();
+    lds_barrier();
+    read(na, nb, 0, fa0, fb0);
+    TDP_FENCE();
+    mfmas(fa1, fb1, 2, 4);
+    TDP_FENCE();
+  };
+  static_assert(kBLoads == 8, "wait_chunks counts 8 loads per chunk");
+  // Prologue: chunks 0 .. kBStages - 2 into stages 0 .. kBStages - 2, wait
+  // for chunk 0, its first fragments.
+  auto prologue = [&](bf16 *a0, bf16 *b0, bf16 *a1, bf16 *b1, bf16 *a2, bf16 *b2)
+      __attribute__((always_inline)) {
+    load_chunk(0, a0, b0);
+    if constexpr (kBStages > 2) load_chunk(min(1, nc - 1), a1, b1);
+    if constexpr (kBStages > 3) load_chunk(min(2, nc - 1), a2, b2);
+    wait_chunks<kBStages - 2>();
+    lds_barrier();
+    read(a0, b0, 0, fa0, fb0);
+  };
+  prologue(sA[0], sB[0], sA[1 % kBStages], sB[1 % kBStages], sA[2 % kBStages],
+           sB[2 % kBStages]);
+  // nc is a multiple of kBStages (host check): every stage index below is a
+  // constant.
+  for (int c0 = 0; c0 < nc; c0 += kBStages) {
+#pragma unroll
+    for (int st = 0; st < kBStages; ++st)
+      chunk(c0 + st, sA[st], sB[st], sA[(st + kBStages - 1) % kBStages],
+            sB[(st + kBStages - 1) % kBStages], sA[(st + 1) % kBStages],
+            sB[(st + 1) % kBStages]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef TDP_FENCE
+
+  // acc[mt][ct][v]: row 128 wm + 32 mt + 8 (v/4) + 4 hh + v%4, column
+  // 128 wn + 32 ct + l32.  The residual forms read all of a 32-row group's
+  // old values before storing any (one wave per SIMD: nothing else hides the
+  // load latency).
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t base = row0 + 128 * wm + 32 * mt;
+    if constexpr (EPI == kEpiResid || EPI == kEpiResidGate) {
+      float old[16][4];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          old[v][ct] = r < M ? static_cast<const float *>(g.c)[r * g.ldc + col0 + 128 * wn +
+                                                                 32 * ct + l32]
+                             : 0.f;
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
+        if (r >= M) continue;
+        const int64_t b = r / g.rows_per_batch;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int64_t n = col0 + 128 * wn + 32 * ct + l32;
+          float gt = 1.0f;
+          if constexpr (EPI == kEpiResidGate)
+            gt = (g.g0 ? g.g0[b * g.g0_stride + n] : 0.f) + (g.g1 ? g.g1[n] : 0.f);
+          static_cast<float *>(g.c)[r * g.ldc + n] = fmaf(gt, acc[mt][ct][v], old[v][ct]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
+        if (r >= M) continue;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int64_t idx = r * g.ldc + col0 + 128 * wn + 32 * ct + l32;
+          const float x = acc[mt][ct][v];
+          if constexpr (EPI == kEpiBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(x);
+          if constexpr (EPI == kEpiF32) static_cast<float *>(g.c)[idx] = x;
+          if constexpr (EPI == kEpiGeluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(gelu_tanh(x));
+          if constexpr (EPI == kEpiSiluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(silu(x));
+        }
+      }
+    }
+  }
+}
+
+// Which form serves the large products: 2 = the large form above, 1 = the
+// wide form.
+#ifndef TDP_GEMM_BIG
+#define TDP_GEMM_BIG 2
+#endif
+
 #ifndef TDP_GEMM_WIDE
 #define TDP_GEMM_WIDE 1
 #endif
@@ -385,6 +740,20 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
     const dim3 wgrid = TDP_GEMM_GROUP_M > 0
                            ? dim3(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8))
                            : dim3(static_cast<uint32_t>(nm), static_cast<uint32_t>(nn));
+    // the large form, except for the read-modify-write epilogues (with one
+    // wave per SIMD their load latency shows; measured slower than the wide
+    // form there)
+    if (TDP_GEMM_BIG == 2 && EPI != kEpiResid && EPI != kEpiResidGate &&
+        a.K % (kBK * kBStages) == 0 && (hd == 0 || a.M * a.K * 2 < (int64_t{1} << 32))) {
+      const dim3 bgrid(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8));
+      if (hd == 0)
+        hipLaunchKernelGGL((gemm_big_kernel<EPI, 0>), bgrid, dim3(kBThreads), 0, stream, a);
+      else if (hd == 64)
+        hipLaunchKernelGGL((gemm_big_kernel<EPI, 64>), bgrid, dim3(kBThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((gemm_big_kernel<EPI, 128>), bgrid, dim3(kBThreads), 0, stream, a);
+      return launch_status();
+    }
     if (hd == 0)
       hipLaunchKernelGGL((gemm_wide_kernel<EPI, 0>), wgrid, dim3(kGThreads), 0, stream, a);
     else if (hd == 64)
