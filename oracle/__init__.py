@@ -21,6 +21,8 @@ step, in plain NumPy:
               self- and cross-attention, FFN) and a step that uses it
   upscale.py    the upscale loop: re-noise, TDP velocity and Euler update per
               step, seam spread of the tiles
+  sp.py         sequence parallelism for the first stage: token partition,
+              head exchange and its inverse, the layer computed the SP way
 
 Where the pages are silent, the readings used are stated in each function's
 docstring.  Pins (tests that tie each function to something other than
@@ -37,3 +39,4 @@ from .blend import gather_tiles, blend_tiles, audio_mean  # noqa: F401
 from .tdp_step import step  # noqa: F401
 from .upscale import (linear_sigmas, renoise, euler_step, seam_spread,  # noqa: F401
                       upscale_loop)
+from .sp import padded_tokens, send_heads, gather_heads, sp_layer, head_share  # noqa: F401

@@ -285,3 +285,33 @@ def test_timestep_without_scale_is_caught(monkeypatch):
 
 
 _ORIG_SEAM = oup.seam_spread
+
+
+# --------------------------------------------------------------------------
+# sequence parallelism
+# --------------------------------------------------------------------------
+
+import oracle.sp as osp  # noqa: E402
+import tests.test_oracle_sp as tsp  # noqa: E402
+
+
+def test_unmasked_padding_is_caught(monkeypatch):
+    def softmax_all(logits, n_valid):
+        m = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - m)
+        return e / e.sum(axis=1, keepdims=True)
+    monkeypatch.setattr(osp, "_softmax_masked", softmax_all)
+    with pytest.raises(AssertionError):
+        tsp.test_sp_layer_equals_untiled_layer(30, 4)
+
+
+def test_exchange_to_the_wrong_rank_is_caught(monkeypatch):
+    def send(x_local, rank, world, t_pad, dst):
+        t_loc, heads, _ = x_local.shape
+        hw = heads // world
+        for s in range(world):
+            src = (s + 1) % world
+            dst[s][rank * t_loc:(rank + 1) * t_loc] = x_local[:, src * hw:(src + 1) * hw]
+    monkeypatch.setattr(osp, "send_heads", send)
+    with pytest.raises(AssertionError):
+        tsp.test_exchange_definition_and_round_trip(24, 4, 8, 4)
