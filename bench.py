@@ -35,6 +35,12 @@ with overlap 8, 32 heads x 128, bf16).  Prints ONE JSON line.
                step's seam spread, and the fused blend/Euler kernel alone on the
                workload's plan against 8 TB/s (algorithmic bytes: tile rows,
                the latent read and written, the inverse map)
+  sp           (--sp W) sequence parallelism for the first stage on the
+               6144-token latent (16x16x24, 32 heads x 128): one rank's share
+               (all tokens, H/W heads) timed on this GPU with its attention
+               core against the bf16 peak, and the head exchange (send of Q, K
+               and V, gather of the output) with every rank's buffer in this
+               GPU's memory, against 8 TB/s
 """
 from __future__ import annotations
 
@@ -349,6 +355,91 @@ def _time_blend_euler(s, B, C, N, n_dst, n_launch=50) -> dict:
     return out
 
 
+def sp_bench(world: int, reps: int = 20) -> dict:
+    """One rank's share of the first stage's attention layer, and the head
+    exchange, on this GPU."""
+    import dataclasses as dc
+
+    import numpy as np
+    import torch
+
+    import tdp_inputs as ti
+    from tiled_video_diffusion_amd import tdp
+    from tiled_video_diffusion_amd.step import TdpStep
+
+    inp = ti.make_inputs("sp_16x16x24")
+    wl = inp.workload
+    H, d, C = wl.heads, wl.head_dim, wl.channels
+    if H % world:
+        raise SystemExit(f"--sp {world}: {H} heads do not divide by the world size")
+    hw = H // world
+    cols = slice(0, hw * d)                    # rank 0's heads
+    share = dc.replace(inp, workload=dc.replace(wl, heads=hw),
+                       wq=np.ascontiguousarray(inp.wq[:, cols]),
+                       wk=np.ascontiguousarray(inp.wk[:, cols]),
+                       wv=np.ascontiguousarray(inp.wv[:, cols]),
+                       wo=np.ascontiguousarray(inp.wo[cols]))
+    st = TdpStep(share)
+    stream = torch.cuda.current_stream()
+    st.gather()
+    st.attn_prepare()
+    for _ in range(3):
+        st.attn_qkv()
+        st.attn_core()
+        st.attn_out()
+    torch.cuda.synchronize()
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)] for n in ("qkv", "core", "out")}
+    for i in range(reps):
+        for n, fn in (("qkv", st.attn_qkv), ("core", st.attn_core), ("out", st.attn_out)):
+            ev[n][i][0].record(stream)
+            fn()
+            ev[n][i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
+    T = wl.n_gen
+    flops = 4.0 * d * hw * T * T
+    core_tf = flops / (ms["core"] * 1e-3) / 1e12
+    st = None
+    # the exchange: this rank's slice of Q, K, V (all heads) to every rank's
+    # buffer, and the output back; every buffer in this GPU's memory
+    t_loc = T // world
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    src = torch.randn((t_loc, H, d), generator=g, device="cuda:0").to(torch.bfloat16)
+    bufs = [torch.empty((world * t_loc, hw, d), dtype=torch.bfloat16, device="cuda:0")
+            for _ in range(world)]
+    back = torch.empty_like(src)
+    nbytes = 2 * t_loc * H * d * 2             # read + write of one slice
+
+    def timed(fn, n=50):
+        for _ in range(3):
+            fn()
+        e = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n)]
+        for a, b in e:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in e]))
+
+    send_ms = timed(lambda: tdp.tdp_sp_send_heads(src, tdp.TDP_BF16, t_loc, H, d, world, 0, bufs,
+                                                  stream))
+    gather_ms = timed(lambda: tdp.tdp_sp_gather_heads(bufs, tdp.TDP_BF16, t_loc, H, d, world, 0,
+                                                      back, stream))
+    return {"workload": wl.name, "tokens": T, "world": world, "heads_per_rank": hw,
+            "share_ms": {k: v for k, v in ms.items()},
+            "share_core": {"achieved": core_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": core_tf / PEAK_BF16_TFLOPS, "flops_per_launch": flops},
+            "exchange": {"bytes_per_launch": nbytes, "send_ms": send_ms,
+                         "gather_ms": gather_ms,
+                         "send_gbs": nbytes / (send_ms * 1e-3) / 1e9,
+                         "gather_gbs": nbytes / (gather_ms * 1e-3) / 1e9,
+                         "per_step": "3 sends (Q, K, V) and 1 gather per attention layer",
+                         "note": "every rank's buffer in this GPU's memory; with peer "
+                                 "pointers the same copies go over the GPU links"}}
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -474,6 +565,10 @@ def run(args) -> dict:
         step = None
         torch.cuda.empty_cache()
         out["loop"] = loop_bench(args.loop, max(2, args.steps // 8), 1)
+    if args.sp:
+        step = None
+        torch.cuda.empty_cache()
+        out["sp"] = sp_bench(args.sp)
     if args.shares:
         step = None
         torch.cuda.empty_cache()
@@ -499,6 +594,9 @@ def main():
     ap.add_argument("--loop", default="",
                     help="also time the upscale loop (an upscale workload name, e.g. "
                          "upscale_t16)")
+    ap.add_argument("--sp", type=int, default=0,
+                    help="also time one rank's share of sequence parallelism on the "
+                         "first-stage latent for this many ranks")
     ap.add_argument("--shares", type=int, default=0,
                     help="also time each rank's round-robin share for this many ranks "
                          "(one after another on this GPU)")

@@ -438,6 +438,39 @@ tdp_status tdp_upscale_loop(const tdp_block_desc *desc, const tdp_plan_dev *plan
                             const float *sigmas, int32_t n_steps, float *x, double *seam,
                             void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* ------------------------------------------------------------------------ */
+
+/* Sequence parallelism (SP) for the first stage: the head exchange.  LTX-2
+ * sequence-parallel guide (how a denoising step is split; the all2all
+ * kernel): the W ranks hold equal contiguous slices of the (padded) tokens;
+ * before self-attention an exchange gives every rank all tokens of H/W of
+ * the heads (rank s: heads [s H/W, (s+1) H/W)), and after it the inverse
+ * exchange returns each rank's token slice with the outputs of all heads.
+ * These calls are one rank's half of each exchange, as direct copies into
+ * (or out of) every rank's buffer: pointers to this GPU's memory, or to peer
+ * buffers mapped into the process.  Cross-GPU completion signalling is the
+ * caller's (not needed on one GPU).
+ *
+ * Layouts (row-major, dtype elements): this rank's slice [t_loc][heads][d];
+ * each rank's head buffer [world t_loc][heads / world][d], token t of rank r
+ * at row r t_loc + t.  Constraints: 1 <= world <= 16, heads % world == 0,
+ * (heads / world) d a multiple of 16 bytes; 16-byte aligned buffers.  The
+ * exchange moves bytes only: tdp_sp_gather_heads after tdp_sp_send_heads
+ * returns the slice bit for bit.  Asynchronous on hip_stream.  Errors:
+ * TDP_ERR_ARG, TDP_ERR_UNSUPPORTED, TDP_ERR_NULL, TDP_ERR_ALIGN, TDP_ERR_HIP. */
+
+/* dst[s] rows [rank t_loc, (rank+1) t_loc) <- src's heads of rank s.
+ * dst: host array of `world` device pointers. */
+tdp_status tdp_sp_send_heads(const void *src, int32_t dtype, int64_t t_loc, int32_t heads,
+                             int32_t head_dim, int32_t world, int32_t rank, void *const *dst,
+                             void *hip_stream);
+
+/* dst's heads of rank s <- src[s] rows [rank t_loc, (rank+1) t_loc).
+ * src: host array of `world` device pointers. */
+tdp_status tdp_sp_gather_heads(const void *const *src, int32_t dtype, int64_t t_loc,
+                               int32_t heads, int32_t head_dim, int32_t world, int32_t rank,
+                               void *dst, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,7 +69,7 @@ class Workload:
         return n
 
 
-# The five workloads.  Sizes follow the TDP page's examples: 16 tiles (as in the
+# The workloads.  Sizes follow the TDP page's examples: 16 tiles (as in the
 # "16 tiles on 4 GPUs" example), 2D H x W grids with an overlap in latent units,
 # negative-time reference tokens, and an untiled audio stream.
 WORKLOADS = {
@@ -93,6 +93,18 @@ WORKLOADS = {
         "blend_32x96x160", grid=(32, 96, 160), tiling=((1, 0), (6, 16), (10, 16)), batch=1,
         channels=128, heads=0, head_dim=0, n_cond=0, n_cond_neg=0, n_audio=0,
         latent_dtype="f32", identity=True, seed=4),
+    # Sequence parallelism for the first stage: the whole latent is one
+    # sequence (a 1x1x1 "tiling"), its heads split over the ranks.  The
+    # 16x16x24 grid is the 6144-token first-stage latent of the sequence-
+    # parallel guide's table (512 x 768 pixels, 121 frames).
+    "sp_small": Workload(
+        "sp_small", grid=(2, 6, 10), tiling=((1, 0), (1, 0), (1, 0)), batch=1,
+        channels=128, heads=8, head_dim=64, n_cond=0, n_cond_neg=0, n_audio=0,
+        latent_dtype="bf16", identity=False, seed=5),
+    "sp_16x16x24": Workload(
+        "sp_16x16x24", grid=(16, 16, 24), tiling=((1, 0), (1, 0), (1, 0)), batch=1,
+        channels=128, heads=32, head_dim=128, n_cond=0, n_cond_neg=0, n_audio=0,
+        latent_dtype="bf16", identity=False, seed=6),
 }
 
 

@@ -287,3 +287,21 @@ def test_upscale_validation():
     sig = (ctypes.c_float * 4)(0.5, 0.3, 0.1, 0.0)
     assert L.tdp_upscale_loop(ctypes.byref(d), ctypes.byref(p), ctypes.byref(w), None, sig, 3,
                               None, None, None, 0, None) == -1
+
+
+def test_sp_exchange_validation():
+    L = tdp.lib()
+    arr = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    P = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    assert L.tdp_sp_send_heads(FAKE, 1, 16, 32, 128, 4, 4, P, None) == -2      # rank >= world
+    assert L.tdp_sp_send_heads(FAKE, 1, 16, 30, 128, 4, 0, P, None) == -4      # heads % world
+    assert L.tdp_sp_send_heads(FAKE, 1, 16, 32, 128, 17, 0, P, None) == -4     # world > 16
+    assert L.tdp_sp_send_heads(FAKE, 1, 16, 4, 4, 4, 0, P, None) == -4         # 2-byte segments
+    assert L.tdp_sp_send_heads(FAKE, 7, 16, 32, 128, 4, 0, P, None) == -4      # dtype
+    assert L.tdp_sp_send_heads(None, 1, 16, 32, 128, 4, 0, P, None) == -1
+    assert L.tdp_sp_send_heads(FAKE + 8, 1, 16, 32, 128, 4, 0, P, None) == -7
+    bad = (ctypes.c_void_p * 4)(FAKE, None, FAKE, FAKE)
+    assert L.tdp_sp_send_heads(FAKE, 1, 16, 32, 128, 4, 0,
+                               ctypes.cast(bad, ctypes.POINTER(ctypes.c_void_p)), None) == -1
+    assert L.tdp_sp_gather_heads(P, 1, 16, 32, 128, 4, 0, None, None) == -1
+    assert L.tdp_sp_gather_heads(P, 1, 0, 32, 128, 4, 0, None, None) == 0      # empty slice

@@ -1,0 +1,143 @@
+"""GPU parity of the sequence-parallel pieces one GPU can run.
+
+  * The head exchange (tdp_sp_send_heads / tdp_sp_gather_heads) with every
+    rank's buffers on this GPU: bit-exact against the oracle's exchange, and
+    the round trip returns each slice bit for bit.
+  * One rank's attention share at its real shape: all tokens of the frame,
+    H/W heads (tdp_tile_attention on a one-tile plan with the rank's head
+    columns of Wq, Wk, Wv and rows of Wo).  Each share against the oracle's
+    (2e-2, max abs error / max abs reference), and the sum of all ranks'
+    shares against the untiled layer and the SP layer of the oracle (2e-2).
+    The 6144-token first-stage latent is checked on sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.sp as osp
+import tdp_inputs as ti
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def say(*a):
+    print("[gpu-sp]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    return float(np.abs(got - want).max() / max(np.abs(want).max(), 1e-30))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("t_loc,H,d,W", [(768, 32, 128, 8), (41, 6, 64, 3), (16, 4, 64, 1),
+                                         (33, 16, 128, 16)])
+def test_exchange_bit_exact(dtype, t_loc, H, d, W):
+    from tiled_video_diffusion_amd import tdp
+    say("exchange", dtype, t_loc, H, d, W)
+    tt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    code = tdp.TDP_BF16 if dtype == "bf16" else tdp.TDP_F32
+    g = torch.Generator().manual_seed(t_loc * 31 + W)
+    slices = [torch.randn((t_loc, H, d), generator=g).to(tt) for _ in range(W)]
+    dev = [x.to("cuda:0") for x in slices]
+    bufs = [torch.full((W * t_loc, H // W, d), float("nan"), dtype=tt, device="cuda:0")
+            for _ in range(W)]
+    for r in range(W):
+        tdp.tdp_sp_send_heads(dev[r], code, t_loc, H, d, W, r, bufs)
+    torch.cuda.synchronize()
+    want = [np.zeros((W * t_loc, H // W, d), np.float32) for _ in range(W)]
+    for r in range(W):
+        osp.send_heads(slices[r].float().numpy(), r, W, W * t_loc, want)
+    for s in range(W):
+        got = bufs[s].float().cpu().numpy()
+        assert np.array_equal(got, want[s]), s
+    for r in range(W):
+        back = torch.empty_like(dev[r])
+        tdp.tdp_sp_gather_heads(bufs, code, t_loc, H, d, W, r, back)
+        torch.cuda.synchronize()
+        assert torch.equal(back.cpu().view(torch.int16 if dtype == "bf16" else torch.int32),
+                           slices[r].view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+def _share(inp, plan, W, r, dev_plan):
+    """Rank r's share on the GPU: y [T][C] float32."""
+    from tiled_video_diffusion_amd import tdp
+    wl = inp.workload
+    H, d, C = wl.heads, wl.head_dim, wl.channels
+    hs = osp.head_share(H, W, r)
+    cols = slice(hs.start * d, hs.stop * d)
+    bf = torch.bfloat16
+    wq, wk, wv = (torch.from_numpy(np.ascontiguousarray(w[:, cols])).to(bf).to("cuda:0")
+                  for w in (inp.wq, inp.wk, inp.wv))
+    wo = torch.from_numpy(np.ascontiguousarray(inp.wo[cols])).to(bf).to("cuda:0")
+    desc = tdp.attn_desc(1, C, H // W, d, 0, tdp.TDP_BF16, tdp.TDP_F32)
+    R = plan.n_rows
+    ws_bytes = tdp.tdp_tile_attention_workspace(desc, 1, R)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty((1, R, C), dtype=torch.float32, device="cuda:0")
+    x_tiles, row_pos, trb = dev_plan
+    tdp.tdp_tile_attention(desc, 1, trb, plan.max_tile_rows, R, x_tiles, row_pos, wq, wk, wv, wo,
+                           None, y, None, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return y[0].cpu().numpy()
+
+
+def _setup(name):
+    from tiled_video_diffusion_amd import tdp
+    inp = ti.make_inputs(name)
+    wl = inp.workload
+    plan = tdp.tdp_plan(wl.grid, wl.tiling)
+    po = oracle.plan(wl.grid, wl.tiling)
+    x = inp.x_global[0][po.row_src]
+    x_tiles = torch.from_numpy(np.ascontiguousarray(x[None])).to(torch.bfloat16).to("cuda:0")
+    row_pos = torch.from_numpy(plan.row_pos).to("cuda:0")
+    trb = torch.from_numpy(plan.tile_row_begin).to("cuda:0")
+    return inp, plan, po, x, (x_tiles, row_pos, trb)
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_rank_shares_sum_to_the_layer(W):
+    inp, plan, po, x, dev_plan = _setup("sp_small")
+    wl = inp.workload
+    H, d = wl.heads, wl.head_dim
+    total = np.zeros((x.shape[0], wl.channels))
+    for r in range(W):
+        got = _share(inp, plan, W, r, dev_plan)
+        hs = osp.head_share(H, W, r)
+        cols = slice(hs.start * d, hs.stop * d)
+        want, _ = oracle.tile_forward(x, po.row_pos, None, inp.wq[:, cols], inp.wk[:, cols],
+                                      inp.wv[:, cols], inp.wo[cols], H // W, d)
+        e = rel_err(got, want)
+        assert e <= TOL, (r, e)
+        total += got
+    full, _ = oracle.tile_forward(x, po.row_pos, None, inp.wq, inp.wk, inp.wv, inp.wo, H, d)
+    sp = osp.sp_layer(x, po.row_pos, inp.wq, inp.wk, inp.wv, inp.wo, H, d, W)
+    e_full, e_sp = rel_err(total, full), rel_err(total, sp)
+    say(f"W={W}: sum of shares vs layer {e_full:.2e}, vs SP layer {e_sp:.2e}")
+    assert e_full <= TOL and e_sp <= TOL
+
+
+def test_rank_share_first_stage_sampled():
+    """The 6144-token first-stage latent, 32 heads x 128 over 8 ranks: ranks 0
+    and 7 (4 heads each) on sampled rows."""
+    inp, plan, po, x, dev_plan = _setup("sp_16x16x24")
+    wl = inp.workload
+    H, d, W = wl.heads, wl.head_dim, 8
+    rng = np.random.default_rng(3)
+    rows = np.array(sorted({0, x.shape[0] - 1} | set(rng.integers(0, x.shape[0], 14).tolist())))
+    for r in (0, 7):
+        got = _share(inp, plan, W, r, dev_plan)
+        hs = osp.head_share(H, W, r)
+        cols = slice(hs.start * d, hs.stop * d)
+        want, _ = oracle.tile_forward(x, po.row_pos, None, inp.wq[:, cols], inp.wk[:, cols],
+                                      inp.wv[:, cols], inp.wo[cols], H // W, d, query_rows=rows)
+        e = rel_err(got[rows], want)
+        say(f"rank {r}: {rows.size} rows {e:.2e}")
+        assert e <= TOL

@@ -113,6 +113,8 @@ _SIGS = {
     "tdp_upscale_workspace": (_I32, [C.POINTER(BlockDesc), C.POINTER(PlanDev), C.POINTER(_SZ)]),
     "tdp_upscale_loop": (_I32, [C.POINTER(BlockDesc), C.POINTER(PlanDev), C.POINTER(BlockWeights),
                                 _P, C.POINTER(C.c_float), _I32, _P, _P, _P, _SZ, _P]),
+    "tdp_sp_send_heads": (_I32, [_P, _I32, _I64, _I32, _I32, _I32, _I32, C.POINTER(_P), _P]),
+    "tdp_sp_gather_heads": (_I32, [C.POINTER(_P), _I32, _I64, _I32, _I32, _I32, _I32, _P, _P]),
 }
 
 _lib = None
@@ -438,3 +440,27 @@ def tdp_upscale_loop(desc, plan: PlanDev, weights: BlockWeights, text, sigmas, n
                                   sig.ctypes.data_as(C.POINTER(C.c_float)), int(n_steps), _ptr(x),
                                   _ptr(seam), _ptr(workspace), workspace_bytes, _stream(stream)),
            "tdp_upscale_loop")
+
+
+# ---------------------------------------------------------------------------
+# sequence parallelism: the head exchange
+# ---------------------------------------------------------------------------
+
+def _ptr_array(bufs):
+    return (C.c_void_p * len(bufs))(*[_ptr(b) for b in bufs])
+
+
+def tdp_sp_send_heads(src, dtype, t_loc, heads, head_dim, world, rank, dst_bufs,
+                      stream=None) -> None:
+    arr = _ptr_array(dst_bufs)
+    _check(lib().tdp_sp_send_heads(_ptr(src), dtype, t_loc, heads, head_dim, world, rank,
+                                   C.cast(arr, C.POINTER(C.c_void_p)), _stream(stream)),
+           "tdp_sp_send_heads")
+
+
+def tdp_sp_gather_heads(src_bufs, dtype, t_loc, heads, head_dim, world, rank, dst,
+                        stream=None) -> None:
+    arr = _ptr_array(src_bufs)
+    _check(lib().tdp_sp_gather_heads(C.cast(arr, C.POINTER(C.c_void_p)), dtype, t_loc, heads,
+                                     head_dim, world, rank, _ptr(dst), _stream(stream)),
+           "tdp_sp_gather_heads")
