@@ -141,3 +141,12 @@ def test_rank_share_first_stage_sampled():
         e = rel_err(got[rows], want)
         say(f"rank {r}: {rows.size} rows {e:.2e}")
         assert e <= TOL
+
+
+def test_exchange_empty_slice_is_a_no_op():
+    from tiled_video_diffusion_amd import tdp
+    bufs = [torch.zeros((8, 2, 64), dtype=torch.bfloat16, device="cuda:0") for _ in range(2)]
+    src = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda:0")
+    tdp.tdp_sp_send_heads(src, tdp.TDP_BF16, 0, 4, 64, 2, 1, bufs)
+    torch.cuda.synchronize()
+    assert all(int(torch.count_nonzero(b)) == 0 for b in bufs)

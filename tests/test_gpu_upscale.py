@@ -291,3 +291,33 @@ def test_upscale_loop_full_width_one_step():
     e = rel_err(v_gpu[toks], v_ref)
     say(f"  sampled velocities ({toks.size} tokens): {e:.2e}")
     assert e <= TOL
+
+
+def test_edge_cases():
+    """renoise at sigma 0 and 1 (closed forms), blend_euler with no generated
+    tokens (x untouched, seam sums zero)."""
+    from tiled_video_diffusion_amd import tdp
+    rng = np.random.default_rng(9)
+    x1 = rng.standard_normal((2, 7, 8)).astype(np.float32)
+    eps = rng.standard_normal((2, 5, 8)).astype(np.float32)
+    x1_d, eps_d = _dev(x1), _dev(eps)
+    x = torch.empty_like(x1_d)
+    tdp.tdp_renoise(x1_d, eps_d, 2, 5, 7, 8, 0.0, x)
+    torch.cuda.synchronize()
+    assert np.array_equal(x.cpu().numpy(), x1)
+    tdp.tdp_renoise(x1_d, eps_d, 2, 5, 7, 8, 1.0, x)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    assert np.array_equal(got[:, :5], eps) and np.array_equal(got[:, 5:], x1[:, 5:])
+    # no generated tokens: only conditioning rows, nothing updated
+    ws_bytes = max(tdp.tdp_blend_euler_workspace(1, 0, 128), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
+    seam = torch.full((3,), -1.0, dtype=torch.float64, device="cuda:0")
+    xc = _dev(rng.standard_normal((1, 4, 128)).astype(np.float32))
+    before = xc.clone()
+    drb = torch.zeros(5, dtype=torch.int64, device="cuda:0")
+    tdp.tdp_blend_euler(None, tdp.TDP_F32, 1, 0, 128, drb, None, None, 0, xc, 4, 0.5, 0.25, seam,
+                        ws, ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(xc, before)
+    assert seam.cpu().tolist() == [0.0, 0.0, 0.0]

@@ -743,8 +743,14 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
     // the large form, except for the read-modify-write epilogues (with one
     // wave per SIMD their load latency shows; measured slower than the wide
     // form there)
+    // (its buffer descriptors cover a workgroup's rows of A and B^T, or all of
+    // a head-major A, in 32-bit byte ranges)
+    constexpr int64_t k4G = int64_t{1} << 32;
+    const bool fits = (static_cast<int64_t>(kWRows) * a.lda + a.K) * 2 < k4G &&
+                      (static_cast<int64_t>(kWCols) * a.ldb + a.K) * 2 < k4G &&
+                      (hd == 0 || a.M * a.K * 2 < k4G);
     if (TDP_GEMM_BIG == 2 && EPI != kEpiResid && EPI != kEpiResidGate &&
-        a.K % (kBK * kBStages) == 0 && (hd == 0 || a.M * a.K * 2 < (int64_t{1} << 32))) {
+        a.K % (kBK * kBStages) == 0 && fits) {
       const dim3 bgrid(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8));
       if (hd == 0)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, 0>), bgrid, dim3(kBThreads), 0, stream, a);
