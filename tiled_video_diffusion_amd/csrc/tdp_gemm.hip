@@ -394,6 +394,13 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_wide_kernel(GemmArgs g) {
 #ifndef TDP_GEMM_STAGES
 #define TDP_GEMM_STAGES 4
 #endif
+// MFMAs of a chunk's last k step issued before its barrier (the rest carry
+// the next chunk's first fragment reads); at most 8.
+#ifndef TDP_GEMM_PRE_BARRIER
+#define TDP_GEMM_PRE_BARRIER 8
+#endif
+constexpr int kBPreBarrier = TDP_GEMM_PRE_BARRIER;
+static_assert(kBPreBarrier >= 0 && kBPreBarrier <= 8, "8 reads after the barrier");
 // 1: the chunk body interleaves MFMAs and memory instructions one by one;
 // 0: grouped (reads, then MFMAs, fenced).
 #ifndef TDP_GEMM_INTERLEAVE
@@ -614,17 +621,21 @@ __global__ __launch_bounds__(kBThreads, 1) void gemm_big_kernel(GemmArgs g) {
       TDP_FENCE();
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kBPreBarrier; ++q) {
       acc[q / 4][q % 4] = mfma32(fa1[q / 4], fb1[q % 4], acc[q / 4][q % 4]);
       TDP_FENCE();
     }
     wait_chunks<kBStages - 2>();
     lds_barrier();
     TDP_FENCE();
+    // the next chunk's step-0 fragments, in the order its first MFMAs use
+    // them: A tile 0, B tiles 0..3, A tiles 1..3
 #pragma unroll
-    for (int q = 8; q < 16; ++q) {
-      if (q < 12) fa0[q - 8] = *reinterpret_cast<const bf16x8 *>(na + afo[q - 8][0]);
-      else fb0[q - 12] = *reinterpret_cast<const bf16x8 *>(nb + bfo[q - 12][0]);
+    for (int q = kBPreBarrier; q < 16; ++q) {
+      const int r = q - kBPreBarrier;
+      if (r == 0) fa0[0] = *reinterpret_cast<const bf16x8 *>(na + afo[0][0]);
+      else if (r < 5) fb0[r - 1] = *reinterpret_cast<const bf16x8 *>(nb + bfo[r - 1][0]);
+      else if (r < 8) fa0[r - 4] = *reinterpret_cast<const bf16x8 *>(na + afo[r - 4][0]);
       acc[q / 4][q % 4] = mfma32(fa1[q / 4], fb1[q % 4], acc[q / 4][q % 4]);
       TDP_FENCE();
     }
