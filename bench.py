@@ -175,8 +175,8 @@ def shares(inp, world_size: int, reps: int = 5) -> dict:
 
     stream = torch.cuda.current_stream()
 
-    def time_share(world, rank):
-        st = TdpStep(inp, world_size=world, rank=rank)
+    def time_share(world, rank, assignment="round_robin"):
+        st = TdpStep(inp, world_size=world, rank=rank, assignment=assignment)
         for _ in range(2):
             st.run()
         torch.cuda.synchronize()
@@ -195,6 +195,7 @@ def shares(inp, world_size: int, reps: int = 5) -> dict:
         return ms, tiles, n_total
 
     rr = [time_share(world_size, r) for r in range(world_size)]
+    lf = [time_share(world_size, r, "longest_first") for r in range(world_size)]
     n_tiles = rr[0][2]
     per_tile = [time_share(n_tiles, t)[0] for t in range(n_tiles)]
     # longest processing time first: each tile to the least loaded rank
@@ -206,6 +207,11 @@ def shares(inp, world_size: int, reps: int = 5) -> dict:
     return {"world_size": world_size, "assignment": "round robin (tile t -> rank t mod W)",
             "ms_per_rank": [m for m, _, _ in rr], "tiles_per_rank": [t for _, t, _ in rr],
             "critical_ms": max(m for m, _, _ in rr),
+            "longest_first": {"ms_per_rank": [m for m, _, _ in lf],
+                              "tiles_per_rank": [t for _, t, _ in lf],
+                              "critical_ms": max(m for m, _, _ in lf),
+                              "assignment": "tiles by rows^2, largest first, each to the "
+                                            "least loaded rank (tdp_plan_desc.assignment = 1)"},
             "per_tile_ms": per_tile,
             "critical_ms_from_tile_times": {"round_robin": max(rr_from_tiles),
                                             "longest_first": max(loads)},

@@ -80,6 +80,13 @@ typedef struct {
   int32_t normalize_positions;/* 1 (default) or 0 ("Position normalization")        */
   int32_t world_size, rank;   /* round-robin share: tile t belongs to rank
                                  t mod world_size ("What it is"); (1, 0) = all     */
+  int32_t assignment;         /* 0 (default): the page's round robin above;
+                                 1: longest first -- tiles by attention cost
+                                 rows^2 (rows = generated + kept conditioning),
+                                 largest first (ties: lower index), each to the
+                                 rank with the least cost so far (ties: lower
+                                 rank).  A rank's tiles are listed in ascending
+                                 index either way.                                 */
 } tdp_plan_desc;
 
 typedef struct {

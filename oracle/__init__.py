@@ -33,7 +33,7 @@ here and checked only through invariants (masks sum to one, shift invariance,
 brute force), because the pages print no worked example.
 """
 from .tile_plan import (Plan, plan, dim_boxes, dim_weights, PlanError,  # noqa: F401
-                        balanced_tile_split)
+                        balanced_tile_split, assign_tiles)
 from .denoise import rope_angles, apply_rope, tile_forward  # noqa: F401
 from .blend import gather_tiles, blend_tiles, audio_mean  # noqa: F401
 from .tdp_step import step  # noqa: F401

@@ -144,8 +144,32 @@ def _keeps(cond_pos: np.ndarray, j: int, ext_start, ext_end) -> bool:
     return all(s[d] < ext_end[d] and e[d] > ext_start[d] for d in range(3))
 
 
+def assign_tiles(costs, world_size: int, assignment: str = "round_robin") -> list:
+    """Owner rank of every tile.
+
+    TDP page, "What it is": tiles are assigned round-robin, tile t to rank
+    t mod world_size.  "longest_first" is a balancing alternative the page
+    does not give (longest-processing-time-first): tiles in decreasing cost
+    (ties: lower index first), each to the rank whose cost so far is least
+    (ties: lower rank).
+    """
+    T = len(costs)
+    if assignment == "round_robin":
+        return [t % world_size for t in range(T)]
+    if assignment != "longest_first":
+        raise PlanError(f"unknown assignment {assignment!r}")
+    order = sorted(range(T), key=lambda t: (-costs[t], t))
+    load = [0] * world_size
+    owner = [0] * T
+    for t in order:
+        r = min(range(world_size), key=lambda q: (load[q], q))
+        owner[t] = r
+        load[r] += costs[t]
+    return owner
+
+
 def plan(grid, tiling, cond_pos=None, normalize_positions: bool = True,
-         world_size: int = 1, rank: int = 0) -> Plan:
+         world_size: int = 1, rank: int = 0, assignment: str = "round_robin") -> Plan:
     """Plan one rank's tiles of a TDP step.
 
     ``grid`` = (F, H, W); ``tiling`` = ((n_f, o_f), (n_h, o_h), (n_w, o_w));
@@ -154,8 +178,9 @@ def plan(grid, tiling, cond_pos=None, normalize_positions: bool = True,
 
     Passages followed (TDP page):
       * "What it is": tiles of the patchified latent, assigned round-robin, so
-        tile t goes to rank ``t mod world_size``.  Tile order (a reading):
-        row-major over (i_f, i_h, i_w), width fastest.
+        tile t goes to rank ``t mod world_size`` (or longest first, see
+        ``assign_tiles``).  Tile order (a reading): row-major over
+        (i_f, i_h, i_w), width fastest; a rank's tiles in ascending order.
       * Token order (a reading): generated token (f, h, w) is global row
         ``(f H + h) W + w``; conditioning token j is row ``N + j`` ("appended
         after the generated tokens").  A tile's rows are its generated tokens,
@@ -211,7 +236,10 @@ def plan(grid, tiling, cond_pos=None, normalize_positions: bool = True,
             keep[t, j] = _keeps(cond_pos, j, ext_s, ext_e)
     k = keep.sum(axis=0).astype(np.int32)
 
-    local = [t for t in range(T) if t % world_size == rank]
+    # Attention cost of a tile: (generated rows + kept conditioning rows)^2.
+    costs = [(gen[t][1].size + int(keep[t].sum())) ** 2 for t in range(T)]
+    owner = assign_tiles(costs, world_size, assignment)
+    local = [t for t in range(T) if owner[t] == rank]
     tile_box = np.zeros((len(local), 3, 2), dtype=np.int32)
     tile_offset = np.zeros((len(local), 3), dtype=F32)
     begin = [0]

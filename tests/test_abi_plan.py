@@ -59,13 +59,24 @@ def test_plan_bit_exact_blend_workload():
     _assert_same_plan(pc, po)
 
 
+@pytest.mark.parametrize("assignment", ["round_robin", "longest_first"])
 @pytest.mark.parametrize("W", [2, 3, 4, 7])
-def test_plan_bit_exact_multi_rank(W):
+def test_plan_bit_exact_multi_rank(W, assignment):
     inp = ti.make_inputs("audio_32x48x80")
     wl = dataclasses.replace(inp.workload, grid=(8, 48, 80))
     for r in range(W):
-        pc = tdp.tdp_plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r)
-        po = oracle.plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r)
+        pc = tdp.tdp_plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r, assignment)
+        po = oracle.plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r, assignment)
+        _assert_same_plan(pc, po)
+
+
+@pytest.mark.parametrize("W", [3, 4, 5])
+def test_plan_bit_exact_longest_first_t16(W):
+    inp = ti.make_inputs("t16_16x64x64")
+    wl = inp.workload
+    for r in range(W):
+        pc = tdp.tdp_plan(wl.grid, wl.tiling, None, True, W, r, "longest_first")
+        po = oracle.plan(wl.grid, wl.tiling, None, True, W, r, "longest_first")
         _assert_same_plan(pc, po)
 
 
@@ -93,8 +104,9 @@ def test_plan_bit_exact_random_descriptors():
         W = int(rng.integers(1, 4))
         r = int(rng.integers(0, W))
         norm = bool(rng.integers(0, 2))
-        pc = tdp.tdp_plan(grid, tiling, cond, norm, W, r)
-        po = oracle.plan(grid, tiling, cond, norm, W, r)
+        asg = "longest_first" if rng.integers(0, 2) else "round_robin"
+        pc = tdp.tdp_plan(grid, tiling, cond, norm, W, r, asg)
+        po = oracle.plan(grid, tiling, cond, norm, W, r, asg)
         _assert_same_plan(pc, po)
 
 
@@ -123,6 +135,13 @@ def test_plan_rejects_invalid(grid, tiling, cond, world, rank, code):
     assert e.value.status == code
     with pytest.raises(oracle.PlanError):
         oracle.plan(grid, tiling, cond, True, world, rank)
+
+
+def test_plan_rejects_unknown_assignment():
+    d, _ = tdp._desc((2, 8, 8), ((1, 0), (2, 2), (1, 0)), None, True, 2, 0)
+    d.assignment = 2
+    s = tdp.PlanSizes()
+    assert tdp.lib().tdp_plan_query(ctypes.byref(d), ctypes.byref(s)) == -2
 
 
 def test_plan_null_and_shape_errors():

@@ -233,17 +233,19 @@ def test_attention_full_size_sampled(name):
         assert e_am <= BLEND_TOL
 
 
+@pytest.mark.parametrize("assignment", ["round_robin", "longest_first"])
 @pytest.mark.parametrize("W", [2, 4])
-def test_multi_rank_sum_equals_single_rank(W):
-    """The page's single all_reduce: summing the W ranks' blends equals one rank's."""
-    say("multi-rank", W)
+def test_multi_rank_sum_equals_single_rank(W, assignment):
+    """The page's single all_reduce: summing the W ranks' blends equals one rank's
+    (round-robin tiles as on the page, or longest first)."""
+    say("multi-rank", W, assignment)
     inp = _variant("audio_32x48x80", grid=(8, 48, 80), heads=4)
     full = _step(inp)
     full.run()
     acc_g = torch.zeros_like(full.y_global)
     acc_a = torch.zeros_like(full.y_audio)
     for r in range(W):
-        s = _step(inp, world_size=W, rank=r)
+        s = _step(inp, world_size=W, rank=r, assignment=assignment)
         s.y_global = acc_g
         s.y_audio = acc_a
         s.run(accumulate=True)

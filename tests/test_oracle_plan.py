@@ -315,3 +315,40 @@ def test_balanced_split_special_cases():
     assert oracle.balanced_tile_split(60) == (6, 10)
     with pytest.raises(oracle.PlanError):
         oracle.balanced_tile_split(0)
+
+
+# --------------------------------------------------------------------------
+# longest-first tile assignment
+# --------------------------------------------------------------------------
+
+def test_longest_first_textbook_case():
+    """Costs 7, 6, 5, 4, 3 on two ranks: 7 -> 0, 6 -> 1, 5 -> 1, 4 -> 0, and 3
+    to rank 0 on the 11/11 tie; loads 14 and 11."""
+    owner = oracle.assign_tiles([7, 6, 5, 4, 3], 2, "longest_first")
+    assert owner == [0, 1, 1, 0, 0]
+    # ties in cost: lower index first
+    assert oracle.assign_tiles([5, 9, 5, 9], 2, "longest_first") == [0, 0, 1, 1]
+
+
+@pytest.mark.parametrize("T,W", [(16, 4), (7, 3), (5, 8), (24, 5)])
+def test_longest_first_with_equal_costs_is_round_robin(T, W):
+    assert oracle.assign_tiles([4] * T, W, "longest_first") == [t % W for t in range(T)]
+
+
+@pytest.mark.parametrize("name,W", [("t16_16x64x64", 4), ("audio_32x48x80", 5),
+                                    ("tiny_2x16x16", 3)])
+def test_longest_first_partitions_and_balances(name, W):
+    inp = ti.make_inputs(name)
+    wl = inp.workload
+    seen, rr_load, lf_load = [], [], []
+    for r in range(W):
+        p_lf = oracle.plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r, "longest_first")
+        p_rr = oracle.plan(wl.grid, wl.tiling, inp.cond_pos, True, W, r)
+        seen += p_lf.tile_id.tolist()
+        assert list(p_lf.tile_id) == sorted(p_lf.tile_id)
+        lf_load.append(int(np.sum(np.diff(p_lf.tile_row_begin).astype(np.int64) ** 2)))
+        rr_load.append(int(np.sum(np.diff(p_rr.tile_row_begin).astype(np.int64) ** 2)))
+    assert sorted(seen) == list(range(wl.n_tiles))
+    assert max(lf_load) <= max(rr_load)
+    if name == "t16_16x64x64":
+        assert max(lf_load) < max(rr_load)      # interior tiles carry 1.44x a corner's cost

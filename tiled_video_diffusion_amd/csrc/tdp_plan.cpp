@@ -89,6 +89,7 @@ tdp_status make_geometry(const tdp_plan_desc *desc, Geometry *g) {
   if (desc->world_size < 1 || desc->rank < 0 || desc->rank >= desc->world_size)
     return TDP_ERR_ARG;
   if (desc->normalize_positions != 0 && desc->normalize_positions != 1) return TDP_ERR_ARG;
+  if (desc->assignment != 0 && desc->assignment != 1) return TDP_ERR_ARG;
   int64_t T = 1, N = 1;
   for (int d = 0; d < 3; ++d) {
     g->dim[d].L = desc->grid[d];
@@ -128,6 +129,47 @@ int64_t box_volume(const int32_t a[3], const int32_t b[3]) {
   return static_cast<int64_t>(b[0] - a[0]) * (b[1] - a[1]) * (b[2] - a[2]);
 }
 
+// Rows of tile t: its generated tokens plus the conditioning tokens it keeps.
+int64_t tile_rows(const Geometry &g, const tdp_plan_desc *desc, int32_t t) {
+  int32_t a[3], b[3];
+  g.tile_box(t, a, b);
+  int64_t rows = box_volume(a, b);
+  for (int32_t j = 0; j < g.M; ++j) rows += keeps(desc->cond_pos + 6 * j, a, b) ? 1 : 0;
+  return rows;
+}
+
+// The tiles of desc->rank, ascending.  Round robin: t mod world_size == rank
+// ("What it is").  Longest first (a balancing alternative the page does not
+// give): tiles by cost rows^2 descending, ties by index, each to the rank
+// with the least accumulated cost, ties to the lower rank.
+std::vector<int32_t> local_tiles(const Geometry &g, const tdp_plan_desc *desc) {
+  std::vector<int32_t> mine;
+  const int32_t W = desc->world_size;
+  if (desc->assignment == 0) {
+    for (int32_t t = desc->rank; t < g.T; t += W) mine.push_back(t);
+    return mine;
+  }
+  std::vector<int64_t> cost(g.T);
+  std::vector<int32_t> order(g.T);
+  for (int32_t t = 0; t < g.T; ++t) {
+    const int64_t r = tile_rows(g, desc, t);
+    cost[t] = r * r;
+    order[t] = t;
+  }
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return cost[x] > cost[y]; });
+  std::vector<int64_t> load(W, 0);
+  for (const int32_t t : order) {
+    int32_t best = 0;
+    for (int32_t r = 1; r < W; ++r)
+      if (load[r] < load[best]) best = r;
+    load[best] += cost[t];
+    if (best == desc->rank) mine.push_back(t);
+  }
+  std::sort(mine.begin(), mine.end());
+  return mine;
+}
+
 }  // namespace
 
 extern "C" {
@@ -155,11 +197,8 @@ tdp_status tdp_plan_query(const tdp_plan_desc *desc, tdp_plan_sizes *sizes) {
   out.n_tiles_total = g.T;
   out.n_gen_total = static_cast<int32_t>(g.N);
   out.n_dst_rows = g.N + g.M;
-  for (int32_t t = desc->rank; t < g.T; t += desc->world_size) {
-    int32_t a[3], b[3];
-    g.tile_box(t, a, b);
-    int64_t rows = box_volume(a, b);
-    for (int32_t j = 0; j < g.M; ++j) rows += keeps(desc->cond_pos + 6 * j, a, b) ? 1 : 0;
+  for (const int32_t t : local_tiles(g, desc)) {
+    const int64_t rows = tile_rows(g, desc, t);
     if (rows > INT32_MAX) return TDP_ERR_ARG;
     out.n_tiles_local += 1;
     out.max_tile_rows = std::max<int32_t>(out.max_tile_rows, static_cast<int32_t>(rows));
@@ -200,7 +239,7 @@ tdp_status tdp_plan(const tdp_plan_desc *desc, const tdp_plan_sizes *sizes,
   int64_t row = 0;
   int32_t li = 0;
   std::vector<float> wdim[3];
-  for (int32_t t = desc->rank; t < g.T; t += desc->world_size, ++li) {
+  for (const int32_t t : local_tiles(g, desc)) {
     int32_t ii[3], a[3], b[3];
     g.tile_coords(t, ii);
     g.tile_box(t, a, b);
@@ -243,6 +282,7 @@ tdp_status tdp_plan(const tdp_plan_desc *desc, const tdp_plan_sizes *sizes,
       }
       ++row;
     }
+    ++li;
   }
   out->tile_row_begin[li] = row;
 

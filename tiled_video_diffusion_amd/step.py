@@ -26,13 +26,13 @@ class TdpStep:
 
     def __init__(self, inputs, normalize_positions: bool = True, world_size: int = 1,
                  rank: int = 0, device: str = "cuda:0", identity: Optional[bool] = None,
-                 rope_base: float = 10000.0):
+                 rope_base: float = 10000.0, assignment: str = "round_robin"):
         wl = inputs.workload
         self.wl = wl
         self.device = torch.device(device)
         self.identity = wl.identity if identity is None else identity
         self.plan = tdp.tdp_plan(wl.grid, wl.tiling, inputs.cond_pos, normalize_positions,
-                                 world_size, rank)
+                                 world_size, rank, assignment)
         p = self.plan
         dev = self.device
         self.latent_dtype = torch.bfloat16 if wl.latent_dtype == "bf16" else torch.float32

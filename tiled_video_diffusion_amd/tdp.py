@@ -39,7 +39,10 @@ class DimTiling(C.Structure):
 class PlanDesc(C.Structure):
     _fields_ = [("grid", C.c_int32 * 3), ("tiling", DimTiling * 3), ("n_cond", C.c_int32),
                 ("cond_pos", C.POINTER(C.c_float)), ("normalize_positions", C.c_int32),
-                ("world_size", C.c_int32), ("rank", C.c_int32)]
+                ("world_size", C.c_int32), ("rank", C.c_int32), ("assignment", C.c_int32)]
+
+
+ASSIGNMENTS = {"round_robin": 0, "longest_first": 1}
 
 
 class PlanSizes(C.Structure):
@@ -195,8 +198,10 @@ class Plan:
         return int(self.sizes["n_dst_rows"])
 
 
-def _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank):
+def _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank,
+          assignment="round_robin"):
     d = PlanDesc()
+    d.assignment = ASSIGNMENTS[assignment]
     for i in range(3):
         d.grid[i] = int(grid[i])
         d.tiling[i].num_tiles = int(tiling[i][0])
@@ -220,17 +225,17 @@ def tdp_balanced_tile_split(n):
 
 
 def tdp_plan_query(grid, tiling, cond_pos=None, normalize_positions=True, world_size=1,
-                   rank=0) -> dict:
-    d, _keep = _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank)
+                   rank=0, assignment="round_robin") -> dict:
+    d, _keep = _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank, assignment)
     s = PlanSizes()
     _check(lib().tdp_plan_query(C.byref(d), C.byref(s)), "tdp_plan_query")
     return {f: getattr(s, f) for f, _ in PlanSizes._fields_}
 
 
 def tdp_plan(grid, tiling, cond_pos=None, normalize_positions=True, world_size=1,
-             rank=0) -> Plan:
+             rank=0, assignment="round_robin") -> Plan:
     """Query sizes, allocate the host arrays and fill them (host only)."""
-    d, _keep = _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank)
+    d, _keep = _desc(grid, tiling, cond_pos, normalize_positions, world_size, rank, assignment)
     s = PlanSizes()
     _check(lib().tdp_plan_query(C.byref(d), C.byref(s)), "tdp_plan_query")
     T, R, M = s.n_tiles_local, s.n_rows, d.n_cond
