@@ -385,28 +385,35 @@ def sp_bench(world: int, reps: int = 20) -> dict:
                        wk=np.ascontiguousarray(inp.wk[:, cols]),
                        wv=np.ascontiguousarray(inp.wv[:, cols]),
                        wo=np.ascontiguousarray(inp.wo[cols]))
-    st = TdpStep(share)
     stream = torch.cuda.current_stream()
-    st.gather()
-    st.attn_prepare()
-    for _ in range(3):
-        st.attn_qkv()
-        st.attn_core()
-        st.attn_out()
-    torch.cuda.synchronize()
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)] for n in ("qkv", "core", "out")}
-    for i in range(reps):
-        for n, fn in (("qkv", st.attn_qkv), ("core", st.attn_core), ("out", st.attn_out)):
-            ev[n][i][0].record(stream)
-            fn()
-            ev[n][i][1].record(stream)
-    torch.cuda.synchronize()
-    ms = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
     T = wl.n_gen
     flops = 4.0 * d * hw * T * T
+
+    def share_ms(kv_splits):
+        st = TdpStep(share, kv_splits=kv_splits)
+        st.gather()
+        st.attn_prepare()
+        for _ in range(3):
+            st.attn_qkv()
+            st.attn_core()
+            st.attn_out()
+        torch.cuda.synchronize()
+        ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)] for n in ("qkv", "core", "out")}
+        for i in range(reps):
+            for n, fn in (("qkv", st.attn_qkv), ("core", st.attn_core), ("out", st.attn_out)):
+                ev[n][i][0].record(stream)
+                fn()
+                ev[n][i][1].record(stream)
+        torch.cuda.synchronize()
+        return {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
+
+    # the automatic choice splits the keys of this launch (few query blocks);
+    # the unsplit core is timed beside it
+    ms = share_ms(0)
+    ms_unsplit = share_ms(1)
     core_tf = flops / (ms["core"] * 1e-3) / 1e12
-    st = None
+    core_tf1 = flops / (ms_unsplit["core"] * 1e-3) / 1e12
     # the exchange: this rank's slice of Q, K, V (all heads) to every rank's
     # buffer, and the output back; every buffer in this GPU's memory
     t_loc = T // world
@@ -436,7 +443,10 @@ def sp_bench(world: int, reps: int = 20) -> dict:
     return {"workload": wl.name, "tokens": T, "world": world, "heads_per_rank": hw,
             "share_ms": {k: v for k, v in ms.items()},
             "share_core": {"achieved": core_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": core_tf / PEAK_BF16_TFLOPS, "flops_per_launch": flops},
+                           "frac": core_tf / PEAK_BF16_TFLOPS, "flops_per_launch": flops,
+                           "kv_splits": "automatic (key parts + combine)"},
+            "share_core_unsplit": {"ms": ms_unsplit["core"], "achieved": core_tf1,
+                                   "frac": core_tf1 / PEAK_BF16_TFLOPS},
             "exchange": {"bytes_per_launch": nbytes, "send_ms": send_ms,
                          "gather_ms": gather_ms,
                          "send_gbs": nbytes / (send_ms * 1e-3) / 1e9,

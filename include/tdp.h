@@ -190,6 +190,15 @@ typedef struct {
   int32_t x_dtype;            /* dtype of x_tiles and x_audio (TDP_F32/TDP_BF16)  */
   int32_t y_dtype;            /* dtype of y_tiles                                 */
   float rope_base;            /* > 0; 10000 in the workloads                      */
+  int32_t kv_splits;          /* 0: chosen from the launch size; 1: never split;
+                               * 2..8: the keys of every query block of the core
+                               * are split into this many parts, each part's
+                               * partial softmax sums (fp32, in the workspace) are
+                               * combined afterwards.  Splitting fills the GPU
+                               * when there are few query blocks (the sequence-
+                               * parallel share: all tokens, few heads).  0 splits
+                               * only such launches; self-attention launches of
+                               * 256 or more query blocks (d = 128) never split. */
 } tdp_attn_desc;
 
 /* Workspace bytes tdp_tile_attention needs for these sizes.  Errors as

@@ -222,6 +222,32 @@ def test_attention_validation():
                                None) == -1
 
 
+def test_attention_kv_splits_field():
+    """kv_splits: 0..8 accepted, others rejected; forced parts add their fp32
+    partial results to the workspace; the automatic choice never splits a
+    launch that already fills the GPU and splits the sequence-parallel share
+    (one 6144-row tile, 4 heads of 128: 96 query blocks) into 2 parts."""
+    L = tdp.lib()
+    n = ctypes.c_size_t()
+
+    def ws(heads, hd, T, R, k):
+        d = tdp.attn_desc(1, 128, heads, hd, 0, 0, 0, 10000.0, k)
+        st = L.tdp_tile_attention_workspace(ctypes.byref(d), T, R, ctypes.byref(n))
+        return st if st else n.value
+    for bad in (-1, 9, 100):
+        assert ws(2, 64, 4, 800, bad) == -2
+    one = ws(4, 128, 1, 6144, 1)
+    eight = ws(4, 128, 1, 6144, 8)
+    parts = 96 * 8 * 256                               # slots x parts x rows
+    assert eight - one >= parts * (128 * 4 + 8)
+    assert eight - one < parts * (128 * 4 + 8) + 1024
+    two = ws(4, 128, 1, 6144, 2)
+    assert two - one >= 96 * 2 * 256 * (128 * 4 + 8)
+    assert ws(4, 128, 1, 6144, 0) == two               # automatic: 2 parts
+    big = dict(heads=32, hd=128, T=16, R=16 * 4096)    # 16 tiles of 4096 rows, 32 heads
+    assert ws(k=0, **big) == ws(k=1, **big)            # automatic: unsplit
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(tdp, "_lib", None)
     monkeypatch.setattr(tdp, "LIB_PATH", str(tmp_path / "nope.so"))

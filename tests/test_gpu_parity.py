@@ -186,6 +186,35 @@ def test_stage_split_equals_fused_call():
     assert torch.equal(fused, s.y_tiles)
 
 
+# --------------------------------------------------------------------------
+# key-split core: the keys of each query block in parts, combined after
+# --------------------------------------------------------------------------
+
+SPLIT_CASES = {
+    # the unsplit kernel on a small launch (the automatic choice would split)
+    "tiny_unsplit": ("tiny_2x16x16", {}, 1),
+    "tiny_2": ("tiny_2x16x16", {}, 2),
+    # more parts than key blocks: empty parts are skipped by the combine
+    "tiny_8": ("tiny_2x16x16", {}, 8),
+    "d64_3": ("d64_8x32x32", {}, 3),
+    # two key segments (tile, then audio), audio queries, ragged lengths
+    "odd_ragged_audio_3": ("tiny_2x16x16", EDGE_CASES["odd_ragged_audio_d128"], 3),
+    "3d_tiles_d64_5": ("d64_8x32x32", EDGE_CASES["3d_tiles_d64"], 5),
+    "remainder_rows_2": ("tiny_2x16x16", EDGE_CASES["remainder_rows"], 2),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_attention_key_split(case):
+    base, kw, k = SPLIT_CASES[case]
+    kw = {key: v for key, v in kw.items() if key != "base"}
+    say("key split", case, "parts", k)
+    inp = _variant(base, **kw) if kw else ti.make_inputs(base)
+    s = _step(inp, kv_splits=k)
+    s.run()
+    _check_full(inp, s)
+
+
 def _sample_rows(p, t, rng, k):
     r0, r1 = int(p.tile_row_begin[t]), int(p.tile_row_begin[t + 1])
     n = r1 - r0
@@ -341,9 +370,11 @@ def test_exact_path_when_score_bound_is_large():
     s_max = (q @ k.T).max(axis=1)
     gap = (np.linalg.norm(q, axis=1) * np.linalg.norm(k, axis=1).max() - s_max) * sl2
     assert gap.min() > 150 and np.abs(s_max * sl2).max() < 20
-    s = _step(inp)
-    s.run()
-    _check_full(inp, s)
+    for k in (0, 3):
+        say("  key parts", k)
+        s = _step(inp, kv_splits=k)
+        s.run()
+        _check_full(inp, s)
 
 
 def test_shift_free_softmax_near_its_limit():
@@ -359,9 +390,11 @@ def test_shift_free_softmax_near_its_limit():
     say("  bounds", [(round(u, 1), round(sm, 1)) for u, sm in bounds])
     assert 55.0 < max(u for u, _ in bounds) < 62.0
     assert max(sm for _, sm in bounds) > 50.0
-    s = _step(inp)
-    s.run()
-    _check_full(inp, s)
+    for k in (0, 4):
+        say("  key parts", k)
+        s = _step(inp, kv_splits=k)
+        s.run()
+        _check_full(inp, s)
 
 
 def test_shift_free_and_exact_workgroups_in_one_launch():
@@ -378,6 +411,8 @@ def test_shift_free_and_exact_workgroups_in_one_launch():
     bounds = _score_bounds(inp)
     say("  bounds", [(round(u, 1), round(sm, 1)) for u, sm in bounds])
     assert bounds[0][0] > 80.0 and bounds[1][0] < 48.0
-    s = _step(inp)
-    s.run()
-    _check_full(inp, s)
+    for k in (0, 2):
+        say("  key parts", k)
+        s = _step(inp, kv_splits=k)
+        s.run()
+        _check_full(inp, s)

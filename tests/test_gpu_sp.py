@@ -66,7 +66,7 @@ def test_exchange_bit_exact(dtype, t_loc, H, d, W):
                            slices[r].view(torch.int16 if dtype == "bf16" else torch.int32))
 
 
-def _share(inp, plan, W, r, dev_plan):
+def _share(inp, plan, W, r, dev_plan, kv_splits=0):
     """Rank r's share on the GPU: y [T][C] float32."""
     from tiled_video_diffusion_amd import tdp
     wl = inp.workload
@@ -77,7 +77,7 @@ def _share(inp, plan, W, r, dev_plan):
     wq, wk, wv = (torch.from_numpy(np.ascontiguousarray(w[:, cols])).to(bf).to("cuda:0")
                   for w in (inp.wq, inp.wk, inp.wv))
     wo = torch.from_numpy(np.ascontiguousarray(inp.wo[cols])).to(bf).to("cuda:0")
-    desc = tdp.attn_desc(1, C, H // W, d, 0, tdp.TDP_BF16, tdp.TDP_F32)
+    desc = tdp.attn_desc(1, C, H // W, d, 0, tdp.TDP_BF16, tdp.TDP_F32, kv_splits=kv_splits)
     R = plan.n_rows
     ws_bytes = tdp.tdp_tile_attention_workspace(desc, 1, R)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda:0")
@@ -141,6 +141,12 @@ def test_rank_share_first_stage_sampled():
         e = rel_err(got[rows], want)
         say(f"rank {r}: {rows.size} rows {e:.2e}")
         assert e <= TOL
+        # the automatic choice splits this launch's keys (96 query blocks);
+        # the unsplit core gives the same layer to the bf16 output rounding
+        one = _share(inp, plan, W, r, dev_plan, kv_splits=1)
+        e1, e_pair = rel_err(one[rows], want), rel_err(got, one)
+        say(f"rank {r} unsplit: {e1:.2e}, split vs unsplit (all rows) {e_pair:.2e}")
+        assert e1 <= TOL and e_pair <= 1e-2
 
 
 def test_exchange_empty_slice_is_a_no_op():

@@ -97,7 +97,36 @@ struct Layout {
   int64_t vt_cols = 0;  // columns per V^T row: the padded tile rows, then the padded audio rows
   size_t off_q = 0, off_k = 0, off_vt = 0, off_qa = 0, off_ka = 0;
   size_t off_o = 0, off_oa = 0, total = 0;
+  int32_t kv_splits = 1;             // key parts per query slot of the core
+  size_t off_op = 0, off_ml = 0;     // its partial results (kv_splits > 1)
 };
+
+constexpr int32_t kMaxKvSplits = 8;
+constexpr int64_t kCUs = 256;        // compute units of the MI355X
+
+// Core workgroups resident at once: d = 128 is held to one per CU by its
+// 131 KB of LDS; d = 64 (4 waves, 32 KB of LDS, ~128 VGPRs) fits four.
+int64_t core_resident(int head_dim) { return kCUs * (head_dim == 64 ? 4 : 1); }
+
+// Key parts per query slot when the slots alone leave compute units idle.
+// Cost of S parts, in quarter key-block times: rounds of resident workgroups
+// x (key blocks per part + 3) x 4, + 2 per part.  The 3 blocks stand for a
+// part's fixed cost (Q fragments, filling the K/V pipeline, partial stores)
+// and the 2 for its share of the combine; both are fitted to the measured
+// sequence-parallel share on the MI355X (96 query blocks of 48 key blocks:
+// 143 us unsplit, 99 us with 2 parts, 112 us with 4, 116 us with 8, the last
+// three including the combine).  At most kMaxKvSplits parts and one per key
+// block; ties keep fewer parts.
+int32_t auto_kv_splits(int64_t slots, int64_t nkb, int64_t resident) {
+  if (slots >= resident || nkb < 2) return 1;
+  auto cost = [&](int64_t s) {
+    return 4 * ceil_div(slots * s, resident) * (ceil_div(nkb, s) + 3) + 2 * s;
+  };
+  int32_t best = 1;
+  for (int32_t s = 2; s <= kMaxKvSplits && s <= nkb; ++s)
+    if (cost(s) < cost(best)) best = s;
+  return best;
+}
 
 tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, Layout *L) {
   if (!d) return TDP_ERR_NULL;
@@ -105,6 +134,7 @@ tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, 
       n_tiles > (1 << 20) || n_rows < 1 || n_rows > INT32_MAX || !(d->rope_base > 0.0f) ||
       !std::isfinite(d->rope_base))
     return TDP_ERR_ARG;
+  if (d->kv_splits < 0 || d->kv_splits > kMaxKvSplits) return TDP_ERR_ARG;
   if (d->C != kC || (d->head_dim != 64 && d->head_dim != 128)) return TDP_ERR_UNSUPPORTED;
   if ((d->x_dtype != TDP_F32 && d->x_dtype != TDP_BF16) ||
       (d->y_dtype != TDP_F32 && d->y_dtype != TDP_BF16))
@@ -136,6 +166,20 @@ tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, 
   L->off_ka = take(B * H * L->a_pad * D * 2);
   L->off_o = take(B * static_cast<size_t>(n_rows) * hidden * 2);
   L->off_oa = take(T * B * A * hidden * 2);
+  // key parts of the core, for the workspace: slots = workgroups of an
+  // unsplit launch (upper bound), key blocks of the longest tile (at most
+  // n_rows rows) + audio; the launch may take fewer parts (max_tile_rows)
+  const int rows_wg = D == 64 ? CoreShape<64>::kRowsWG : CoreShape<128>::kRowsWG;
+  const int bn = D == 64 ? CoreShape<64>::kBN : CoreShape<128>::kBN;
+  const int64_t slots = (L->npb / (kUnit / kBlk) + static_cast<int64_t>(T) * L->n_aqb) *
+                        static_cast<int64_t>(B * H) * (kUnit / rows_wg);
+  const int64_t nkb = ceil_div(n_rows, bn) + ceil_div(d->n_audio, bn);
+  L->kv_splits = d->kv_splits > 0 ? d->kv_splits : auto_kv_splits(slots, nkb, core_resident(D));
+  if (L->kv_splits > 1) {
+    const size_t parts = static_cast<size_t>(slots) * L->kv_splits * rows_wg;
+    L->off_op = take(parts * D * 4);
+    L->off_ml = take(parts * 8);
+  }
   L->total = off;
   return TDP_OK;
 }
@@ -711,7 +755,50 @@ struct CoreArgs {
   int32_t T, heads, batch, A, n_aqb, max_rows, hidden;
   const uint32_t *kmax2;      // [B][heads][T+1] float bits of the largest squared K norm
   int32_t tile_keys;           // 0: attend the second key segment only (cross-attention)
+  // Key-split launches only: S parts per query slot, the unnormalized fp32
+  // partial O [slot][S][rows per workgroup][D] and its (m, l) per row.
+  int32_t kv_splits;
+  float *op;
+  float2 *ml;
 };
+
+// What one query slot of the core covers: (batch, head), tile, first query
+// row and the number of queries from there (the caller clamps it to its
+// rows).  False when the slot holds no queries.
+struct CoreSlot {
+  int64_t bh, b, r0, pad0;
+  int32_t h, t, q0, len0, nq;
+  bool audio_q;
+};
+
+template <int kRowsWG>
+__device__ __forceinline__ bool core_slot(const CoreArgs &a, int64_t lid, CoreSlot &s) {
+  constexpr int kSplit = kUnit / kRowsWG;   // workgroups per 256-row unit
+  const int64_t item = lid / kSplit;
+  const int part = static_cast<int>(lid - item * kSplit);
+  s.bh = item / a.units_per_bh;
+  const int64_t u = item - s.bh * a.units_per_bh;
+  s.b = s.bh / a.heads;
+  s.h = static_cast<int>(s.bh - s.b * a.heads);
+  if (u < a.n_units) {
+    s.t = a.blk_tile[u * (kUnit / kBlk)];
+    if (s.t < 0) return false;
+    s.q0 = a.blk_q0[u * (kUnit / kBlk)];
+    s.audio_q = false;
+  } else {
+    const int64_t ua = u - a.n_units;
+    s.t = static_cast<int32_t>(ua / a.n_aqb);
+    s.q0 = static_cast<int32_t>((ua - static_cast<int64_t>(s.t) * a.n_aqb) * kUnit);
+    s.audio_q = true;
+  }
+  s.q0 += part * kRowsWG;
+  tile_rows(a.trb, s.t, a.n_rows, a.max_rows, &s.r0, &s.len0);
+  s.pad0 = static_cast<int64_t>(a.pad_begin[s.t]) * kBlk;
+  s.len0 = static_cast<int32_t>(min(static_cast<int64_t>(s.len0),
+                                    static_cast<int64_t>(a.pad_begin[s.t + 1]) * kBlk - s.pad0));
+  s.nq = s.audio_q ? (a.A - s.q0) : (s.len0 - s.q0);
+  return s.nq > 0;
+}
 
 // LDS staging of one kBN-key block, unpadded rows with an XOR swizzle of the
 // 16-byte chunks inside a row (the layout; the kernel declares the buffers):
@@ -929,7 +1016,7 @@ constexpr bool kPipeFor = TDP_ATTN_PIPE < 0 ? (D >= 128 && kNG == 1 && CoreShape
 // workgroup ids go to the 8 XCDs in turn; the id is remapped so each XCD
 // walks a contiguous range of work items and the workgroups sharing a tile's
 // K/V run together on one L2.
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(64 * CoreShape<D>::kWaves, 8 / (CoreShape<D>::kWaves * kNG))
 void attn_core_kernel(CoreArgs a) {
   constexpr int kBN = CoreShape<D>::kBN;
@@ -958,8 +1045,15 @@ void attn_core_kernel(CoreArgs a) {
 
   const int64_t G = gridDim.x;
   const int64_t bid = blockIdx.x;
-  const int64_t lid = (bid % 8) * (G / 8) + bid / 8;   // gridDim.x is a multiple of 8
+  int64_t lid = (bid % 8) * (G / 8) + bid / 8;   // gridDim.x is a multiple of 8
+  int sp = 0;                                    // key split of the slot (SPLIT)
+  if constexpr (SPLIT) {
+    const int64_t slot = lid / a.kv_splits;
+    sp = static_cast<int>(lid - slot * a.kv_splits);
+    lid = slot;
+  }
   if (lid >= a.total_units * kSplit) return;
+  // (the same decode as core_slot, written out: the combine uses the helper)
   const int64_t item = lid / kSplit;
   const int part = static_cast<int>(lid - item * kSplit);
   const int64_t bh = item / a.units_per_bh;
@@ -1013,6 +1107,18 @@ void attn_core_kernel(CoreArgs a) {
   const int nkb0 = a.tile_keys ? static_cast<int>(ceil_div(len0, kBN)) : 0;
   const int nkb1 = static_cast<int>(ceil_div(a.A, kBN));
   const int nkb = nkb0 + nkb1;
+  // Key blocks [jb, je) of this workgroup: all of them, or split part sp.
+  int jb = 0, je = nkb;   // (the unsplit kernel uses 0 and nkb as written)
+  if constexpr (SPLIT) {
+    jb = static_cast<int>(static_cast<int64_t>(nkb) * sp / a.kv_splits);
+    je = static_cast<int>(static_cast<int64_t>(nkb) * (sp + 1) / a.kv_splits);
+    if (jb == je) {   // an empty part: l = 0 tells the combine to skip it
+      const int64_t mrow = (lid * a.kv_splits + sp) * kCoreRowsWG;
+      for (int r = threadIdx.x; r < min(nq, kCoreRowsWG); r += blockDim.x)
+        a.ml[mrow + r] = make_float2(-INFINITY, 0.f);
+      return;
+    }
+  }
   if (nkb == 0) return;
   // padded keys this lane holds in the last block of each segment
   // real keys in the last block of each segment, and the padded keys this
@@ -1025,16 +1131,16 @@ void attn_core_kernel(CoreArgs a) {
   const DirectStage<D> ds(__builtin_amdgcn_readfirstlane(wave), lane,
                           static_cast<uint32_t>(a.vt_cols));
   const FragOffsets<D> fo(l32, hh);
-  // Block j (clamped to the last block) of the tile-then-audio key sequence,
-  // straight into an LDS buffer.
+  // Block j (clamped to the last block of the range) of the tile-then-audio
+  // key sequence, straight into an LDS buffer.
   auto load_k = [&](int j, bf16 *buf) __attribute__((always_inline)) {
-    j = min(j, nkb - 1);
+    j = min(j, (SPLIT ? je : nkb) - 1);
     const bf16 *kb = j < nkb0 ? kseg0 + static_cast<int64_t>(j) * kBN * D
                               : kseg1 + static_cast<int64_t>(j - nkb0) * kBN * D;
     ds.load_k(kb, buf);
   };
   auto load_v = [&](int j, bf16 *buf) __attribute__((always_inline)) {
-    j = min(j, nkb - 1);
+    j = min(j, (SPLIT ? je : nkb) - 1);
     const bool s0 = j < nkb0;
     ds.load_v(s0 ? vseg0 + j * kBN : vseg1 + (j - nkb0) * kBN, buf);
   };
@@ -1083,9 +1189,9 @@ void attn_core_kernel(CoreArgs a) {
       for (int i = 0; i < kDT; ++i) o[g][i] = f32x16{};
       l_run[g] = 0.f;
     }
-    load_k(0, sk0);
-    load_v(0, sv0);
-    if constexpr (kPipe) load_k(1, sk1);
+    load_k(SPLIT ? jb : 0, sk0);
+    load_v(SPLIT ? jb : 0, sv0);
+    if constexpr (kPipe) load_k(SPLIT ? jb + 1 : 1, sk1);
     loads_landed_barrier();
     if constexpr (kPipe) {
       qk_block<D, NG>(sk0, qf, sa, fo);
@@ -1185,13 +1291,14 @@ void attn_core_kernel(CoreArgs a) {
 
   auto run_half = [&](auto exact_tag, auto upper) __attribute__((always_inline)) {
     prologue();
-    for (int j = 0; j < nkb; j += 2) {
+    const int jend = SPLIT ? je : nkb;
+    for (int j = SPLIT ? jb : 0; j < jend; j += 2) {
       if constexpr (kPipe) {
         step(exact_tag, upper, P0{}, j, sa, sb);
-        if (j + 1 < nkb) step(exact_tag, upper, P1{}, j + 1, sb, sa);
+        if (j + 1 < jend) step(exact_tag, upper, P1{}, j + 1, sb, sa);
       } else {
         step(exact_tag, upper, P0{}, j, sa, sa);
-        if (j + 1 < nkb) step(exact_tag, upper, P1{}, j + 1, sa, sa);
+        if (j + 1 < jend) step(exact_tag, upper, P1{}, j + 1, sa, sa);
       }
     }
   };
@@ -1211,7 +1318,10 @@ void attn_core_kernel(CoreArgs a) {
     // l >= 2^-kNoShift here unless the inputs hold Inf or NaN; such rows
     // take the exact path too.
     bool bad = false;
-    const float pad_ones = static_cast<float>(nz0 + nz1);
+    // padded keys of the segments whose last block lies in [jb, je)
+    const float pad_ones = SPLIT ? static_cast<float>((jb < nkb0 && nkb0 <= je ? nz0 : 0) +
+                                                      (je == nkb ? nz1 : 0))
+                                 : static_cast<float>(nz0 + nz1);
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       l_run[g] -= pad_ones;
@@ -1228,6 +1338,26 @@ void attn_core_kernel(CoreArgs a) {
     for (int g = 0; g < NG; ++g) l_tot[g] = l_run[g] + __shfl_xor(l_run[g], 32);
   }
 
+  if constexpr (SPLIT) {
+    // The part's unnormalized O (fp32) and its (m, l): O_true = 2^m O.
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int row = wave * 32 * NG + 32 * g + l32;
+      if (row < nq) {
+        const int64_t prow = (lid * a.kv_splits + sp) * kCoreRowsWG + row;
+        float *dst = a.op + prow * D + 4 * hh;
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+          for (int gg = 0; gg < 4; ++gg)
+            *reinterpret_cast<float4 *>(dst + 32 * dt + 8 * gg) =
+                make_float4(o[g][dt][4 * gg + 0], o[g][dt][4 * gg + 1], o[g][dt][4 * gg + 2],
+                            o[g][dt][4 * gg + 3]);
+        if (hh == 0) a.ml[prow] = make_float2(exact ? m_run[g] : 0.f, l_tot[g]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const float inv = 1.0f / l_tot[g];
@@ -1253,6 +1383,63 @@ void attn_core_kernel(CoreArgs a) {
   }
 }
 
+
+// Key-split launches: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s with
+// m = max_s m_s, per query row of every slot, rounded to bf16 into the same
+// place as the unsplit core's output.  Parts with l = 0 hold no keys and are
+// skipped.  A workgroup takes kRPP rows of one slot, D/4 threads per row and
+// 4 columns per thread; all of a thread's loads are issued together.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(CoreArgs a) {
+  constexpr int kRowsWG = CoreShape<D>::kRowsWG;
+  constexpr int kTPR = D / 4;
+  constexpr int kRPP = 256 / kTPR;            // rows per workgroup
+  constexpr int kWGS = kRowsWG / kRPP;        // workgroups per slot
+  const int64_t slot = blockIdx.x / kWGS;
+  CoreSlot cs;
+  if (!core_slot<kRowsWG>(a, slot, cs)) return;
+  const int row = static_cast<int>(blockIdx.x % kWGS) * kRPP + static_cast<int>(threadIdx.x) / kTPR;
+  if (row >= min(cs.nq, kRowsWG)) return;
+  const int S = a.kv_splits;
+  const int c4 = threadIdx.x % kTPR;
+  const int64_t base = slot * S * kRowsWG + row;   // (part 0, this row)
+  float2 e[kMaxKvSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxKvSplits; ++s)
+    e[s] = s < S ? a.ml[base + s * kRowsWG] : make_float2(0.f, 0.f);
+  float4 v[kMaxKvSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxKvSplits; ++s)
+    v[s] = e[s].y > 0.f ? *reinterpret_cast<const float4 *>(a.op + (base + s * kRowsWG) * D + 4 * c4)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+  float m = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxKvSplits; ++s)
+    if (e[s].y > 0.f) m = fmaxf(m, e[s].x);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxKvSplits; ++s) {
+    if (!(e[s].y > 0.f)) continue;
+    const float w = __builtin_amdgcn_exp2f(e[s].x - m);
+    acc.x = fmaf(w, v[s].x, acc.x);
+    acc.y = fmaf(w, v[s].y, acc.y);
+    acc.z = fmaf(w, v[s].z, acc.z);
+    acc.w = fmaf(w, v[s].w, acc.w);
+    l = fmaf(w, e[s].y, l);
+  }
+  const float inv = 1.0f / l;
+  bf16 *dst = cs.audio_q
+      ? a.oa + (((static_cast<int64_t>(cs.t) * a.batch + cs.b) * a.heads + cs.h) * a.A + cs.q0 +
+                row) * D
+      : a.o + ((cs.b * a.heads + cs.h) * a.n_rows + cs.r0 + cs.q0 + row) * D;
+  bf16x4 o4;
+  o4[0] = static_cast<bf16>(acc.x * inv);
+  o4[1] = static_cast<bf16>(acc.y * inv);
+  o4[2] = static_cast<bf16>(acc.z * inv);
+  o4[3] = static_cast<bf16>(acc.w * inv);
+  *reinterpret_cast<bf16x4 *>(dst + 4 * c4) = o4;
+}
 
 // ---------------------------------------------------------------------------
 // out_proj
@@ -1423,10 +1610,31 @@ void launch_core(const Call &c, hipStream_t stream, bool tile_keys = true,
   a.max_rows = c.max_rows;
   a.hidden = L.hidden;
   a.kmax2 = ws_at<uint32_t>(c.ws, L.off_kmax);
-  const int64_t grid = ceil_div(a.total_units * (kUnit / CoreShape<D>::kRowsWG), 8) * 8;
-  hipLaunchKernelGGL(attn_core_kernel<D>, dim3(static_cast<uint32_t>(grid)),
-                     dim3(64 * CoreShape<D>::kWaves), 0,
-                     stream, a);
+  const int64_t slots = a.total_units * (kUnit / CoreShape<D>::kRowsWG);
+  // Cross-attention (second segment only) is never split: its keys are few.
+  // Chosen parts: as the layout's, or fewer when the longest tile
+  // (max_rows) is shorter than the layout's bound.
+  int32_t S = tile_keys ? L.kv_splits : 1;
+  if (S > 1 && c.d->kv_splits == 0) {
+    constexpr int64_t bn = CoreShape<D>::kBN;
+    const int64_t nkb = ceil_div(c.max_rows, bn) + ceil_div(c.d->n_audio, bn);
+    S = min(S, auto_kv_splits(slots, nkb, core_resident(D)));
+  }
+  if (S == 1) {
+    const int64_t grid = ceil_div(slots, 8) * 8;
+    hipLaunchKernelGGL((attn_core_kernel<D, false>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(64 * CoreShape<D>::kWaves), 0, stream, a);
+    return;
+  }
+  a.kv_splits = S;
+  a.op = ws_at<float>(c.ws, L.off_op);
+  a.ml = ws_at<float2>(c.ws, L.off_ml);
+  const int64_t grid = ceil_div(slots * S, 8) * 8;
+  hipLaunchKernelGGL((attn_core_kernel<D, true>), dim3(static_cast<uint32_t>(grid)),
+                     dim3(64 * CoreShape<D>::kWaves), 0, stream, a);
+  constexpr int64_t kCombineWGs = CoreShape<D>::kRowsWG / (256 / (D / 4));   // per slot
+  hipLaunchKernelGGL(attn_combine_kernel<D>, dim3(static_cast<uint32_t>(slots * kCombineWGs)),
+                     dim3(256), 0, stream, a);
 }
 
 }  // namespace
@@ -1464,7 +1672,11 @@ extern "C" tdp_status tdp_attn_core(const tdp_attn_desc *desc, int32_t n_tiles,
   const int64_t units = (c.L.npb / (kUnit / kBlk) + static_cast<int64_t>(n_tiles) * c.L.n_aqb) *
                         desc->batch * desc->heads;
   const int64_t rows_wg = desc->head_dim == 64 ? CoreShape<64>::kRowsWG : CoreShape<128>::kRowsWG;
-  if (ceil_div(units * (kUnit / rows_wg), 8) * 8 > INT32_MAX) return TDP_ERR_ARG;
+  const int64_t slots = units * (kUnit / rows_wg);
+  // grids: the core (slots x parts) and, split, the combine (<= 32 per slot)
+  if (ceil_div(slots * c.L.kv_splits, 8) * 8 > INT32_MAX ||
+      (c.L.kv_splits > 1 && slots * 32 > INT32_MAX))
+    return TDP_ERR_ARG;
   const hipStream_t stream = as_stream(hip_stream);
   if (desc->head_dim == 64) launch_core<64>(c, stream);
   else launch_core<128>(c, stream);

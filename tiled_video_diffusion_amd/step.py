@@ -26,7 +26,8 @@ class TdpStep:
 
     def __init__(self, inputs, normalize_positions: bool = True, world_size: int = 1,
                  rank: int = 0, device: str = "cuda:0", identity: Optional[bool] = None,
-                 rope_base: float = 10000.0, assignment: str = "round_robin"):
+                 rope_base: float = 10000.0, assignment: str = "round_robin",
+                 kv_splits: int = 0):
         wl = inputs.workload
         self.wl = wl
         self.device = torch.device(device)
@@ -67,7 +68,7 @@ class TdpStep:
             self.wv = _dev(inputs.wv, dev, torch.bfloat16)
             self.wo = _dev(inputs.wo, dev, torch.bfloat16)
             self.desc = tdp.attn_desc(B, C, wl.heads, wl.head_dim, self.n_audio, self.code,
-                                      self.code, rope_base)
+                                      self.code, rope_base, kv_splits)
             if self.n_audio:
                 self.x_audio = _dev(inputs.x_aud, dev, self.latent_dtype)
                 self.y_audio_tiles = torch.empty((p.n_tiles_local, B, self.n_audio, C),

@@ -60,7 +60,7 @@ class PlanOut(C.Structure):
 class AttnDesc(C.Structure):
     _fields_ = [("batch", C.c_int32), ("C", C.c_int32), ("heads", C.c_int32),
                 ("head_dim", C.c_int32), ("n_audio", C.c_int32), ("x_dtype", C.c_int32),
-                ("y_dtype", C.c_int32), ("rope_base", C.c_float)]
+                ("y_dtype", C.c_int32), ("rope_base", C.c_float), ("kv_splits", C.c_int32)]
 
 
 class BlockDesc(C.Structure):
@@ -289,8 +289,9 @@ def tdp_gather_tiles(x_global, dtype, batch, n_src_rows, C_, row_src, n_rows, x_
                                   n_rows, _ptr(x_tiles), _stream(stream)), "tdp_gather_tiles")
 
 
-def attn_desc(batch, C_, heads, head_dim, n_audio, x_dtype, y_dtype, rope_base=10000.0):
-    return AttnDesc(batch, C_, heads, head_dim, n_audio, x_dtype, y_dtype, rope_base)
+def attn_desc(batch, C_, heads, head_dim, n_audio, x_dtype, y_dtype, rope_base=10000.0,
+              kv_splits=0):
+    return AttnDesc(batch, C_, heads, head_dim, n_audio, x_dtype, y_dtype, rope_base, kv_splits)
 
 
 def tdp_tile_attention_workspace(desc: AttnDesc, n_tiles, n_rows) -> int:
