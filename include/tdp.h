@@ -202,7 +202,9 @@ typedef struct {
 } tdp_attn_desc;
 
 /* Workspace bytes tdp_tile_attention needs for these sizes.  Errors as
- * tdp_tile_attention's shape checks. */
+ * tdp_tile_attention's shape checks.  When desc->kv_splits asks for key parts
+ * (or 0 chooses them for a launch of few query blocks) the bytes include the
+ * parts' fp32 partial results: (query blocks x parts x rows) x (4 head_dim + 8). */
 tdp_status tdp_tile_attention_workspace(const tdp_attn_desc *desc, int32_t n_tiles,
                                         int64_t n_rows, size_t *bytes);
 
@@ -234,7 +236,8 @@ tdp_status tdp_tile_attention(const tdp_attn_desc *desc, int32_t n_tiles,
  *  prepare:  transposed weights and the tile -> 128-row block table.
  *  qkv_rope: the Q/K/V projection with RoPE, into the workspace.
  *  core:     softmax(QK^T/sqrt(d))V per tile, head and batch, into the
- *            workspace (bf16 O).
+ *            workspace (bf16 O); with key parts (desc->kv_splits), the
+ *            parts' partial sums and then their combination.
  *  out_proj: Y = O Wo into y_tiles and y_audio_tiles. */
 tdp_status tdp_attn_prepare(const tdp_attn_desc *desc, int32_t n_tiles,
                             const int64_t *tile_row_begin, int32_t max_tile_rows,

@@ -18,6 +18,7 @@
 //             softmax needs one cross-half exchange per 64-key block, and P
 //             stays in registers as the B operand of the second MFMA.
 //   out_proj  Y = O Wo on MFMA, into y_tiles / y_audio_tiles.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -109,18 +110,27 @@ constexpr int64_t kCUs = 256;        // compute units of the MI355X
 int64_t core_resident(int head_dim) { return kCUs * (head_dim == 64 ? 4 : 1); }
 
 // Key parts per query slot when the slots alone leave compute units idle.
-// Cost of S parts, in quarter key-block times: rounds of resident workgroups
-// x (key blocks per part + 3) x 4, + 2 per part.  The 3 blocks stand for a
-// part's fixed cost (Q fragments, filling the K/V pipeline, partial stores)
-// and the 2 for its share of the combine; both are fitted to the measured
-// sequence-parallel share on the MI355X (96 query blocks of 48 key blocks:
-// 143 us unsplit, 99 us with 2 parts, 112 us with 4, 116 us with 8, the last
-// three including the combine).  At most kMaxKvSplits parts and one per key
-// block; ties keep fewer parts.
+// Cost of S parts, in key-block times of a full chip:
+//   rounds x (key blocks per part + 3) x (0.70 + 0.30 f) + 1.7 x S slots / resident
+// with rounds = ceil(S slots / resident) and f = min(1, S slots / resident)
+// the share of resident workgroups a round occupies.  The 3 blocks stand for
+// a part's fixed cost (Q fragments, filling the K/V pipeline, partial
+// stores); the f term for the shader clock, which falls as more compute
+// units run MFMA (the power limit); the last term for the combine's traffic.
+// The constants are fitted to the sequence-parallel shares measured on the
+// MI355X (6144 keys, head dim 128, core + combine):
+//   96 query blocks:  1 part 143-149 us, 2 parts 99-102, 4 parts 112, 8 parts 116;
+//   192 query blocks: 1 part 167 us, 4 parts 184;
+//   48 query blocks:  1 part 140 us, 5 parts 58.
+// At most kMaxKvSplits parts and one per key block; ties keep fewer parts.
 int32_t auto_kv_splits(int64_t slots, int64_t nkb, int64_t resident) {
   if (slots >= resident || nkb < 2) return 1;
   auto cost = [&](int64_t s) {
-    return 4 * ceil_div(slots * s, resident) * (ceil_div(nkb, s) + 3) + 2 * s;
+    const double used = static_cast<double>(slots * s) / static_cast<double>(resident);
+    const double rounds = static_cast<double>(ceil_div(slots * s, resident));
+    const double t = rounds * static_cast<double>(ceil_div(nkb, s) + 3) *
+                     (0.70 + 0.30 * std::min(used, 1.0));
+    return s > 1 ? t + 1.7 * used : t;
   };
   int32_t best = 1;
   for (int32_t s = 2; s <= kMaxKvSplits && s <= nkb; ++s)
