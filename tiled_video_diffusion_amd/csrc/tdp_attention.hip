@@ -1000,7 +1000,11 @@ constexpr bool kPipeFor = TDP_ATTN_PIPE < 0 ? (D >= 128 && kNG == 1 && CoreShape
 
 // One workgroup = kWaves waves x kNG x 32 query rows of one (batch, head,
 // tile) against all keys of the tile, then the audio keys; a 256-row unit of
-// the padded row space is split over kUnit / kRowsWG workgroups.
+// the padded row space is split over kUnit / kRowsWG workgroups.  SPLIT: each
+// such query slot gets kv_splits workgroups, workgroup sp taking key blocks
+// [nkb sp / S, nkb (sp + 1) / S) of the same sequence and leaving its
+// unnormalized O and (m, l) for attn_combine_kernel; the rest is the same
+// code (the unsplit instantiation compiles as if the split did not exist).
 //
 // Per kBN-key block j the wave (1) issues the direct loads of K(j+1) and
 // V(j+1) into the LDS buffers of block j-1, (2) computes S(j) on MFMA, turns
