@@ -244,6 +244,10 @@ def test_attention_kv_splits_field():
     two = ws(4, 128, 1, 6144, 2)
     assert two - one >= 96 * 2 * 256 * (128 * 4 + 8)
     assert ws(4, 128, 1, 6144, 0) == two               # automatic: 2 parts
+    # the other measured shares: 2 heads (48 query blocks) take 5 parts,
+    # 8 heads (192 query blocks) none
+    assert ws(2, 128, 1, 6144, 0) == ws(2, 128, 1, 6144, 5)
+    assert ws(8, 128, 1, 6144, 0) == ws(8, 128, 1, 6144, 1)
     big = dict(heads=32, hd=128, T=16, R=16 * 4096)    # 16 tiles of 4096 rows, 32 heads
     assert ws(k=0, **big) == ws(k=1, **big)            # automatic: unsplit
 
