@@ -124,15 +124,17 @@ def test_rank_shares_sum_to_the_layer(W):
     assert e_full <= TOL and e_sp <= TOL
 
 
-def test_rank_share_first_stage_sampled():
-    """The 6144-token first-stage latent, 32 heads x 128 over 8 ranks: ranks 0
-    and 7 (4 heads each) on sampled rows."""
+@pytest.mark.parametrize("W", [8, 16])
+def test_rank_share_first_stage_sampled(W):
+    """The 6144-token first-stage latent, 32 heads x 128 over W ranks: the
+    first and last rank (32/W heads each) on sampled rows.  The core splits
+    the keys of these launches (2 parts at 8 ranks, 5 at 16)."""
     inp, plan, po, x, dev_plan = _setup("sp_16x16x24")
     wl = inp.workload
-    H, d, W = wl.heads, wl.head_dim, 8
+    H, d = wl.heads, wl.head_dim
     rng = np.random.default_rng(3)
     rows = np.array(sorted({0, x.shape[0] - 1} | set(rng.integers(0, x.shape[0], 14).tolist())))
-    for r in (0, 7):
+    for r in (0, W - 1):
         got = _share(inp, plan, W, r, dev_plan)
         hs = osp.head_share(H, W, r)
         cols = slice(hs.start * d, hs.stop * d)
@@ -141,7 +143,6 @@ def test_rank_share_first_stage_sampled():
         e = rel_err(got[rows], want)
         say(f"rank {r}: {rows.size} rows {e:.2e}")
         assert e <= TOL
-        # the automatic choice splits this launch's keys (96 query blocks);
         # the unsplit core gives the same layer to the bf16 output rounding
         one = _share(inp, plan, W, r, dev_plan, kv_splits=1)
         e1, e_pair = rel_err(one[rows], want), rel_err(got, one)
