@@ -223,13 +223,16 @@ def _sample_rows(p, t, rng, k):
     return np.array(sorted(picks)), r0, r1
 
 
-@pytest.mark.parametrize("name", ["t16_16x64x64", "audio_32x48x80"])
-def test_attention_full_size_sampled(name):
-    """Full-size workloads in the benchmark's launch configuration, sampled rows."""
-    say("attention sampled", name)
+@pytest.mark.parametrize("name,kv_splits", [("t16_16x64x64", 0), ("audio_32x48x80", 0),
+                                             ("t16_16x64x64", 2), ("audio_32x48x80", 3)])
+def test_attention_full_size_sampled(name, kv_splits):
+    """Full-size workloads in the benchmark's launch configuration (these
+    launches fill the GPU, so the core runs unsplit), sampled rows; then the
+    same with the key split forced."""
+    say("attention sampled", name, "key parts", kv_splits)
     inp = ti.make_inputs(name)
     wl = inp.workload
-    s = _step(inp)
+    s = _step(inp, kv_splits=kv_splits)
     s.run()
     torch.cuda.synchronize()
     p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
