@@ -24,6 +24,10 @@ namespace {
 
 constexpr int kRowsPerWg = 4;   // rows (one per wave) per RMSNorm workgroup
 constexpr float kRmsEps = 1e-6f;
+// 1: rows of 256, 1024, 2048 or 4096 features go through the register form.
+#ifndef TDP_RMS_ROWS
+#define TDP_RMS_ROWS 1
+#endif
 
 // One wave per row m (batch entry b = m / rows_per_batch):
 //   with y: x[m][:] += g * y[m][:] first (the residual add of the branch that
@@ -111,6 +115,85 @@ __global__ __launch_bounds__(64 * kRowsPerWg) void rms_mod_kernel(
     }
   }
 }
+
+// The same for D = 256 NC with the row held in registers: every load of x
+// and y is issued before the first use, and the second pass reads no x
+// again (the loop form above keeps one 16-byte load per lane in flight and
+// re-reads the row).  Same arithmetic in the same order, so the results
+// are bitwise those of rms_mod_kernel<true>.  NT: x is read and written and
+// h written with non-temporal hints (for x larger than the 256 MB
+// last-level cache, where keeping these streams out of it pays).
+template <int NC, bool NT>
+__global__ __launch_bounds__(64 * kRowsPerWg) void rms_mod_row_kernel(
+    float *__restrict__ x, int64_t M, int64_t rows_per_batch, const float *__restrict__ e,
+    const float *__restrict__ table, int32_t shift_row, const bf16 *y,
+    const float *__restrict__ ge, const float *__restrict__ gt, bf16 *h) {
+  constexpr int D = 256 * NC;
+  const int lane = threadIdx.x & 63;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * kRowsPerWg + (threadIdx.x >> 6);
+  if (m >= M) return;
+  float *xr = x + m * D;
+  const int64_t b = m / rows_per_batch;
+  const float *es = e ? e + (b * 6 + shift_row) * D : nullptr;
+  const float *ts = table ? table + static_cast<int64_t>(shift_row) * D : nullptr;
+  const float *gs = ge ? ge + b * 6 * D : nullptr;
+  const bf16 *yr = y ? y + m * D : nullptr;
+  bf16 *hr = h + m * D;
+  f32x4 v[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const f32x4 *p = reinterpret_cast<const f32x4 *>(xr + 256 * c + 4 * lane);
+    v[c] = NT ? __builtin_nontemporal_load(p) : *p;
+  }
+  float ss = 0.f;
+  if (yr) {
+    bf16x4 yv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      yv[c] = *reinterpret_cast<const bf16x4 *>(yr + 256 * c + 4 * lane);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int j = 256 * c + 4 * lane;
+      f32x4 g = {1.f, 1.f, 1.f, 1.f};
+      if (gs || gt) {
+        g = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (gs) g += *reinterpret_cast<const f32x4 *>(gs + j);
+        if (gt) g += *reinterpret_cast<const f32x4 *>(gt + j);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[c][q] = fmaf(g[q], static_cast<float>(yv[c][q]), v[c][q]);
+      f32x4 *p = reinterpret_cast<f32x4 *>(xr + j);
+      if (NT) __builtin_nontemporal_store(v[c], p);
+      else *p = v[c];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    ss = fmaf(v[c][0], v[c][0], fmaf(v[c][1], v[c][1], fmaf(v[c][2], v[c][2], fmaf(v[c][3], v[c][3], ss))));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float rs = 1.0f / sqrtf(ss / static_cast<float>(D) + kRmsEps);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j = 256 * c + 4 * lane;
+    f32x4 shift = {0.f, 0.f, 0.f, 0.f}, scale = {0.f, 0.f, 0.f, 0.f};
+    if (es) {
+      shift += *reinterpret_cast<const f32x4 *>(es + j);
+      scale += *reinterpret_cast<const f32x4 *>(es + D + j);
+    }
+    if (ts) {
+      shift += *reinterpret_cast<const f32x4 *>(ts + j);
+      scale += *reinterpret_cast<const f32x4 *>(ts + D + j);
+    }
+    bf16x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = static_cast<bf16>((v[c][q] * rs) * (1.0f + scale[q]) + shift[q]);
+    bf16x4 *p = reinterpret_cast<bf16x4 *>(hr + j);
+    if (NT) __builtin_nontemporal_store(o, p);
+    else *p = o;
+  }
+}
+
 
 // emb[b][i] = cos(tau_b w_i), emb[b][half + i] = sin(tau_b w_i),
 // w_i = 10000^(-i / half), rounded to bf16.
@@ -243,6 +326,25 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
   auto rms = [&](const float *table, int shift_row, const bf16 *y = nullptr,
                  const float *gate_e = nullptr, const float *gate_t = nullptr) {
     const dim3 grid(static_cast<uint32_t>((M + kRowsPerWg - 1) / kRowsPerWg));
+    const float *ep = table ? E : nullptr;
+    const bool nt = M * D * 4 >= (int64_t{256} << 20);   // x beyond the last-level cache
+#define TDP_RMS_ROW(NC)                                                                        \
+  if (D == 256 * NC) {                                                                         \
+    if (nt)                                                                                    \
+      hipLaunchKernelGGL((rms_mod_row_kernel<NC, true>), grid, dim3(64 * kRowsPerWg), 0,        \
+                         stream, x, M, n_rows, ep, table, shift_row, y, gate_e, gate_t, h);    \
+    else                                                                                       \
+      hipLaunchKernelGGL((rms_mod_row_kernel<NC, false>), grid, dim3(64 * kRowsPerWg), 0,       \
+                         stream, x, M, n_rows, ep, table, shift_row, y, gate_e, gate_t, h);    \
+    return launch_status();                                                                    \
+  }
+    if (TDP_RMS_ROWS) {
+      TDP_RMS_ROW(16)
+      TDP_RMS_ROW(8)
+      TDP_RMS_ROW(4)
+      TDP_RMS_ROW(1)
+    }
+#undef TDP_RMS_ROW
     if (D % 256 == 0)
       hipLaunchKernelGGL(rms_mod_kernel<true>, grid, dim3(64 * kRowsPerWg), 0, stream, x, M,
                          static_cast<int32_t>(D), n_rows, table ? E : nullptr, table, shift_row,
