@@ -632,11 +632,13 @@ struct HeadsArgs {
   const int64_t *trb;
   int64_t n_rows;
   int32_t max_rows;
+  int32_t heads_per_wg;        // heads [z h, z h + h) for blockIdx.z = z
 };
 
 // One workgroup = 128 rows of the padded row space of one batch entry (tile
 // rows: one block of the block table; TEXT: one 128-row block of the text
-// rows); thread = (row, half of the head dims).
+// rows) and heads_per_wg of the heads (blockIdx.z); thread = (row, half of
+// the head dims).
 template <int D, bool TEXT>
 __global__ __launch_bounds__(256) void rows_to_heads_kernel(HeadsArgs a) {
   constexpr int kHalf = D / 2;        // head dims per thread
@@ -709,7 +711,8 @@ __global__ __launch_bounds__(256) void rows_to_heads_kernel(HeadsArgs a) {
       }
     }
   };
-  for (int h = 0; h < a.heads; ++h) {
+  const int h_end = min(a.heads, static_cast<int>(blockIdx.z + 1) * a.heads_per_wg);
+  for (int h = static_cast<int>(blockIdx.z) * a.heads_per_wg; h < h_end; ++h) {
     const int64_t slab = b * a.heads + h;
     bf16x8 out[kHalf / 8];
     if (a.q_col >= 0) {
@@ -1819,7 +1822,13 @@ tdp_status attn_rows_to_heads(const tdp_attn_desc *desc, int32_t n_tiles, const 
   a.trb = trb;
   a.n_rows = n_rows;
   a.max_rows = max_rows;
-  const dim3 grid(static_cast<uint32_t>(text ? L.a_pad / kBlk : L.npb), desc->batch);
+  // heads split over workgroups until about 4096 of them (4 per CU are
+  // resident; each walks its heads one after another)
+  const int64_t wgs = (text ? L.a_pad / kBlk : L.npb) * desc->batch;
+  const int64_t groups = std::min<int64_t>(desc->heads, std::max<int64_t>(1, ceil_div(4096, wgs)));
+  a.heads_per_wg = static_cast<int32_t>(ceil_div(desc->heads, groups));
+  const dim3 grid(static_cast<uint32_t>(text ? L.a_pad / kBlk : L.npb), desc->batch,
+                  static_cast<uint32_t>(ceil_div(desc->heads, a.heads_per_wg)));
   if (D == 128) {
     if (text) hipLaunchKernelGGL((rows_to_heads_kernel<128, true>), grid, dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((rows_to_heads_kernel<128, false>), grid, dim3(256), 0, stream, a);
