@@ -419,3 +419,98 @@ def test_shift_free_and_exact_workgroups_in_one_launch():
         s = _step(inp, kv_splits=k)
         s.run()
         _check_full(inp, s)
+
+
+def _very_negative_inputs(head_dim, score_log2):
+    """Inputs where a few query rows score about -score_log2 (log2 units, the
+    kernel's scale log2(e)/sqrt(d)) against every real key of their tile and
+    every audio key, far below the score 0 of a key padding a block.  Tile
+    rows (129-131) and audio rows (5) are not multiples of any key block.
+
+    Construction: channel 0 holds a constant a on every token (tile rows,
+    conditioning rows and audio), channel 1 is -1 on the chosen query tokens
+    and 0 elsewhere.  In each head the last feature, which RoPE leaves
+    unrotated, is fed only by channel 0 for K (= a) and by channel 1 for Q
+    (= -Bq), so those queries score -a Bq against every key.  All other
+    weights are the workload's, scaled by 0.1, so the rest of the scores are
+    small and the Cauchy-Schwarz bound of the chosen rows stays near
+    a Bq log2(e)/sqrt(d)."""
+    base = _variant("tiny_2x16x16", grid=(2, 8, 12), tiling=((1, 0), (1, 0), (2, 4)),
+                    n_cond=3, n_cond_neg=1, n_audio=5, head_dim=head_dim, heads=2)
+    wl = base.workload
+    F, H, W = wl.grid
+    d = wl.head_dim
+    a = 8.0
+    bq = score_log2 / (a * 1.4426950408889634 / np.sqrt(d))
+    x = base.x_global.copy()
+    xa = base.x_aud.copy()
+    x[:, :, 0] = a
+    x[:, :, 1] = 0.0
+    xa[:, :, 0] = a
+    xa[:, :, 1] = 0.0
+    # (f, h, w): in both tiles (w in [4, 8)), tile 0 only, tile 1 only
+    targets = [(1 * H + 3) * W + 5, (0 * H + 2) * W + 1, (1 * H + 7) * W + 10]
+    x[:, targets, 1] = -1.0
+    wq = ti.round_to_bf16(base.wq * 0.1)
+    wk = ti.round_to_bf16(base.wk * 0.1)
+    wq[0, :] = 0.0
+    wk[1, :] = 0.0
+    for h in range(wl.heads):
+        u = h * d + d - 1
+        wq[:, u] = 0.0
+        wk[:, u] = 0.0
+        wq[1, u] = ti.round_to_bf16(np.array([bq], np.float32))[0]
+        wk[0, u] = 1.0
+    return dataclasses.replace(base, x_global=x, x_aud=xa, wq=wq, wk=wk), targets
+
+
+def _target_scores(inp, targets):
+    """Largest score (log2 units) of each target token's query against the
+    real keys of every tile holding it (tile rows and audio rows), batch 0."""
+    wl = inp.workload
+    d = wl.head_dim
+    p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    sl2 = 1.4426950408889634 / np.sqrt(d)
+    worst = -np.inf
+    for t in range(p.tile_id.size):
+        r0, r1 = int(p.tile_row_begin[t]), int(p.tile_row_begin[t + 1])
+        src = p.row_src[r0:r1]
+        seq = np.concatenate([inp.x_global[0, src], inp.x_aud[0]]).astype(np.float64)
+        ang = np.concatenate([oracle.rope_angles(p.row_pos[r0:r1], d),
+                              np.zeros((inp.x_aud.shape[1], d // 2))])
+        rows = [i for i, n in enumerate(src) if n in targets]
+        for h in range(wl.heads):
+            q = oracle.apply_rope((seq @ inp.wq)[:, h * d:(h + 1) * d], ang)
+            k = oracle.apply_rope((seq @ inp.wk)[:, h * d:(h + 1) * d], ang)
+            worst = max(worst, float((q[rows] @ k.T).max() * sl2))
+    return worst
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("score_log2,regime", [(45.0, "shift-free"), (100.0, "exact")])
+def test_queries_far_below_padded_key_scores(head_dim, score_log2, regime):
+    """Every real score of some queries lies near -45 (bound under the
+    shift-free limit 64) or -100 (bound above it: exact online softmax), far
+    below the 0 that a padded key would score.  Padded keys must weigh
+    nothing on either path, unsplit and with the keys split in parts."""
+    say("queries far below padding", head_dim, regime)
+    inp, targets = _very_negative_inputs(head_dim, score_log2)
+    worst = _target_scores(inp, targets)
+    bound = max(u for u, _ in _score_bounds(inp))
+    say(f"  largest target score {worst:.1f}, largest bound {bound:.1f}")
+    assert worst < -30.0
+    assert (bound < 64.0) if regime == "shift-free" else (bound > 64.0)
+    wl = inp.workload
+    p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    rows = np.nonzero(np.isin(p.row_src, targets))[0]
+    for k in (1, 3):
+        say("  key parts", k)
+        s = _step(inp, kv_splits=k)
+        s.run()
+        _check_full(inp, s)
+        r = oracle.step(inp)
+        yt = _np(s.y_tiles)
+        for b in range(wl.batch):
+            for i in rows:
+                e = rel_err(yt[b, i], r.y_tiles[b, i])
+                assert np.all(np.isfinite(yt[b, i])) and e <= ATTN_TOL, (b, i, e)

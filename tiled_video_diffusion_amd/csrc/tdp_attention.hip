@@ -988,6 +988,21 @@ __device__ __forceinline__ int padded_keys(int kvalid, int hh) {
   return n;
 }
 
+// Scores of keys >= kvalid (the zero rows padding a segment's last block)
+// set to -inf, so they take no part in the block maximum and get p = 0.  The
+// lane's score v of 32-key tile i belongs to key 32 i + 8 (v/4) + 4 hh + v%4.
+template <int NG, int N>
+__device__ __forceinline__ void mask_padded(f32x16 (&s)[NG][N], int kvalid, int hh) {
+  const int kv = kvalid - 4 * hh;   // compared with compile-time key offsets
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        s[g][i][v] = (32 * i + 8 * (v / 4) + v % 4 >= kv) ? -INFINITY : s[g][i][v];
+}
+
 // 1: S of block j+1 is computed while block j is exponentiated (two S sets);
 // 0: each block's S is computed in its own step (one S set; with two query
 // groups the second group's S overlaps the first group's exp).
@@ -1024,9 +1039,12 @@ constexpr bool kPipeFor = TDP_ATTN_PIPE < 0 ? (D >= 128 && kNG == 1 && CoreShape
 // else the exact online softmax for the whole workgroup.
 //
 // Keys past the end of a segment are the zero rows the QKV stage writes into
-// the padding: score exactly 0, V row 0.  They only add the bf16 weight of a
-// zero score to the row sum, once per padded key a lane holds, which is
-// taken off again.
+// the padding: score exactly 0, V row 0.  On the shift-free path each adds
+// p = 1 to the row sum of the lane holding it, taken off again after the
+// loop; when a lane's sum is then below 2^-6 of what was taken off (every
+// real score of the query far below 0), that difference has lost precision
+// and the workgroup runs the exact path instead.  The exact path masks them
+// (score -inf, p = 0).
 //
 // Work items of one (batch, head) are contiguous: the units of every tile in
 // tile order, then the audio query units of every tile.  Consecutive
@@ -1222,12 +1240,13 @@ void attn_core_kernel(CoreArgs a) {
   // softmax with a lazily moved maximum (moved only when a part's max exceeds
   // it by more than kLazy, so p <= 2^kLazy; the O rescale is rare and sits on
   // a real branch).  kvalid: keys of the part below this index are real, the
-  // rest are zero padding (score 0), whose weight the exact path takes off
-  // here; the shift-free path takes p = 1 per padded key off after the loop.
+  // rest are zero padding (score 0), which the exact path masks here (p = 0);
+  // the shift-free path takes p = 1 per padded key off after the loop.
   auto soft = [&](auto exact_tag, auto &sc, auto &pf, int kvalid) __attribute__((always_inline)) {
     constexpr bool kExact = decltype(exact_tag)::value;
     constexpr int N = sizeof(sc[0]) / sizeof(f32x16);
     if constexpr (kExact) {
+      if (kvalid < 32 * N) mask_padded<NG, N>(sc, kvalid, hh);
       float mb[NG];
       bool grow = false;
 #pragma unroll
@@ -1253,14 +1272,10 @@ void attn_core_kernel(CoreArgs a) {
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const float lsum = exp_pack<kExact, N>(sc[g], kExact ? m_run[g] : 0.f, pf[g]);
-      if constexpr (kExact) {
-        const int nz = padded_keys<32 * N>(kvalid, hh);
-        const float pz = static_cast<float>(static_cast<bf16>(__builtin_amdgcn_exp2f(-m_run[g])));
-        l_run[g] += nz > 0 ? lsum - static_cast<float>(nz) * pz : lsum;
-      } else {
-        l_run[g] += lsum;
-      }
+      // (m_run is finite here: part 0 of every block holds the block's first
+      // key, which is real; the guard keeps -inf - -inf out regardless)
+      const float m = kExact ? (m_run[g] == -INFINITY ? 0.f : m_run[g]) : 0.f;
+      l_run[g] += exp_pack<kExact, N>(sc[g], m, pf[g]);
     }
   };
 
@@ -1332,8 +1347,11 @@ void attn_core_kernel(CoreArgs a) {
   bool exact = __syncthreads_or(need_exact);
   if (!exact) {
     run(std::false_type{});
-    // l >= 2^-kNoShift here unless the inputs hold Inf or NaN; such rows
-    // take the exact path too.
+    // l >= 2^-kNoShift here unless the inputs hold Inf or NaN, or every real
+    // score of a query lies so far below 0 that taking the padded keys'
+    // weight off cancelled (a lane's sum under 2^-6 of that weight: its
+    // rounding error may then exceed 2^-11 of the result); such workgroups
+    // take the exact path, which masks the padded keys.
     bool bad = false;
     // padded keys of the segments whose last block lies in [jb, je)
     const float pad_ones = SPLIT ? static_cast<float>((jb < nkb0 && nkb0 <= je ? nz0 : 0) +
@@ -1342,6 +1360,7 @@ void attn_core_kernel(CoreArgs a) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       l_run[g] -= pad_ones;
+      bad = bad || !(l_run[g] >= 0x1p-6f * pad_ones);
       l_tot[g] = l_run[g] + __shfl_xor(l_run[g], 32);
       bad = bad || !(l_tot[g] >= 0x1p-90f);
     }
