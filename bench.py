@@ -18,8 +18,20 @@ with overlap 8, 32 heads x 128, bf16).  Prints ONE JSON line.
   blend_stress gather and blend alone on the 32x96x160 fp32 latent
                (6x10 tiles, overlap 16, identity denoiser), algorithmic bytes
                per launch over mean launch time, against 8 TB/s
-  cpu_baseline the CPU oracle (float64 NumPy) on a bounded sample of the same
-               step, scaled to a whole step by attention flops
+  legs         the same step timed on the 8x32x32 latent (4 tiles, 32 heads x
+               64) and on the audio workload (32x48x80, 2x3x4 tiles, batch 2,
+               256 audio tokens, 16 heads x 128): wall time per step, latent
+               tokens/s, per-stage times and the attention core's roofline
+  gpu_clock    the shader clock sampled (sysfs, else amd-smi / rocm-smi) while
+               the 16-tile core repeats for a few seconds after the timed
+               region, with the ROCm and HIP versions
+  cpu_baseline the CPU oracle (float64 NumPy, untuned) on a stated sample of
+               the same step: plan, gather and blend of the whole step, and the
+               denoiser on one whole tile of each distinct size (all heads and
+               batch entries) as (tile, batch, head) work items in a pool of
+               one process per host core (at most 16); the measured wall times
+               are reported, and the step's value scales the denoiser sample to
+               all tiles by attention flops
   shares       (--shares W) how the step would split over W GPUs: each rank's
                round-robin share (its real shape) timed alone on this GPU, the
                critical path (slowest rank), and each tile timed alone, from
@@ -45,10 +57,15 @@ with overlap 8, 32 heads x 128, bf16).  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import re
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -57,32 +74,280 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 CSRC = os.path.join(ROOT, "tiled_video_diffusion_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_core_t16_16x64x64_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+# Source files each kernel family is compiled from (a change in any of them
+# makes that family's recorded counters stale).
+KERNEL_SOURCES = {
+    "attn_core_kernel": ("tdp_attention.hip", "tdp_common.h"),
+    "attn_combine_kernel": ("tdp_attention.hip", "tdp_common.h"),
+    "qkv_rope_kernel": ("tdp_attention.hip", "tdp_common.h"),
+    "gemm_kernel": ("tdp_gemm.hip", "tdp_common.h", "tdp_internal.h"),
+    "gather_rows_kernel": ("tdp_gather_blend.hip", "tdp_common.h"),
+    "blend_rows_kernel": ("tdp_gather_blend.hip", "tdp_common.h"),
+    "audio_mean_kernel": ("tdp_gather_blend.hip", "tdp_common.h"),
+}
 
 
-def core_source_digest() -> str:
-    """Digest of the sources the attention core is compiled from."""
+def source_digest(kernel: str) -> str:
+    """Digest of the sources a kernel is compiled from."""
+    family = kernel.split("<")[0]
+    files = KERNEL_SOURCES.get(family, ("tdp_attention.hip", "tdp_gemm.hip",
+                                        "tdp_gather_blend.hip", "tdp_common.h"))
     h = hashlib.sha256()
-    for f in ("tdp_attention.hip", "tdp_common.h"):
+    for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def core_traffic(workload: str):
-    """HBM bytes per attention-core launch from the committed counter runs.
-
-    None unless the counters were taken on this workload from the same kernel
-    source (a changed kernel makes them stale).
-    """
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes (read, write) per launch of `kernel` on `workload` from the
+    committed counter runs (profiles/hbm_traffic.json); None unless they were
+    taken from the kernel's current sources."""
     try:
         with open(TRAFFIC_FILE) as fh:
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("source_digest") != core_source_digest():
-        return None
-    return rec.get("attn_core_bytes_per_launch")
+    for e in rec.get("entries", []):
+        if e.get("workload") == workload and e.get("kernel") == kernel:
+            if e.get("source_digest") != source_digest(kernel):
+                return None
+            return e["read_bytes"], e["write_bytes"]
+    return None
+
+
+def short_kernel_name(name: str) -> str:
+    """'void tdp::(anonymous namespace)::k<128, false>(tdp::...)' -> 'k<128, false>'."""
+    n = name.strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth = 0
+    for i, ch in enumerate(n):                 # cut the argument list at depth 0
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not n[:i].endswith("anonymous namespace"):
+            if n[i:].startswith("(anonymous"):
+                continue
+            n = n[:i]
+            break
+    return n.replace("tdp::(anonymous namespace)::", "").replace("tdp::", "").strip()
+
+
+def counters_to_json(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """Fold two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) of one bench.py run with --calibrate-copy-mib 2048 into
+    profiles/hbm_traffic.json: per kernel, the mean over its dispatches, scaled
+    by what each counter reads for the run's 2 GiB fill (writes only) and 2 GiB
+    float32 negation (reads and writes)."""
+    def per_kernel(d, counter):
+        out = {}
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        for f in files:
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter:
+                        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    f = per_kernel(fetch_dir, "FETCH_SIZE")
+    w = per_kernel(write_dir, "WRITE_SIZE")
+    mean = {k: sum(v) / len(v) for k, v in f.items()}
+    wmean = {k: sum(v) / len(v) for k, v in w.items()}
+    fill = [k for k in f if "FillFunctor" in k]
+    neg = [k for k in f if "neg" in k.lower()]
+    if len(fill) != 1 or len(neg) != 1:
+        raise SystemExit(f"calibration kernels not found (fill {fill}, negation {neg})")
+    fs = 2097152.0 / mean[neg[0]]
+    ws = 2097152.0 / wmean[fill[0]]
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        rec = {"entries": []}
+    rec["note"] = ("HBM bytes per launch: rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                   "dispatch, mean over the run's dispatches of each kernel) times 1024 "
+                   "times the scale each counter needs to read a 2 GiB float32 negation "
+                   "(FETCH_SIZE) and a 2 GiB fill (WRITE_SIZE) as their true sizes")
+    keep = [e for e in rec.get("entries", []) if e.get("workload") != workload]
+    for k in sorted(mean):
+        if k in fill or k in neg or k not in wmean:
+            continue
+        kern = short_kernel_name(k)
+        keep.append({"workload": workload, "kernel": kern, "source_digest": source_digest(kern),
+                     "dispatches": len(f[k]), "fetch_kib_raw": round(mean[k], 1),
+                     "write_kib_raw": round(wmean[k], 1), "fetch_scale": round(fs, 5),
+                     "write_scale": round(ws, 5),
+                     "read_bytes": int(round(mean[k] * 1024 * fs)),
+                     "write_bytes": int(round(wmean[k] * 1024 * ws))})
+    rec["entries"] = keep
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    return rec
+
+
+def versions() -> dict:
+    """ROCm, HIP (torch build) and amdgpu driver versions of this machine."""
+    out = {}
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            out["rocm"] = fh.read().strip()
+    except OSError:
+        out["rocm"] = None
+    try:
+        import torch
+        out["torch"] = torch.__version__
+        out["torch_hip"] = torch.version.hip
+    except Exception:
+        pass
+    try:
+        with open("/sys/module/amdgpu/version") as fh:
+            out["amdgpu_driver"] = fh.read().strip()
+    except OSError:
+        out["amdgpu_driver"] = None
+    return out
+
+
+class ClockSampler:
+    """Samples the shader (gfx) clock of the GPU at PCI address `bdf` in a
+    thread: sysfs (hwmon freq1 'sclk', else the current pp_dpm_sclk level),
+    else amd-smi / rocm-smi.  Values in MHz."""
+
+    def __init__(self, bdf: str):
+        self.bdf = bdf
+        self.samples = []
+        self.source = None
+        self.errors = []
+        self._stop = threading.Event()
+        self._thread = None
+        dev = os.path.join("/sys/bus/pci/devices", bdf)
+        self._hwmon = None
+        for h in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+            try:
+                with open(os.path.join(h, "freq1_label")) as fh:
+                    if fh.read().strip() == "sclk":
+                        self._hwmon = os.path.join(h, "freq1_input")
+            except OSError:
+                pass
+        self._dpm = os.path.join(dev, "pp_dpm_sclk")
+
+    def _sysfs(self):
+        if self._hwmon:
+            try:
+                with open(self._hwmon) as fh:
+                    return float(fh.read().strip()) / 1e6, "sysfs hwmon freq1_input (sclk)"
+            except (OSError, ValueError) as e:
+                self.errors.append(f"hwmon: {e}")
+                self._hwmon = None
+        try:
+            with open(self._dpm) as fh:
+                for line in fh:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm][Hh]z", line)
+                        if m:
+                            return float(m.group(1)), "sysfs pp_dpm_sclk (current level)"
+        except OSError:
+            pass
+        return None, None
+
+    def _smi(self):
+        cmds = (["amd-smi", "metric", "--clock", "--json"],
+                ["rocm-smi", "--showclocks", "--json"])
+        for cmd in cmds:
+            try:
+                r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+            except (OSError, subprocess.TimeoutExpired) as e:
+                self.errors.append(f"{cmd[0]}: {e}")
+                continue
+            if r.returncode != 0:
+                self.errors.append(f"{cmd[0]}: rc {r.returncode}")
+                continue
+            vals = self._parse_smi(r.stdout)
+            if vals:
+                return vals, " ".join(cmd) + " (median over the GPU's gfx clocks)"
+        return None, None
+
+    def _parse_smi(self, text):
+        """MHz values of the gfx clocks of this GPU in amd-smi / rocm-smi JSON."""
+        try:
+            data = json.loads(text)
+        except ValueError:
+            return None
+        found = []
+
+        def num(v):
+            if isinstance(v, dict):
+                v = v.get("value", v.get("clk"))
+                if isinstance(v, dict):
+                    v = v.get("value")
+            if isinstance(v, (int, float)):
+                return float(v)
+            if isinstance(v, str):
+                m = re.search(r"(\d+(?:\.\d+)?)\s*[Mm][Hh]z", v)
+                return float(m.group(1)) if m else None
+            return None
+
+        def walk(o, want):
+            if isinstance(o, dict):
+                for k, v in o.items():
+                    kl = str(k).lower()
+                    if kl.startswith("gfx") and isinstance(v, dict) and "clk" in v:
+                        x = num(v["clk"])
+                        if x:
+                            found.append(x)
+                    elif "sclk clock speed" in kl:
+                        x = num(v)
+                        if x:
+                            found.append(x)
+                    else:
+                        walk(v, want)
+            elif isinstance(o, list):
+                for v in o:
+                    walk(v, want)
+
+        gpus = data if isinstance(data, list) else [data]
+        # amd-smi lists every GPU; keep the one whose bus id matches, when given
+        chosen = [g for g in gpus if isinstance(g, dict) and
+                  self.bdf.lower() in json.dumps(g).lower()] or gpus[:1]
+        walk(chosen, None)
+        if not found:
+            return None
+        found.sort()
+        return found[len(found) // 2]
+
+    def _run(self):
+        while not self._stop.is_set():
+            v, src = self._sysfs()
+            if v is None:
+                v, src = self._smi()
+            if v is None:
+                return
+            self.source = src
+            self.samples.append(v)
+            self._stop.wait(0.02)
+
+    def __enter__(self):
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=30)
+
+    def summary(self, what: str) -> dict:
+        if not self.samples:
+            return {"mhz_median": None, "source": None, "window": what,
+                    "errors": self.errors[:4] or ["no clock source answered"]}
+        v = sorted(self.samples)
+        return {"mhz_median": v[len(v) // 2], "mhz_min": v[0], "mhz_max": v[-1],
+                "n_samples": len(v), "source": self.source, "window": what}
 
 
 def calibrate_copy(mib: int) -> None:
@@ -119,52 +384,103 @@ def blend_bytes(plan, wl) -> float:
             + 8.0 * (plan.n_dst_rows + 1))               # dst_row_begin
 
 
-def cpu_baseline(inp, plan, budget_s: float = 15.0) -> dict:
-    """Time the oracle on whole tiles until the budget is spent; scale by flops."""
-    import numpy as np
-    import oracle
-    wl = inp.workload
-    threads = len(os.sched_getaffinity(0))
+_CPU = {}
+
+
+def _cpu_init(shared: dict) -> None:
+    """Pool worker set-up: one BLAS thread per process, the sample's arrays."""
     try:
-        from threadpoolctl import threadpool_info
-        info = threadpool_info()
-        if info:
-            threads = max(int(i.get("num_threads", 0)) for i in info)
+        from threadpoolctl import threadpool_limits
+        _CPU["limit"] = threadpool_limits(1)
     except Exception:
         pass
+    _CPU.update(shared)
+
+
+def _cpu_item(item):
+    """One (tile, batch, head) work item: the oracle's tile forward restricted
+    to head h (its columns of Wq/Wk/Wv and rows of Wo), whose output is head
+    h's share of the tile's y (the output projection is a sum over heads)."""
+    import oracle
+    t, b, h = item
+    d = _CPU["head_dim"]
+    cols = slice(h * d, (h + 1) * d)
+    xa = None if _CPU["x_aud"] is None else _CPU["x_aud"][b]
+    y, ya = oracle.tile_forward(_CPU["x"][t][b], _CPU["pos"][t], xa, _CPU["wq"][:, cols],
+                                _CPU["wk"][:, cols], _CPU["wv"][:, cols], _CPU["wo"][cols],
+                                1, d)
+    return t, b, h, y, ya
+
+
+def _cpu_nop(_):
+    return os.getpid()
+
+
+def cpu_baseline(inp, plan, max_workers: int = 16, full: bool = False) -> dict:
+    """The oracle, untuned, on this host's cores, on a stated sample of the
+    step: plan + gather + blend of the whole step, and the denoiser on one
+    whole tile of each distinct row count (all heads and batch entries; every
+    tile with ``full``) as (tile, batch, head) items in a process pool."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+
+    import oracle
+    wl = inp.workload
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
     t0 = time.perf_counter()
     p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    t_plan = time.perf_counter() - t0
+    t0 = time.perf_counter()
     x_tiles = oracle.gather_tiles(inp.x_global, p)
-    t_plan_gather = time.perf_counter() - t0
-    order = np.argsort(np.diff(p.tile_row_begin))           # smallest tiles first
-    done_flops, t_tiles, n_tiles = 0.0, 0.0, 0
+    t_gather = time.perf_counter() - t0
+    rows = np.diff(p.tile_row_begin)
+    if full:
+        sample = list(range(rows.size))
+    else:
+        sample = sorted({int(np.nonzero(rows == r)[0][0]) for r in np.unique(rows)})
+    shared = {"head_dim": wl.head_dim, "wq": inp.wq, "wk": inp.wk, "wv": inp.wv, "wo": inp.wo,
+              "x_aud": inp.x_aud,
+              "x": {t: x_tiles[:, p.tile_row_begin[t]:p.tile_row_begin[t + 1]] for t in sample},
+              "pos": {t: p.row_pos[p.tile_row_begin[t]:p.tile_row_begin[t + 1]] for t in sample}}
+    items = [(t, b, h) for t in sample for b in range(wl.batch) for h in range(wl.heads)]
     y_tiles = np.zeros(x_tiles.shape, dtype=np.float64)
-    for t in order:
-        r0, r1 = int(p.tile_row_begin[t]), int(p.tile_row_begin[t + 1])
-        t1 = time.perf_counter()
-        for b in range(wl.batch):
-            xa = None if inp.x_aud is None else inp.x_aud[b]
-            y, _ = oracle.tile_forward(x_tiles[b, r0:r1], p.row_pos[r0:r1], xa, inp.wq, inp.wk,
-                                       inp.wv, inp.wo, wl.heads, wl.head_dim)
-            y_tiles[b, r0:r1] = y
-        t_tiles += time.perf_counter() - t1
-        n = (r1 - r0) + wl.n_audio
-        done_flops += 4.0 * wl.head_dim * wl.heads * wl.batch * n * n
-        n_tiles += 1
-        if t_tiles >= budget_s:
-            break
-    t1 = time.perf_counter()
+    # spawned workers (fresh interpreters: this process has initialised the
+    # GPU); a worker that dies raises BrokenProcessPool instead of hanging
+    with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
+                                initializer=_cpu_init, initargs=(shared,)) as pool:
+        list(pool.map(_cpu_nop, range(4 * workers)))     # workers up before the clock
+        t0 = time.perf_counter()
+        for t, b, h, y, ya in pool.map(_cpu_item, items):
+            r0 = p.tile_row_begin[t]
+            y_tiles[b, r0:r0 + y.shape[0]] += y
+        t_denoise = time.perf_counter() - t0
+    t0 = time.perf_counter()
     oracle.blend_tiles(y_tiles, p)
-    t_blend = time.perf_counter() - t1
-    total_flops = attn_flops(plan, wl)
-    est = t_plan_gather + t_blend + t_tiles * total_flops / done_flops
+    t_blend = time.perf_counter() - t0
+    n = rows.astype(np.float64) + wl.n_audio
+    per_tile = 4.0 * wl.head_dim * wl.heads * wl.batch * n * n
+    f_sample, f_total = float(per_tile[sample].sum()), float(per_tile.sum())
+    step_s = t_plan + t_gather + t_blend + t_denoise * f_total / f_sample
     tokens = wl.batch * wl.n_gen
-    return {"value": tokens / est, "unit": "latent tokens/s", "cores": threads,
+    what = ("all tiles" if full else
+            f"tiles {sample} (one of each of the {len(sample)} distinct row counts "
+            f"{[int(rows[t]) for t in sample]})")
+    return {"value": tokens / step_s, "unit": "latent tokens/s", "cores": workers,
             "kind": "oracle",
-            "sample": (f"float64 NumPy oracle: plan + gather + blend of the whole step, "
-                       f"denoiser on {n_tiles} of {p.tile_id.size} tiles "
-                       f"({t_tiles:.1f} s), scaled to the step by attention flops; "
-                       f"estimated {est:.1f} s per step")}
+            "sample": (f"float64 NumPy oracle, {workers} processes x 1 BLAS thread: "
+                       f"plan {t_plan:.2f} s + gather {t_gather:.2f} s + blend {t_blend:.2f} s "
+                       f"of the whole step, and the denoiser on {what}, all {wl.heads} heads "
+                       f"x {wl.batch} batch entries = {len(items)} (tile, batch, head) "
+                       f"items: {t_denoise:.1f} s measured wall time; the value scales "
+                       f"that denoiser time to the step's {rows.size} tiles by attention "
+                       f"flops ({f_total / f_sample:.2f}x): {step_s:.1f} s per step"),
+            "measured": {"plan_s": t_plan, "gather_s": t_gather, "blend_s": t_blend,
+                         "denoiser_wall_s": t_denoise, "tiles": sample,
+                         "tile_rows": [int(rows[t]) for t in sample],
+                         "work_items": len(items), "attn_flops": f_sample},
+            "step_s_scaled": step_s, "attn_flops_step": f_total}
 
 
 def shares(inp, world_size: int, reps: int = 5) -> dict:
@@ -456,6 +772,106 @@ def sp_bench(world: int, reps: int = 20) -> dict:
                                  "pointers the same copies go over the GPU links"}}
 
 
+def time_step(step, steps: int, warmup: int, stream) -> tuple:
+    """W untimed steps, then K timed ones: wall ms per step (synchronized on
+    both sides) and the mean ms of every stage from HIP events recorded on the
+    launch stream around each stage."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    names = ["gather", "prepare", "qkv", "core", "out", "blend", "audio"]
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)] for n in names}
+
+    def stage(i, name, fn):
+        ev[name][i][0].record(stream)
+        fn()
+        ev[name][i][1].record(stream)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        stage(i, "gather", step.gather)
+        if not step.identity:
+            stage(i, "prepare", step.attn_prepare)
+            stage(i, "qkv", step.attn_qkv)
+            stage(i, "core", step.attn_core)
+            stage(i, "out", step.attn_out)
+        stage(i, "blend", step.blend)
+        if step.n_audio:
+            stage(i, "audio", step.audio)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    used = ["gather", "blend"] + ([] if step.identity else ["prepare", "qkv", "core", "out"]) + \
+        (["audio"] if step.n_audio else [])
+    stage_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in used}
+    return ms_per_step, stage_ms
+
+
+def core_roofline(wl, plan, core_ms: float) -> dict:
+    flops = attn_flops(plan, wl)
+    achieved = flops / (core_ms * 1e-3) / 1e12
+    kern = f"attn_core_kernel<{wl.head_dim}, false>"
+    tr = recorded_traffic(wl.name, kern)
+    return {"kernel": kern, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": None if tr is None else tr[0] + tr[1],
+            "flops_per_launch": flops, "ms_per_launch": core_ms}
+
+
+def leg(name: str, steps: int, warmup: int) -> dict:
+    """The whole step on another workload: throughput and the core's roofline."""
+    import torch
+
+    import tdp_inputs as ti
+    from tiled_video_diffusion_amd.step import TdpStep
+
+    inp = ti.make_inputs(name)
+    wl = inp.workload
+    step = TdpStep(inp)
+    ms, stage_ms = time_step(step, steps, warmup, torch.cuda.current_stream())
+    p = step.plan
+    out = {"workload": name, "batch": wl.batch, "grid": list(wl.grid), "tiles": p.n_tiles_total,
+           "rows": p.n_rows, "heads": wl.heads, "head_dim": wl.head_dim, "n_cond": wl.n_cond,
+           "n_audio": wl.n_audio, "steps": steps, "warmup": warmup, "ms_per_step": ms,
+           "latent_tokens_per_s": wl.batch * wl.n_gen / (ms * 1e-3), "stage_ms": stage_ms,
+           "core": core_roofline(wl, p, stage_ms["core"])}
+    del step
+    torch.cuda.empty_cache()
+    return out
+
+
+def clock_window(step, seconds: float) -> dict:
+    """The core of `step` repeated for about `seconds` while a thread samples
+    the shader clock of this GPU."""
+    import torch
+
+    props = torch.cuda.get_device_properties(0)
+    bdf = "{:04x}:{:02x}:{:02x}.0".format(getattr(props, "pci_domain_id", 0),
+                                          getattr(props, "pci_bus_id", 0),
+                                          getattr(props, "pci_device_id", 0))
+    step.attn_core()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step.attn_core()
+    torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-4)
+    n = max(1, int(seconds / one))
+    with ClockSampler(bdf) as cs:
+        for i in range(n):
+            step.attn_core()
+            if i % 16 == 15:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+    out = cs.summary(f"{n} back-to-back launches of the attention core ({n * one:.1f} s) "
+                     "after the timed region")
+    out["pci_bdf"] = bdf
+    return out
+
+
 def run(args) -> dict:
     import numpy as np
     import torch
@@ -475,57 +891,22 @@ def run(args) -> dict:
     step = TdpStep(inp)
     p = step.plan
     stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
-        step.run()
-    torch.cuda.synchronize()
-
-    names = ["gather", "prepare", "qkv", "core", "out", "blend", "audio"]
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)] for n in names}
-
-    def stage(i, name, fn):
-        ev[name][i][0].record(stream)
-        fn()
-        ev[name][i][1].record(stream)
-
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        stage(i, "gather", step.gather)
-        if not step.identity:
-            stage(i, "prepare", step.attn_prepare)
-            stage(i, "qkv", step.attn_qkv)
-            stage(i, "core", step.attn_core)
-            stage(i, "out", step.attn_out)
-        stage(i, "blend", step.blend)
-        if step.n_audio:
-            stage(i, "audio", step.audio)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-
-    def mean_ms(name):
-        vals = [a.elapsed_time(b) for a, b in ev[name]]
-        return float(np.mean(vals))
-
-    used = ["gather", "blend"] + ([] if step.identity else ["prepare", "qkv", "core", "out"]) + \
-        (["audio"] if step.n_audio else [])
-    stage_ms = {n: mean_ms(n) for n in used}
+    ms_per_step, stage_ms = time_step(step, args.steps, args.warmup, stream)
     tokens = wl.batch * wl.n_gen
     value = tokens / (ms_per_step * 1e-3)
+    roofline = (core_roofline(wl, p, stage_ms["core"]) if not step.identity else None)
 
-    flops = attn_flops(p, wl)
-    core_ms = stage_ms.get("core", float("nan"))
-    achieved = flops / (core_ms * 1e-3) / 1e12
-    roofline = {"kernel": "attn_core_kernel", "bound": "mfma", "achieved": achieved,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": core_traffic(wl.name), "flops_per_launch": flops,
-                "ms_per_launch": core_ms}
+    gpu_clock = None
+    if args.clock_s > 0 and not step.identity:
+        gpu_clock = clock_window(step, args.clock_s)
+    gpu_clock = {**(gpu_clock or {}), "versions": versions()}
 
     # gather + blend stress, alone
     bs = None
     if not args.skip_blend_stress:
+        if args.workload != "blend_32x96x160":
+            step = None
+            torch.cuda.empty_cache()
         binp = ti.make_inputs("blend_32x96x160")
         bstep = TdpStep(binp)
         bwl = binp.workload
@@ -548,7 +929,20 @@ def run(args) -> dict:
                          "bytes_per_launch": gather_bytes(bstep.plan, bwl)},
               "blend": {"achieved": bb, "frac": bb / PEAK_HBM_GBS, "ms_per_launch": b_ms,
                         "bytes_per_launch": blend_bytes(bstep.plan, bwl)}}
+        # HBM bytes the counters saw (overlap rows the gather reads twice hit
+        # in cache, so its counter bytes are below the algorithmic ones)
+        for key, kern, ms in (("gather", "gather_rows_kernel<true>", g_ms),
+                              ("blend", "blend_rows_kernel<float, true>", b_ms)):
+            tr = recorded_traffic("blend_32x96x160", kern)
+            if tr is not None:
+                cb = (tr[0] + tr[1]) / (ms * 1e-3) / 1e9
+                bs[key]["counter_bytes_per_launch"] = tr[0] + tr[1]
+                bs[key]["counter_achieved"] = cb
+                bs[key]["counter_frac"] = cb / PEAK_HBM_GBS
+            else:
+                bs[key]["counter_bytes_per_launch"] = None
         del bstep
+        torch.cuda.empty_cache()
 
     out = {
         "metric": "latent tokens/s per TDP step (1 GPU); attn MFMA %; blend HBM GB/s",
@@ -563,34 +957,37 @@ def run(args) -> dict:
                    "rows": p.n_rows, "parallelism": "all tiles on one GPU"},
         "roofline": roofline,
         "stage_ms": stage_ms, "plan_ms": plan_ms,
-        "attn_mfma_frac_whole_attention": flops / (sum(stage_ms.get(n, 0.0) for n in
-                                                       ("prepare", "qkv", "core", "out")) * 1e-3)
-        / (PEAK_BF16_TFLOPS * 1e12) if not step.identity else None,
+        "attn_mfma_frac_whole_attention": attn_flops(p, wl) / (sum(stage_ms.get(n, 0.0) for n in
+                                                                   ("prepare", "qkv", "core", "out")) * 1e-3)
+        / (PEAK_BF16_TFLOPS * 1e12) if roofline else None,
+        "gpu_clock": gpu_clock,
         "blend_stress": bs,
     }
+    step = None
+    torch.cuda.empty_cache()
+    if not args.skip_legs:
+        out["legs"] = {n: leg(n, args.steps, args.warmup) for n in args.legs.split(",") if n}
     if args.calibrate_copy_mib:
-        step = None
         torch.cuda.empty_cache()
         calibrate_copy(args.calibrate_copy_mib)
         out["calibrate_copy_mib"] = args.calibrate_copy_mib
     if args.block:
-        step = None
         torch.cuda.empty_cache()
         out["block"] = block_bench(args.block, max(2, args.steps // 4), 1)
     if args.loop:
-        step = None
         torch.cuda.empty_cache()
         out["loop"] = loop_bench(args.loop, max(2, args.steps // 8), 1)
     if args.sp:
-        step = None
         torch.cuda.empty_cache()
         out["sp"] = sp_bench(args.sp)
     if args.shares:
-        step = None
         torch.cuda.empty_cache()
         out["shares"] = shares(inp, args.shares)
-    if not args.skip_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, p, args.cpu_budget)
+    if not args.skip_cpu_baseline and not wl.identity:
+        try:
+            out["cpu_baseline"] = cpu_baseline(inp, p, full=args.cpu_full)
+        except Exception as e:        # report, keep the GPU figures
+            out["cpu_baseline"] = {"value": None, "error": f"{type(e).__name__}: {e}"}
     return out
 
 
@@ -600,10 +997,20 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="t16_16x64x64")
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of oracle denoiser work in the CPU baseline sample")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="CPU baseline on every tile of the step (no scaling; minutes)")
     ap.add_argument("--skip-cpu-baseline", action="store_true")
     ap.add_argument("--skip-blend-stress", action="store_true")
+    ap.add_argument("--legs", default="d64_8x32x32,audio_32x48x80",
+                    help="other workloads whose whole step is also timed (comma list)")
+    ap.add_argument("--skip-legs", action="store_true")
+    ap.add_argument("--clock-s", type=float, default=2.0,
+                    help="seconds of repeated core launches while the shader clock is "
+                         "sampled (0: no clock window)")
+    ap.add_argument("--counters-to-json", nargs=3, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR"),
+                    help="fold two rocprofv3 --pmc output directories (FETCH_SIZE, "
+                         "WRITE_SIZE) of a bench.py run on WORKLOAD into "
+                         "profiles/hbm_traffic.json, then exit (no GPU needed)")
     ap.add_argument("--block", default="",
                     help="also time the step with the per-tile transformer block (a block "
                          "workload name, e.g. block_t16)")
@@ -620,6 +1027,10 @@ def main():
                     help="after the run, a fill and a negation of this many MiB (for scaling "
                          "HBM byte counters)")
     args = ap.parse_args()
+    if args.counters_to_json:
+        rec = counters_to_json(*args.counters_to_json)
+        print(json.dumps(rec, indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
