@@ -258,6 +258,28 @@ tdp_status tdp_attn_out_proj(const tdp_attn_desc *desc, int32_t n_tiles,
                              int64_t n_rows, void *y_tiles, float *y_audio_tiles,
                              void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * tdp_tile_attention layer with the same arguments minus the workspace, which
+ * comes from a scratch array inside the library instead.  That array has
+ * TDP_NOALLOC_SCRATCH_BYTES bytes; every GPU the library runs on holds its own
+ * copy from the first use until the process ends.  The call allocates
+ * nothing and uses the current device's copy (make the stream's device
+ * current).  Every call on one GPU shares that copy: calls that overlap on one
+ * GPU (other streams, other threads) race and give wrong results; calls in
+ * one stream are ordered.  Results equal tdp_tile_attention's bit for bit.
+ * Errors: those of tdp_tile_attention; TDP_ERR_BUFFER when
+ * tdp_tile_attention_workspace for these sizes exceeds
+ * TDP_NOALLOC_SCRATCH_BYTES (checked before any device work);
+ * TDP_ERR_HIP when the scratch address cannot be found. */
+#define TDP_NOALLOC_SCRATCH_BYTES (64u << 20)
+tdp_status tdp_tile_attention_noalloc(const tdp_attn_desc *desc, int32_t n_tiles,
+                                      const int64_t *tile_row_begin, int32_t max_tile_rows,
+                                      int64_t n_rows, const void *x_tiles,
+                                      const float *row_pos, const void *wq, const void *wk,
+                                      const void *wv, const void *wo, const void *x_audio,
+                                      void *y_tiles, float *y_audio_tiles, void *hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Blend (device) - the on-device stand-in for the multi-GPU all_reduce      */
 /* ------------------------------------------------------------------------ */

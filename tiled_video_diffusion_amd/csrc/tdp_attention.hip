@@ -20,6 +20,7 @@
 //   out_proj  Y = O Wo on MFMA, into y_tiles / y_audio_tiles.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "tdp_common.h"
@@ -1781,6 +1782,64 @@ extern "C" tdp_status tdp_tile_attention(const tdp_attn_desc *desc, int32_t n_ti
   if (s != TDP_OK) return s;
   return tdp_attn_out_proj(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, y_tiles,
                            y_audio_tiles, workspace, workspace_bytes, hip_stream);
+}
+
+// ---------------------------------------------------------------------------
+// the attention layer without a caller workspace
+// ---------------------------------------------------------------------------
+
+// Device scratch of tdp_tile_attention_noalloc: its whole workspace (weights
+// transposed, block table, K-norm maxima, Q/K/V^T, O, key-split partials).
+// Each GPU the library runs on holds its own copy for the life of the
+// process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[TDP_NOALLOC_SCRATCH_BYTES];
+
+namespace tdp {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+tdp_status scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TDP_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TDP_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return TDP_OK;
+}
+
+}  // namespace
+}  // namespace tdp
+
+extern "C" tdp_status tdp_tile_attention_noalloc(const tdp_attn_desc *desc, int32_t n_tiles,
+                                                 const int64_t *tile_row_begin,
+                                                 int32_t max_tile_rows, int64_t n_rows,
+                                                 const void *x_tiles, const float *row_pos,
+                                                 const void *wq, const void *wk, const void *wv,
+                                                 const void *wo, const void *x_audio,
+                                                 void *y_tiles, float *y_audio_tiles,
+                                                 void *hip_stream) {
+  // sizes first: a call that does not fit fails before touching the device
+  Layout L;
+  tdp_status s = make_layout(desc, n_tiles, n_rows, &L);
+  if (s != TDP_OK) return s;
+  if (L.total > static_cast<size_t>(TDP_NOALLOC_SCRATCH_BYTES)) return TDP_ERR_BUFFER;
+  void *ws = nullptr;
+  if ((s = scratch_address(&ws)) != TDP_OK) return s;
+  // every region of the workspace is rewritten by the call's own kernels
+  // (the K-norm maxima are cleared by a kernel of the prepare stage)
+  return tdp_tile_attention(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_tiles,
+                            row_pos, wq, wk, wv, wo, x_audio, y_tiles, y_audio_tiles, ws,
+                            static_cast<size_t>(TDP_NOALLOC_SCRATCH_BYTES), hip_stream);
 }
 
 // ---------------------------------------------------------------------------

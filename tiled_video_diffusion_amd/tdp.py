@@ -96,6 +96,8 @@ _SIGS = {
     "tdp_tile_attention_workspace": (_I32, [C.POINTER(AttnDesc), _I32, _I64, C.POINTER(_SZ)]),
     "tdp_tile_attention": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P, _P,
                                   _P, _P, _P, _P, _P, _SZ, _P]),
+    "tdp_tile_attention_noalloc": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P,
+                                          _P, _P, _P, _P, _P, _P, _P]),
     "tdp_attn_prepare": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P, _P,
                                 _SZ, _P]),
     "tdp_attn_qkv_rope": (_I32, [C.POINTER(AttnDesc), _I32, _P, _I32, _I64, _P, _P, _P, _P, _SZ,
@@ -309,6 +311,16 @@ def tdp_tile_attention(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_t
         _ptr(row_pos), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(x_audio), _ptr(y_tiles),
         _ptr(y_audio_tiles), _ptr(workspace), workspace_bytes, _stream(stream)),
         "tdp_tile_attention")
+
+
+def tdp_tile_attention_noalloc(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, x_tiles,
+                               row_pos, wq, wk, wv, wo, x_audio, y_tiles, y_audio_tiles,
+                               stream=None) -> None:
+    _check(lib().tdp_tile_attention_noalloc(
+        C.byref(desc), n_tiles, _ptr(tile_row_begin), max_tile_rows, n_rows, _ptr(x_tiles),
+        _ptr(row_pos), _ptr(wq), _ptr(wk), _ptr(wv), _ptr(wo), _ptr(x_audio), _ptr(y_tiles),
+        _ptr(y_audio_tiles), _stream(stream)),
+        "tdp_tile_attention_noalloc")
 
 
 def tdp_attn_prepare(desc, n_tiles, tile_row_begin, max_tile_rows, n_rows, wq, wk, wv, wo,
