@@ -416,11 +416,15 @@ def _cpu_nop(_):
     return os.getpid()
 
 
-def cpu_baseline(inp, plan, max_workers: int = 16, full: bool = False) -> dict:
-    """The oracle, untuned, on this host's cores, on a stated sample of the
-    step: plan + gather + blend of the whole step, and the denoiser on one
-    whole tile of each distinct row count (all heads and batch entries; every
-    tile with ``full``) as (tile, batch, head) items in a process pool."""
+def cpu_baseline(inp, plan, max_workers: int = 16, full: bool = False,
+                 full_budget_s: float = 45.0) -> dict:
+    """The oracle, untuned, on this host's cores: plan + gather + blend of the
+    whole step, and the denoiser as (tile, batch, head) items in a process
+    pool.  The denoiser first runs on one whole tile of each distinct row
+    count (all heads and batch entries); when the rest of the step would take
+    at most ``full_budget_s`` at that rate (or with ``full``), it then runs on
+    every tile of the step and that whole-step wall time is the result, with
+    no scaling; otherwise the sample is scaled to the step by attention flops."""
     import concurrent.futures as cf
     import multiprocessing as mp
 
@@ -436,51 +440,63 @@ def cpu_baseline(inp, plan, max_workers: int = 16, full: bool = False) -> dict:
     x_tiles = oracle.gather_tiles(inp.x_global, p)
     t_gather = time.perf_counter() - t0
     rows = np.diff(p.tile_row_begin)
-    if full:
-        sample = list(range(rows.size))
-    else:
-        sample = sorted({int(np.nonzero(rows == r)[0][0]) for r in np.unique(rows)})
+    all_tiles = list(range(rows.size))
+    sample = sorted({int(np.nonzero(rows == r)[0][0]) for r in np.unique(rows)})
+    n = rows.astype(np.float64) + wl.n_audio
+    per_tile = 4.0 * wl.head_dim * wl.heads * wl.batch * n * n
+    f_total = float(per_tile.sum())
     shared = {"head_dim": wl.head_dim, "wq": inp.wq, "wk": inp.wk, "wv": inp.wv, "wo": inp.wo,
               "x_aud": inp.x_aud,
-              "x": {t: x_tiles[:, p.tile_row_begin[t]:p.tile_row_begin[t + 1]] for t in sample},
-              "pos": {t: p.row_pos[p.tile_row_begin[t]:p.tile_row_begin[t + 1]] for t in sample}}
-    items = [(t, b, h) for t in sample for b in range(wl.batch) for h in range(wl.heads)]
-    y_tiles = np.zeros(x_tiles.shape, dtype=np.float64)
+              "x": {t: x_tiles[:, p.tile_row_begin[t]:p.tile_row_begin[t + 1]] for t in all_tiles},
+              "pos": {t: p.row_pos[p.tile_row_begin[t]:p.tile_row_begin[t + 1]]
+                      for t in all_tiles}}
+
+    def denoise(pool, tiles):
+        items = [(t, b, h) for t in tiles for b in range(wl.batch) for h in range(wl.heads)]
+        y_tiles = np.zeros(x_tiles.shape, dtype=np.float64)
+        t0 = time.perf_counter()
+        for t, b, h, y, ya in pool.map(_cpu_item, items):
+            r0 = p.tile_row_begin[t]
+            y_tiles[b, r0:r0 + y.shape[0]] += y
+        return time.perf_counter() - t0, y_tiles, len(items)
+
     # spawned workers (fresh interpreters: this process has initialised the
     # GPU); a worker that dies raises BrokenProcessPool instead of hanging
     with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn"),
                                 initializer=_cpu_init, initargs=(shared,)) as pool:
         list(pool.map(_cpu_nop, range(4 * workers)))     # workers up before the clock
-        t0 = time.perf_counter()
-        for t, b, h, y, ya in pool.map(_cpu_item, items):
-            r0 = p.tile_row_begin[t]
-            y_tiles[b, r0:r0 + y.shape[0]] += y
-        t_denoise = time.perf_counter() - t0
+        t_sample, y_tiles, n_items = denoise(pool, sample)
+        f_sample = float(per_tile[sample].sum())
+        whole = full or t_sample * (f_total - f_sample) / f_sample <= full_budget_s
+        if whole:
+            t_denoise, y_tiles, n_items = denoise(pool, all_tiles)
     t0 = time.perf_counter()
     oracle.blend_tiles(y_tiles, p)
     t_blend = time.perf_counter() - t0
-    n = rows.astype(np.float64) + wl.n_audio
-    per_tile = 4.0 * wl.head_dim * wl.heads * wl.batch * n * n
-    f_sample, f_total = float(per_tile[sample].sum()), float(per_tile.sum())
-    step_s = t_plan + t_gather + t_blend + t_denoise * f_total / f_sample
     tokens = wl.batch * wl.n_gen
-    what = ("all tiles" if full else
-            f"tiles {sample} (one of each of the {len(sample)} distinct row counts "
-            f"{[int(rows[t]) for t in sample]})")
+    head = (f"float64 NumPy oracle, {workers} processes x 1 BLAS thread: plan {t_plan:.2f} s "
+            f"+ gather {t_gather:.2f} s + blend {t_blend:.2f} s of the whole step")
+    measured = {"plan_s": t_plan, "gather_s": t_gather, "blend_s": t_blend,
+                "sample_tiles": sample, "sample_tile_rows": [int(rows[t]) for t in sample],
+                "sample_denoiser_wall_s": t_sample}
+    if whole:
+        step_s = t_plan + t_gather + t_denoise + t_blend
+        measured.update({"denoiser_wall_s": t_denoise, "tiles": rows.size,
+                         "work_items": n_items})
+        sample_txt = (f"{head}, and the denoiser on all {rows.size} tiles x {wl.heads} heads x "
+                      f"{wl.batch} batch entries = {n_items} (tile, batch, head) items: "
+                      f"{t_denoise:.1f} s; the whole step measured, {step_s:.1f} s, no scaling")
+    else:
+        step_s = t_plan + t_gather + t_blend + t_sample * f_total / f_sample
+        measured.update({"denoiser_wall_s": t_sample, "tiles": sample, "work_items": n_items})
+        sample_txt = (f"{head}, and the denoiser on tiles {sample} (one of each distinct row "
+                      f"count, {[int(rows[t]) for t in sample]}) x {wl.heads} heads x "
+                      f"{wl.batch} batch entries = {n_items} items: {t_sample:.1f} s measured; "
+                      f"scaled to the step's {rows.size} tiles by attention flops "
+                      f"({f_total / f_sample:.2f}x): {step_s:.1f} s per step")
     return {"value": tokens / step_s, "unit": "latent tokens/s", "cores": workers,
-            "kind": "oracle",
-            "sample": (f"float64 NumPy oracle, {workers} processes x 1 BLAS thread: "
-                       f"plan {t_plan:.2f} s + gather {t_gather:.2f} s + blend {t_blend:.2f} s "
-                       f"of the whole step, and the denoiser on {what}, all {wl.heads} heads "
-                       f"x {wl.batch} batch entries = {len(items)} (tile, batch, head) "
-                       f"items: {t_denoise:.1f} s measured wall time; the value scales "
-                       f"that denoiser time to the step's {rows.size} tiles by attention "
-                       f"flops ({f_total / f_sample:.2f}x): {step_s:.1f} s per step"),
-            "measured": {"plan_s": t_plan, "gather_s": t_gather, "blend_s": t_blend,
-                         "denoiser_wall_s": t_denoise, "tiles": sample,
-                         "tile_rows": [int(rows[t]) for t in sample],
-                         "work_items": len(items), "attn_flops": f_sample},
-            "step_s_scaled": step_s, "attn_flops_step": f_total}
+            "kind": "oracle", "sample": sample_txt, "whole_step_measured": whole,
+            "measured": measured, "step_s": step_s, "attn_flops_step": f_total}
 
 
 def shares(inp, world_size: int, reps: int = 5) -> dict:

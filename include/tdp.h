@@ -166,9 +166,9 @@ tdp_status tdp_gather_tiles(const void *x_global, int32_t dtype, int32_t batch,
 /* Per-tile attention (device)                                               */
 /* ------------------------------------------------------------------------ */
 
-/* The denoiser run on every tile ("What it is": every rank runs the full
- * transformer on its tiles; "When to use it": attention is quadratic in a
- * tile's token count).  It is one multi-head self-attention layer, no bias,
+/* The denoiser run on every tile ("What it is": each rank applies the whole
+ * denoising network to the tiles it holds; "When to use it": the cost of
+ * attention grows with the square of a tile's token count).  It is one multi-head self-attention layer, no bias,
  * no norm, no residual:  per tile t and batch b, with S = [tile rows ; audio
  * rows] (audio untiled, attended on every tile forward),
  *   Q = S Wq, K = S Wk, V = S Wv          (bf16 operands, fp32 accumulation)
@@ -305,8 +305,9 @@ tdp_status tdp_blend_accumulate(const void *y_tiles, int32_t dtype, int32_t batc
                                 int64_t n_dst_rows, float *y_global, int32_t accumulate,
                                 void *hip_stream);
 
-/* Audio average ("What it is": audio is processed untiled on every tile
- * forward and averaged across tiles):
+/* Audio average ("What it is": the audio stream is not cut into tiles; it
+ * enters each tile's forward pass, and the tiles' audio results are then
+ * averaged):
  *   y_audio[b][a][:] (+)= sum_t (1 / n_tiles_total) * y_audio_tiles[t][b][a][:]
  * over the n_tiles_local tiles given, in ascending t, float32.
  *  y_audio_tiles: device [n_tiles_local][batch][A][C] float32.
@@ -320,8 +321,8 @@ tdp_status tdp_audio_accumulate(const float *y_audio_tiles, int32_t n_tiles_loca
 /* Per-tile transformer block (device)                                       */
 /* ------------------------------------------------------------------------ */
 
-/* The TDP page ("What it is") has every rank run the full transformer on its
- * tiles and describes no part of it.  This library's reading is L blocks of
+/* The TDP page ("What it is") has each rank apply the whole denoising
+ * network to its tiles and describes no part of it.  This library's reading is L blocks of
  *   h = rms(x)(1 + scale_a) + shift_a;  x += gate_a * SelfAttn(h)
  *   h = rms(x);                         x += CrossAttn(h, text)
  *   h = rms(x)(1 + scale_f) + shift_f;  x += gate_f * FFN(h)

@@ -50,8 +50,9 @@ def blend_tiles(y_tiles: np.ndarray, p: Plan, n_dst: int | None = None,
 def audio_mean(y_aud_tiles: np.ndarray, n_tiles_total: int) -> np.ndarray:
     """Average of the per-tile audio outputs: ``sum_t (1/T) y_aud_t`` (float64).
 
-    TDP page, "What it is" and its warning box: audio is processed untiled on
-    every tile forward and the results are averaged across tiles.  With
+    TDP page, "What it is" and its warning box: the audio stream is not cut
+    into tiles, it enters each tile's forward pass, and the tiles' audio
+    results are averaged.  With
     several ranks each rank sums its own tiles with weight 1/T_total, so the
     sum over ranks is the mean over all tiles.
     """

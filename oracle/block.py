@@ -1,9 +1,9 @@
-"""Oracle transformer block per tile (the "full transformer" a rank runs).
+"""Oracle transformer block per tile (the whole network a rank applies).
 
 Test infrastructure (see the package docstring).  Float64 throughout.
 
-TDP page, "What it is": every rank runs the full transformer on its own
-tile(s).  The pages describe neither the transformer nor its block, so the
+TDP page, "What it is": each rank applies the whole denoising network to the
+tiles it holds.  The pages describe neither the transformer nor its block, so the
 block here is a reading, the diffusion-transformer layout with one shared
 timestep modulation ("AdaLN-single"), written out step by step:
 

@@ -3,11 +3,12 @@ projection.  Float64 throughout.
 
 Test infrastructure (see the package docstring).
 
-TDP page, "What it is": every rank runs the full transformer on its own tiles;
-"When to use it": self-attention is quadratic in a tile's token count, which is
-where the time goes.  The pages do not describe the transformer, so the
-denoiser here is one multi-head self-attention layer (a reading): no bias, no
-norm, no residual, scale 1/sqrt(d), bidirectional, no mask.
+TDP page, "What it is": each rank applies the whole denoising network to the
+tiles it holds; "When to use it": the cost of self-attention grows with the
+square of a tile's token count, and that is where the time goes.  The pages do
+not describe the transformer, so the denoiser here is one multi-head
+self-attention layer (a reading): no bias, no norm, no residual, scale
+1/sqrt(d), bidirectional, no mask.
 """
 from __future__ import annotations
 
@@ -68,7 +69,8 @@ def tile_forward(x_tile: np.ndarray, pos: np.ndarray, x_aud: Optional[np.ndarray
     """One tile's (and one batch entry's) denoiser forward.
 
     The sequence is the tile's rows followed by the audio tokens, if any.
-    TDP page, "What it is": audio is processed untiled on every tile forward.
+    TDP page, "What it is": the audio stream is not cut into tiles; it enters
+    each tile's forward pass.
     Reading used: the audio tokens join each tile's self-attention as queries
     and as keys/values, with no rotation (they have no grid position).
 

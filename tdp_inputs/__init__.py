@@ -189,7 +189,7 @@ def make_inputs(wl: Workload | str, seed: Optional[int] = None) -> Inputs:
 
 
 # ---------------------------------------------------------------------------
-# The per-tile transformer block (the "full transformer" every rank runs)
+# The per-tile transformer block (the whole network each rank applies to its tiles)
 # ---------------------------------------------------------------------------
 
 @dataclasses.dataclass(frozen=True)

@@ -354,3 +354,48 @@ def test_sp_exchange_validation():
                                ctypes.cast(bad, ctypes.POINTER(ctypes.c_void_p)), None) == -1
     assert L.tdp_sp_gather_heads(P, 1, 16, 32, 128, 4, 0, None, None) == -1
     assert L.tdp_sp_gather_heads(P, 1, 0, 32, 128, 4, 0, None, None) == 0      # empty slice
+
+
+def _declared_arg_counts():
+    """Argument count of every function declared in include/tdp.h."""
+    import re
+    text = open(tdp.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(tdp_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", text):
+        args = m.group(2).strip()
+        out[m.group(1)] = 0 if args in ("", "void") else args.count(",") + 1
+    return out
+
+
+# The calls of the boundary the hot path's design fixes (the plan, gather,
+# attention and blend of one step), with their argument counts as declared.
+# Two depart from that design, on purpose: tdp_tile_attention takes n_rows
+# (the device CSR's last entry, needed by the host to size launches without
+# a device read), and the audio mean is its own call rather than the blend
+# over a second plan.
+BOUNDARY_ARGS = {
+    "tdp_status_string": 1,
+    "tdp_plan_query": 2,
+    "tdp_plan": 3,
+    "tdp_gather_tiles": 9,
+    "tdp_tile_attention_workspace": 4,
+    "tdp_tile_attention": 17,
+    "tdp_blend_accumulate": 12,
+    "tdp_audio_accumulate": 9,
+    "tdp_balanced_tile_split": 3,
+}
+
+
+def test_boundary_calls_and_argument_counts():
+    declared = _declared_arg_counts()
+    for name, n in BOUNDARY_ARGS.items():
+        assert name in declared, name
+        assert declared[name] == n, (name, declared[name], n)
+    # the binding marshals exactly the declared arguments of every call
+    for name, n in declared.items():
+        assert len(tdp._SIGS[name][1]) == n, (name, len(tdp._SIGS[name][1]), n)
+    # the descriptor fields the departures add
+    assert [f for f, _ in tdp.AttnDesc._fields_][-1] == "kv_splits"
+    assert "assignment" in [f for f, _ in tdp.PlanDesc._fields_]
+    assert "n_gen_total" in [f for f, _ in tdp.PlanSizes._fields_]

@@ -1,5 +1,5 @@
-// The per-tile transformer block for gfx950: the "full transformer" every rank
-// runs on its tiles (TDP page, "What it is"), built as L blocks of
+// The per-tile transformer block for gfx950: the whole denoising network each
+// rank applies to its tiles (TDP page, "What it is"), built as L blocks of
 //
 //   h = rms(x) (1 + scale_a) + shift_a;  x += gate_a * SelfAttn(h)
 //   h = rms(x);                          x += CrossAttn(h, text)
