@@ -1421,6 +1421,444 @@ void attn_core_kernel(CoreArgs a) {
 }
 
 
+// ---------------------------------------------------------------------------
+// core, two query groups per wave (head dim 128, unsplit launches)
+// ---------------------------------------------------------------------------
+//
+// 4 waves x 64 queries (two groups of 32 per wave) = 256 queries of one
+// (batch, head, tile) per workgroup, 128-key blocks, one workgroup per CU and
+// so one wave per SIMD.  Each K or V^T fragment a wave reads from LDS feeds
+// the MFMAs of both its query groups: half the LDS reads per MFMA of the
+// 8-wave form, whose 1 KB per MFMA (plus the K/V staging) would exceed the
+// CU's LDS bandwidth before the MFMA rate is reached.
+//
+// With one wave per SIMD nothing else covers latency, so the block loop is a
+// software pipeline over 32-key tiles tau in a fixed instruction order (a
+// scheduling fence after each MFMA and its companions).  Iteration tau:
+//   phase 1: 16 MFMAs of O += V(tau-1) P(tau-1), with the reads of the K
+//            fragments of tile tau+1 and the exponentials of group 0 of S(tau)
+//   phase 2: 16 MFMAs of S(tau+1) = K(tau+1) Q^T, with the reads of the V
+//            fragments of tile tau+1 and the exponentials of group 1 of S(tau)
+// Fragments of a block are read in iterations 4j-1 .. 4j+2; at the start of
+// iteration 4j+3 every wave waits for its share of block j+1's direct loads
+// (issued one block earlier) and meets the others at the one barrier of the
+// block, after which block j's buffers take block j+2.  The direct loads are
+// buffer_load ... lds in inline assembly: the compiler does not track them,
+// so its waits for fragment reads stay exact.
+//
+// Softmax: the shift-free form of attn_core_kernel when the Cauchy-Schwarz
+// bound allows it; otherwise (and when taking the padded keys' weight off
+// cancelled) a plain exact online softmax, tile by tile, without the
+// pipeline.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of `bytes` bytes at `base` (wave-uniform): raw, stride 0.
+__device__ __forceinline__ i32x4 buf_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(p & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((p >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane at descriptor offset voff + soff (soff wave-uniform)
+// into LDS: the wave's 64 lanes fill the 1 KB at `lds` (wave-uniform) in
+// lane order.
+__device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                           const bf16 *lds) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16 *)lds));
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+               : "memory");
+}
+
+#ifndef TDP_ATTN_NG2
+#define TDP_ATTN_NG2 1
+#endif
+#define TDP_NG2_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
+  static_assert(D == 128, "the two-group core is built for head dim 128");
+  constexpr int kBN = 128, kKT = kBN / 32, kW = 4;
+  constexpr int kSteps = D / 16, kDT = D / 32;
+  constexpr int kRows = 256;                            // queries per workgroup
+  constexpr int kLoads = kBN * D * 2 / 1024 / kW;       // 1 KB loads per wave, K or V^T block
+  static_assert(kLoads == 8 && kDT * 2 == 8 && kSteps == 8, "loop counts below");
+  // One LDS array: K buffers 0 and 1, then V^T buffers 0 and 1.  Fragment
+  // reads address it as a per-lane byte offset plus a compile-time constant,
+  // which the LDS read carries in its immediate offset field.
+  __shared__ __attribute__((aligned(16))) bf16 smem[4 * kBN * D];
+  constexpr int kBufEl = kBN * D;
+  auto kbuf = [&](auto par) -> bf16 * { return smem + decltype(par)::value * kBufEl; };
+  auto vbuf = [&](auto par) -> bf16 * { return smem + (2 + decltype(par)::value) * kBufEl; };
+  bf16 *const sk0 = smem, *const sk1 = smem + kBufEl;
+  bf16 *const sv0 = smem + 2 * kBufEl, *const sv1 = smem + 3 * kBufEl;
+  (void)sv1;
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+
+  const int64_t G = gridDim.x;
+  const int64_t bid = blockIdx.x;
+  const int64_t lid = (bid % 8) * (G / 8) + bid / 8;   // gridDim.x is a multiple of 8
+  if (lid >= a.total_units) return;                    // one workgroup per 256-row unit
+  const int64_t bh = lid / a.units_per_bh;
+  const int64_t u = lid - bh * a.units_per_bh;
+  const int64_t b = bh / a.heads;
+  const int h = static_cast<int>(bh - b * a.heads);
+  int32_t t, q0;
+  bool audio_q;
+  if (u < a.n_units) {
+    t = a.blk_tile[u * (kUnit / kBlk)];
+    if (t < 0) return;
+    q0 = a.blk_q0[u * (kUnit / kBlk)];
+    audio_q = false;
+  } else {
+    const int64_t ua = u - a.n_units;
+    t = static_cast<int32_t>(ua / a.n_aqb);
+    q0 = static_cast<int32_t>((ua - static_cast<int64_t>(t) * a.n_aqb) * kUnit);
+    audio_q = true;
+  }
+  int64_t r0;
+  int32_t len0;
+  tile_rows(a.trb, t, a.n_rows, a.max_rows, &r0, &len0);
+  const int64_t pad0 = static_cast<int64_t>(a.pad_begin[t]) * kBlk;
+  len0 = static_cast<int32_t>(min(static_cast<int64_t>(len0),
+                                  static_cast<int64_t>(a.pad_begin[t + 1]) * kBlk - pad0));
+  const int32_t nq = audio_q ? (a.A - q0) : (len0 - q0);
+  if (nq <= 0) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+
+  // Q fragments: group g holds query row 64 wave + 32 g + l32.
+  const bf16 *qsrc = audio_q ? a.qa + ((bh * a.a_pad) + q0) * D
+                             : a.q + ((bh * a.n_pad) + pad0 + q0) * D;
+  bf16x8 qf[2][kSteps];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st)
+      qf[g][st] = *reinterpret_cast<const bf16x8 *>(qsrc + (64 * wave + 32 * g + l32) * D +
+                                                    16 * st + 8 * hh);
+
+  // key blocks: the tile's rows (segment 0), then the audio rows (segment 1)
+  const int nkb0 = a.tile_keys ? static_cast<int>(ceil_div(len0, kBN)) : 0;
+  const int nkb1 = static_cast<int>(ceil_div(a.A, kBN));
+  const int nkb = nkb0 + nkb1;
+  if (nkb == 0) return;
+  const int kvalid0 = nkb0 > 0 ? len0 - (nkb0 - 1) * kBN : kBN;
+  const int kvalid1 = nkb1 > 0 ? a.A - (nkb1 - 1) * kBN : kBN;
+  const int nz = (nkb0 > 0 ? padded_keys<kBN>(kvalid0, hh) : 0) +
+                 (nkb1 > 0 ? padded_keys<kBN>(kvalid1, hh) : 0);
+
+  // Per-lane byte offsets of the direct loads: 1 KB unit i * 4 + wave of a
+  // block, in the swizzled layouts of CoreSmem (K rows of D, V^T rows of the
+  // slab's vt_cols columns).  Unit i holds K rows (V^T rows) 16 i + 4 wave +
+  // lane / 16, whose swizzle key (row % 16) does not depend on i: unit i's
+  // offset is unit 0's plus the wave-uniform 16 i rows.
+  static_assert(2 * D == 256 && 2 * kBN == 256 && CoreSmem<D>::kCPR == 16, "16 chunks a row");
+  uint32_t koff0, voff0;
+  {
+    const int r = 4 * uwave + lane / 16, p = lane % 16;
+    koff0 = 2u * static_cast<uint32_t>(r * D + 8 * (p ^ CoreSmem<D>::ksw(r)));
+    voff0 = 2u * (static_cast<uint32_t>(r) * static_cast<uint32_t>(a.vt_cols) +
+                  static_cast<uint32_t>(8 * (p ^ CoreSmem<D>::vsw(r))));
+  }
+  const uint32_t vstep = 2u * 16u * static_cast<uint32_t>(a.vt_cols);   // bytes per 16 V^T rows
+  const bf16 *kslab0 = a.k + (bh * a.n_pad + pad0) * D;
+  const bf16 *kslab1 = a.ka + bh * a.a_pad * D;
+  const bf16 *vslab = a.vt + bh * D * a.vt_cols;
+  const uint32_t kbytes = kBN * D * 2;
+  const uint32_t vbytes = static_cast<uint32_t>(((D - 1) * a.vt_cols + kBN) * 2);
+  // Block j (clamped to the last; past it, in-range data is re-read and
+  // never used) straight into LDS: kLoads of K, then kLoads of V^T; load
+  // i < 8 is of K, 8..15 of V^T.
+  auto block_rsrc = [&](int j, i32x4 &kr, i32x4 &vr) __attribute__((always_inline)) {
+    j = min(j, nkb - 1);
+    const bool s0 = j < nkb0;
+    kr = buf_rsrc(s0 ? kslab0 + static_cast<int64_t>(j) * kBN * D
+                     : kslab1 + static_cast<int64_t>(j - nkb0) * kBN * D, kbytes);
+    vr = buf_rsrc(vslab + (s0 ? pad0 + static_cast<int64_t>(j) * kBN
+                              : a.n_pad + static_cast<int64_t>(j - nkb0) * kBN), vbytes);
+  };
+  auto load_one = [&](int i, const i32x4 &kr, const i32x4 &vr, bf16 *kb, bf16 *vb)
+      __attribute__((always_inline)) {
+    if (i < kLoads)
+      lds_load16(kr, koff0, static_cast<uint32_t>(i) * (16 * 2 * D), kb + (i * kW + uwave) * 512);
+    else
+      lds_load16(vr, voff0, static_cast<uint32_t>(i - kLoads) * vstep,
+                 vb + ((i - kLoads) * kW + uwave) * 512);
+  };
+  auto load_block = [&](int j, bf16 *kb, bf16 *vb) __attribute__((always_inline)) {
+    i32x4 kr, vr;
+    block_rsrc(j, kr, vr);
+#pragma unroll
+    for (int i = 0; i < 2 * kLoads; ++i) load_one(i, kr, vr, kb, vb);
+  };
+
+  // Cauchy-Schwarz bound of the shift-free softmax (see attn_core_kernel).
+  constexpr float kNoShift = 64.f;
+  bool need_exact = false;
+  {
+    const uint32_t *km = a.kmax2 + bh * (a.T + 1);
+    float kk = nkb0 > 0 ? __uint_as_float(km[t]) : 0.f;
+    if (nkb1 > 0) kk = fmaxf(kk, __uint_as_float(km[a.T]));
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      float qq = 0.f;
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = static_cast<float>(qf[g][st][e]);
+          qq = fmaf(x, x, qq);
+        }
+      qq += __shfl_xor(qq, 32);
+      const float ub = sqrtf(qq) * sqrtf(kk) * 1.0009765625f;
+      need_exact = need_exact || !(ub <= kNoShift);
+    }
+  }
+  bool exact = __syncthreads_or(need_exact);
+
+  const FragOffsets<D> fo(l32, hh);
+  f32x16 o[2][kDT];
+  float l_tot[2];
+  const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+
+  if (!exact) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < kDT; ++i) o[g][i] = f32x16{};
+    f32x16 sc[2][2];        // [parity of the tile][group] scores
+    bf16x8 pf[2][2][2];     // [parity][group][16-key half] bf16 P
+    bf16x8 kf[kSteps];      // K fragments of the next tile (a few live at a time)
+    bf16x8 vf[kDT][2];      // V^T fragments [32-row group of d][16-key half]
+    float lsum[2] = {0.f, 0.f};
+    float e0 = 0.f, e1 = 0.f;
+    // P and V^T of "tile -1" are zero: the first PV step adds nothing.
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int x = 0; x < 2; ++x) pf[1][g][x] = bf16x8{};
+#pragma unroll
+    for (int i = 0; i < kDT; ++i) vf[i][0] = vf[i][1] = bf16x8{};
+
+    // blocks 0 and 1 into LDS; wait for block 0 (block 1's 16 loads stay in
+    // flight); S(0) from tile 0's K fragments
+    load_block(0, sk0, sv0);
+    load_block(1, sk1, sv1);
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    lds_barrier();
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(sk0 + fo.k[st]);
+      sc[0][0] = mfma32(k8, qf[0][st], st == 0 ? f32x16{} : sc[0][0]);
+      sc[0][1] = mfma32(k8, qf[1][st], st == 0 ? f32x16{} : sc[0][1]);
+    }
+
+    // Softmax step q (0..15) of group g of S(tau): even q exponentiates
+    // scores q, q+1; odd q packs them into P and adds them to the row sum.
+    auto soft_step = [&](auto pc_tag, int g, int q) __attribute__((always_inline)) {
+      constexpr int PC = decltype(pc_tag)::value;
+      if (q % 2 == 0) {
+        e0 = __builtin_amdgcn_exp2f(sc[PC][g][q]);
+        e1 = __builtin_amdgcn_exp2f(sc[PC][g][q + 1]);
+      } else {
+        const int v = q - 1;
+        const bf16x2 pp = {static_cast<bf16>(e0), static_cast<bf16>(e1)};
+        pf[PC][g][v / 8][v % 8] = pp[0];
+        pf[PC][g][v / 8][v % 8 + 1] = pp[1];
+        lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[g], false);
+      }
+    };
+    constexpr int kLead = 3;   // K fragment reads run this many k steps ahead
+
+    // Iteration on tile tau = 4 j + T of block j (buffers of parity BP):
+    //  phase 1: O += V(tau-1) P(tau-1), each V^T fragment refilled with
+    //           tile tau's right after its last use; group 0 of P(tau);
+    //  [T = 3: wait for block j+1, barrier, block j+2's loads go out]
+    //  phase 2: S(tau+1) = K(tau+1) Q^T, K fragments read kLead steps
+    //           ahead; group 1 of P(tau).
+    auto iter = [&](auto t_tag, auto bp_tag, int j) __attribute__((always_inline)) {
+      constexpr int T = decltype(t_tag)::value;
+      constexpr int BP = decltype(bp_tag)::value;
+      constexpr int PC = T % 2, PN = 1 - PC;          // parity of tau, of tau +- 1
+      constexpr int TN = (T + 1) % kKT;               // tile index of tau + 1 in its block
+      constexpr int NBP = T == kKT - 1 ? 1 - BP : BP; // its buffers
+      const std::integral_constant<int, PC> pc{};
+      const bf16 *kc = kbuf(std::integral_constant<int, BP>{});
+      const bf16 *vc = vbuf(std::integral_constant<int, BP>{});
+      const bf16 *kn = kbuf(std::integral_constant<int, NBP>{});
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int dt = q / 4, x = (q / 2) % 2, g = q % 2;
+        o[g][dt] = mfma32(vf[dt][x], pf[PN][g][x], o[g][dt]);
+        if (g == 1)   // both groups have read vf[dt][x]: tile tau's goes in
+          vf[dt][x] = *reinterpret_cast<const bf16x8 *>(vc + 32 * dt * kBN + fo.v[T][x]);
+        soft_step(pc, 0, q);
+        if constexpr (T != kKT - 1) {
+          if (q >= 16 - 2 * kLead && q % 2 == 0)
+            kf[(q - (16 - 2 * kLead)) / 2] =
+                *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[(q - (16 - 2 * kLead)) / 2]);
+        }
+        TDP_NG2_FENCE();
+      }
+      i32x4 kr, vr;
+      if constexpr (T == kKT - 1) {
+        // block j + 1 landed (this wave's loads, then everyone's); every wave
+        // is past its reads of block j, whose buffers now take block j + 2
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        block_rsrc(j + 2, kr, vr);
+#pragma unroll
+        for (int st = 0; st < kLead; ++st)
+          kf[st] = *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[st]);
+        TDP_NG2_FENCE();
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int st = q / 2, g = q % 2;
+        sc[PN][g] = mfma32(kf[st], qf[g][st], st == 0 ? f32x16{} : sc[PN][g]);
+        if (g == 1 && st + kLead < kSteps)
+          kf[st + kLead] =
+              *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[st + kLead]);
+        soft_step(pc, 1, q);
+        if constexpr (T == kKT - 1) {
+          load_one(q, kr, vr, kbuf(std::integral_constant<int, BP>{}),
+                   vbuf(std::integral_constant<int, BP>{}));
+        }
+        TDP_NG2_FENCE();
+      }
+    };
+    auto block = [&](auto bp_tag, int j) __attribute__((always_inline)) {
+      iter(std::integral_constant<int, 0>{}, bp_tag, j);
+      iter(std::integral_constant<int, 1>{}, bp_tag, j);
+      iter(std::integral_constant<int, 2>{}, bp_tag, j);
+      iter(std::integral_constant<int, 3>{}, bp_tag, j);
+    };
+    for (int j = 0; j < nkb; j += 2) {
+      block(P0{}, j);
+      if (j + 1 < nkb) block(P1{}, j + 1);
+    }
+    // the last tile's P V (tau = 4 nkb - 1 has parity 1)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int dt = q / 4, x = (q / 2) % 2, g = q % 2;
+      o[g][dt] = mfma32(vf[dt][x], pf[1][g][x], o[g][dt]);
+    }
+    // every direct load done before the buffers are reused or the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // padded keys scored 0 (p = 1 each); see attn_core_kernel for the check
+    bool bad = false;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const float lr = lsum[g] - static_cast<float>(nz);
+      bad = bad || !(lr >= 0x1p-6f * static_cast<float>(nz));
+      l_tot[g] = lr + __shfl_xor(lr, 32);
+      bad = bad || !(l_tot[g] >= 0x1p-90f);
+    }
+    exact = __syncthreads_or(bad);
+  }
+
+  if (exact) {
+    // The exact online softmax, tile by tile (rare: a score bound above the
+    // shift-free range, or a cancelled sum).  Padded keys are masked.
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < kDT; ++i) o[g][i] = f32x16{};
+    // (the buffers are free: every wave passed the check above after its
+    // loads completed)
+    auto xblock = [&](auto par, int j) __attribute__((always_inline)) {
+      const bf16 *kb = kbuf(par), *vb = vbuf(par);
+      load_block(j + 1, kbuf(std::integral_constant<int, 1 - decltype(par)::value>{}),
+                 vbuf(std::integral_constant<int, 1 - decltype(par)::value>{}));
+      const int kvalid = (j == nkb0 - 1) ? kvalid0 : ((j == nkb - 1 && nkb1 > 0) ? kvalid1 : kBN);
+#pragma unroll
+      for (int i = 0; i < kKT; ++i) {
+        f32x16 sx[2][1];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) sx[g][0] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          const bf16x8 k8 = *reinterpret_cast<const bf16x8 *>(kb + 32 * i * D + fo.k[st]);
+          sx[0][0] = mfma32(k8, qf[0][st], sx[0][0]);
+          sx[1][0] = mfma32(k8, qf[1][st], sx[1][0]);
+        }
+        if (kvalid - 32 * i < 32) mask_padded<2, 1>(sx, kvalid - 32 * i, hh);
+        bf16x8 px[2][1][2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float mb = block_max<1>(sx[g]);
+          if (mb > m_run[g] + kLazy) {
+            const float m_new = fmaxf(m_run[g], mb);
+            const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+#pragma unroll
+            for (int dd = 0; dd < kDT; ++dd)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) o[g][dd][v] *= alpha;
+            l_run[g] *= alpha;
+            m_run[g] = m_new;
+          }
+          const float m = m_run[g] == -INFINITY ? 0.f : m_run[g];
+          l_run[g] += exp_pack<true, 1>(sx[g], m, px[g]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const bf16x8 v8 = *reinterpret_cast<const bf16x8 *>(vb + 32 * dt * kBN + fo.v[i][x]);
+            o[0][dt] = mfma32(v8, px[0][0][x], o[0][dt]);
+            o[1][dt] = mfma32(v8, px[1][0][x], o[1][dt]);
+          }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+    };
+    load_block(0, sk0, sv0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    for (int j = 0; j < nkb; j += 2) {
+      xblock(P0{}, j);
+      if (j + 1 < nkb) xblock(P1{}, j + 1);
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) l_tot[g] = l_run[g] + __shfl_xor(l_run[g], 32);
+  }
+
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float inv = 1.0f / l_tot[g];
+    const int row = 64 * wave + 32 * g + l32;
+    if (row < nq) {
+      bf16 *dst = audio_q
+          ? a.oa + (((static_cast<int64_t>(t) * a.batch + b) * a.heads + h) * a.A + q0 + row) * D
+          : a.o + ((b * a.heads + h) * a.n_rows + r0 + q0 + row) * D;
+      dst += 4 * hh;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) {
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          bf16x4 v4;
+          v4[0] = static_cast<bf16>(o[g][dt][4 * gg + 0] * inv);
+          v4[1] = static_cast<bf16>(o[g][dt][4 * gg + 1] * inv);
+          v4[2] = static_cast<bf16>(o[g][dt][4 * gg + 2] * inv);
+          v4[3] = static_cast<bf16>(o[g][dt][4 * gg + 3] * inv);
+          *reinterpret_cast<bf16x4 *>(dst + 32 * dt + 8 * gg) = v4;
+        }
+      }
+    }
+  }
+}
+
 // Key-split launches: O = sum_s 2^(m_s - m) O_s / sum_s 2^(m_s - m) l_s with
 // m = max_s m_s, per query row of every slot, rounded to bf16 into the same
 // place as the unsplit core's output.  Parts with l = 0 hold no keys and are
@@ -1659,6 +2097,12 @@ void launch_core(const Call &c, hipStream_t stream, bool tile_keys = true,
   }
   if (S == 1) {
     const int64_t grid = ceil_div(slots, 8) * 8;
+    if constexpr (D == 128 && TDP_ATTN_NG2) {
+      static_assert(CoreShape<D>::kRowsWG == 256, "one 256-query workgroup per unit");
+      hipLaunchKernelGGL((attn_core2_kernel<D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+                         stream, a);
+      return;
+    }
     hipLaunchKernelGGL((attn_core_kernel<D, false>), dim3(static_cast<uint32_t>(grid)),
                        dim3(64 * CoreShape<D>::kWaves), 0, stream, a);
     return;
