@@ -80,6 +80,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 # makes that family's recorded counters stale).
 KERNEL_SOURCES = {
     "attn_core_kernel": ("tdp_attention.hip", "tdp_common.h"),
+    "attn_core2_kernel": ("tdp_attention.hip", "tdp_common.h"),
     "attn_combine_kernel": ("tdp_attention.hip", "tdp_common.h"),
     "qkv_rope_kernel": ("tdp_attention.hip", "tdp_common.h"),
     "gemm_kernel": ("tdp_gemm.hip", "tdp_common.h", "tdp_internal.h"),
@@ -118,9 +119,44 @@ def recorded_traffic(workload: str, kernel: str):
     return None
 
 
+def _unmangle(n: str) -> str:
+    """The kernel name and template arguments of an Itanium-mangled
+    `tdp::(anonymous namespace)::k<...>` symbol, which rocprofv3 leaves mangled
+    when a template argument is bfloat16 (`DF16b`), e.g.
+    '_ZN3tdp12_GLOBAL__N_115qkv_rope_kernelIDF16bLi128ELb0EEEv...' ->
+    'qkv_rope_kernel<__bf16, 128, false>'.  Other forms come back unchanged."""
+    m = re.match(r"_ZN(?:3tdp)?(?:12_GLOBAL__N_1)?(\d+)", n)
+    if not m:
+        return n
+    ln = int(m.group(1))
+    name = n[m.end():m.end() + ln]
+    rest = n[m.end() + ln:]
+    if not rest.startswith("I"):
+        return name
+    args, i = [], 1
+    types = {"DF16b": "__bf16", "f": "float", "d": "double", "i": "int", "l": "long"}
+    while i < len(rest) and rest[i] != "E":
+        lit = re.match(r"L(b|i|l)(n?\d+)E", rest[i:])
+        if lit:
+            v = lit.group(2).replace("n", "-")
+            args.append({"0": "false", "1": "true"}[v] if lit.group(1) == "b" else v)
+            i += lit.end()
+            continue
+        for code, ty in types.items():
+            if rest.startswith(code, i):
+                args.append(ty)
+                i += len(code)
+                break
+        else:
+            return n
+    return f"{name}<{', '.join(args)}>"
+
+
 def short_kernel_name(name: str) -> str:
     """'void tdp::(anonymous namespace)::k<128, false>(tdp::...)' -> 'k<128, false>'."""
     n = name.strip()
+    if n.startswith("_Z"):
+        return _unmangle(n)
     if n.startswith("void "):
         n = n[5:]
     depth = 0
@@ -176,7 +212,7 @@ def counters_to_json(workload: str, fetch_dir: str, write_dir: str) -> dict:
                    "(FETCH_SIZE) and a 2 GiB fill (WRITE_SIZE) as their true sizes")
     keep = [e for e in rec.get("entries", []) if e.get("workload") != workload]
     for k in sorted(mean):
-        if k in fill or k in neg or k not in wmean:
+        if k in fill or k in neg or k not in wmean or k.startswith("__amd"):
             continue
         kern = short_kernel_name(k)
         keep.append({"workload": workload, "kernel": kern, "source_digest": source_digest(kern),
@@ -830,7 +866,11 @@ def time_step(step, steps: int, warmup: int, stream) -> tuple:
 def core_roofline(wl, plan, core_ms: float) -> dict:
     flops = attn_flops(plan, wl)
     achieved = flops / (core_ms * 1e-3) / 1e12
-    kern = f"attn_core_kernel<{wl.head_dim}, false>"
+    # The library runs the two-query-group kernel at head dim 128 and the
+    # one-group kernel otherwise; none of the timed workloads splits its keys
+    # (the rocprofv3 traces of each workload show the kernel launched).
+    kern = ("attn_core2_kernel<128>" if wl.head_dim == 128
+            else f"attn_core_kernel<{wl.head_dim}, false>")
     tr = recorded_traffic(wl.name, kern)
     return {"kernel": kern, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
