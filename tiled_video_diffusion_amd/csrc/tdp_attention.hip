@@ -1481,14 +1481,39 @@ __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t s
 #endif
 #define TDP_NG2_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Fragment offsets of the two-group core (128-key blocks at either head
+// dim): K row l32, head-dim chunk 2 st + hh, in CoreSmem's K swizzle; V^T
+// row l32 of a 32-row group, key chunk 4 kt + 2 u + hh, rows of 128 keys
+// swizzled by row % 16.
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
-  static_assert(D == 128, "the two-group core is built for head dim 128");
+struct Frag2 {
+  int32_t k[D / 16];
+  int32_t v[4][2];
+  __device__ Frag2(int l32, int hh) {
+    const int ks = CoreSmem<D>::ksw(l32), vs = l32 % 16;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) k[st] = l32 * D + 8 * ((2 * st + hh) ^ ks);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) v[kt][u] = l32 * 128 + 8 * ((4 * kt + 2 * u + hh) ^ vs);
+  }
+};
+
+// Head dim 128: one workgroup (and so one wave) per SIMD.  Head dim 64 needs
+// half the registers and runs two workgroups per CU.
+template <int D>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreArgs a) {
+  static_assert(D == 128 || D == 64, "the two-group core is built for head dim 64 or 128");
   constexpr int kBN = 128, kKT = kBN / 32, kW = 4;
   constexpr int kSteps = D / 16, kDT = D / 32;
   constexpr int kRows = 256;                            // queries per workgroup
   constexpr int kLoads = kBN * D * 2 / 1024 / kW;       // 1 KB loads per wave, K or V^T block
-  static_assert(kLoads == 8 && kDT * 2 == 8 && kSteps == 8, "loop counts below");
+  // MFMAs per phase of a 32-key tile: O += V P (phase 1), S = K Q^T (phase 2);
+  // each phase also takes the 16 softmax steps of one group, kR1 / kR2 per MFMA
+  constexpr int kP1 = 4 * kDT, kP2 = 2 * kSteps;
+  constexpr int kR1 = 16 / kP1, kR2 = 16 / kP2;
+  static_assert(kLoads == D / 16 && 2 * kLoads == kP2, "one direct load per phase-2 MFMA");
   // One LDS array: K buffers 0 and 1, then V^T buffers 0 and 1.  Fragment
   // reads address it as a per-lane byte offset plus a compile-time constant,
   // which the LDS read carries in its immediate offset field.
@@ -1558,17 +1583,21 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
                  (nkb1 > 0 ? padded_keys<kBN>(kvalid1, hh) : 0);
 
   // Per-lane byte offsets of the direct loads: 1 KB unit i * 4 + wave of a
-  // block, in the swizzled layouts of CoreSmem (K rows of D, V^T rows of the
-  // slab's vt_cols columns).  Unit i holds K rows (V^T rows) 16 i + 4 wave +
-  // lane / 16, whose swizzle key (row % 16) does not depend on i: unit i's
-  // offset is unit 0's plus the wave-uniform 16 i rows.
-  static_assert(2 * D == 256 && 2 * kBN == 256 && CoreSmem<D>::kCPR == 16, "16 chunks a row");
+  // block, in the swizzled layouts (K rows of D in CoreSmem's swizzle, V^T
+  // rows of 128 keys swizzled by row % 16, read from the slab's vt_cols
+  // columns).  A K unit holds kKR rows, kKR (4 i + wave) + lane / kCPR; a V^T
+  // unit 4 rows, 16 i + 4 wave + lane / 16.  Neither swizzle key depends on
+  // i, so unit i's offset is unit 0's plus a wave-uniform step: 4 KB of K,
+  // 16 V^T rows.
+  constexpr int kCPR = D / 8, kKR = 64 / kCPR;
+  static_assert(CoreSmem<D>::kCPR == kCPR, "16-byte chunks per K row");
   uint32_t koff0, voff0;
   {
-    const int r = 4 * uwave + lane / 16, p = lane % 16;
+    const int r = kKR * uwave + lane / kCPR, p = lane % kCPR;
     koff0 = 2u * static_cast<uint32_t>(r * D + 8 * (p ^ CoreSmem<D>::ksw(r)));
-    voff0 = 2u * (static_cast<uint32_t>(r) * static_cast<uint32_t>(a.vt_cols) +
-                  static_cast<uint32_t>(8 * (p ^ CoreSmem<D>::vsw(r))));
+    const int vr = 4 * uwave + lane / 16, vp = lane % 16;
+    voff0 = 2u * (static_cast<uint32_t>(vr) * static_cast<uint32_t>(a.vt_cols) +
+                  static_cast<uint32_t>(8 * (vp ^ (vr % 16))));
   }
   const uint32_t vstep = 2u * 16u * static_cast<uint32_t>(a.vt_cols);   // bytes per 16 V^T rows
   const bf16 *kslab0 = a.k + (bh * a.n_pad + pad0) * D;
@@ -1590,7 +1619,7 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
   auto load_one = [&](int i, const i32x4 &kr, const i32x4 &vr, bf16 *kb, bf16 *vb)
       __attribute__((always_inline)) {
     if (i < kLoads)
-      lds_load16(kr, koff0, static_cast<uint32_t>(i) * (16 * 2 * D), kb + (i * kW + uwave) * 512);
+      lds_load16(kr, koff0, static_cast<uint32_t>(i) * 4096u, kb + (i * kW + uwave) * 512);
     else
       lds_load16(vr, voff0, static_cast<uint32_t>(i - kLoads) * vstep,
                  vb + ((i - kLoads) * kW + uwave) * 512);
@@ -1626,7 +1655,10 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
   }
   bool exact = __syncthreads_or(need_exact);
 
-  const FragOffsets<D> fo(l32, hh);
+  // (at head dim 128 FragOffsets<128> holds the same offsets; it stays there,
+  // as the register allocation of this kernel is sensitive to its form)
+  using Frags = std::conditional_t<D == 128, FragOffsets<D>, Frag2<D>>;
+  const Frags fo(l32, hh);
   f32x16 o[2][kDT];
   float l_tot[2];
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
@@ -1654,7 +1686,8 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
     // flight); S(0) from tile 0's K fragments
     load_block(0, sk0, sv0);
     load_block(1, sk1, sv1);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    if constexpr (2 * kLoads == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     lds_barrier();
 #pragma unroll
     for (int st = 0; st < kSteps; ++st) {
@@ -1678,7 +1711,7 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
         lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[g], false);
       }
     };
-    constexpr int kLead = 3;   // K fragment reads run this many k steps ahead
+    constexpr int kLead = kSteps == 8 ? 3 : 2;   // K fragment reads run this many k steps ahead
 
     // Iteration on tile tau = 4 j + T of block j (buffers of parity BP):
     //  phase 1: O += V(tau-1) P(tau-1), each V^T fragment refilled with
@@ -1697,16 +1730,17 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
       const bf16 *vc = vbuf(std::integral_constant<int, BP>{});
       const bf16 *kn = kbuf(std::integral_constant<int, NBP>{});
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < kP1; ++q) {
         const int dt = q / 4, x = (q / 2) % 2, g = q % 2;
         o[g][dt] = mfma32(vf[dt][x], pf[PN][g][x], o[g][dt]);
         if (g == 1)   // both groups have read vf[dt][x]: tile tau's goes in
           vf[dt][x] = *reinterpret_cast<const bf16x8 *>(vc + 32 * dt * kBN + fo.v[T][x]);
-        soft_step(pc, 0, q);
+#pragma unroll
+        for (int r = 0; r < kR1; ++r) soft_step(pc, 0, kR1 * q + r);
         if constexpr (T != kKT - 1) {
-          if (q >= 16 - 2 * kLead && q % 2 == 0)
-            kf[(q - (16 - 2 * kLead)) / 2] =
-                *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[(q - (16 - 2 * kLead)) / 2]);
+          if (q >= kP1 - 2 * kLead && q % 2 == 0)
+            kf[(q - (kP1 - 2 * kLead)) / 2] =
+                *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[(q - (kP1 - 2 * kLead)) / 2]);
         }
         TDP_NG2_FENCE();
       }
@@ -1723,13 +1757,14 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
         TDP_NG2_FENCE();
       }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < kP2; ++q) {
         const int st = q / 2, g = q % 2;
         sc[PN][g] = mfma32(kf[st], qf[g][st], st == 0 ? f32x16{} : sc[PN][g]);
         if (g == 1 && st + kLead < kSteps)
           kf[st + kLead] =
               *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[st + kLead]);
-        soft_step(pc, 1, q);
+#pragma unroll
+        for (int r = 0; r < kR2; ++r) soft_step(pc, 1, kR2 * q + r);
         if constexpr (T == kKT - 1) {
           load_one(q, kr, vr, kbuf(std::integral_constant<int, BP>{}),
                    vbuf(std::integral_constant<int, BP>{}));
@@ -1749,7 +1784,7 @@ __global__ __launch_bounds__(256, 1) void attn_core2_kernel(CoreArgs a) {
     }
     // the last tile's P V (tau = 4 nkb - 1 has parity 1)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < kP1; ++q) {
       const int dt = q / 4, x = (q / 2) % 2, g = q % 2;
       o[g][dt] = mfma32(vf[dt][x], pf[1][g][x], o[g][dt]);
     }
@@ -2097,9 +2132,10 @@ void launch_core(const Call &c, hipStream_t stream, bool tile_keys = true,
   }
   if (S == 1) {
     const int64_t grid = ceil_div(slots, 8) * 8;
-    if constexpr (D == 128 && TDP_ATTN_NG2) {
-      static_assert(CoreShape<D>::kRowsWG == 256, "one 256-query workgroup per unit");
-      hipLaunchKernelGGL((attn_core2_kernel<D>), dim3(static_cast<uint32_t>(grid)), dim3(256), 0,
+    if constexpr (TDP_ATTN_NG2) {
+      // one 256-query workgroup per unit
+      const int64_t grid2 = ceil_div(a.total_units, 8) * 8;
+      hipLaunchKernelGGL((attn_core2_kernel<D>), dim3(static_cast<uint32_t>(grid2)), dim3(256), 0,
                          stream, a);
       return;
     }
