@@ -733,6 +733,178 @@ __global__ __launch_bounds__(kBThreads, 1) void gemm_big_kernel(GemmArgs g) {
   }
 }
 
+// Register-staged form: 256 x 256 per workgroup, 4 waves of 128 x 128 (one
+// wave per SIMD), k in chunks of 64 through two LDS buffers.  A chunk's
+// global loads land in registers two chunks ahead of its use and go into
+// LDS one chunk ahead, so a load has about a chunk and a half to arrive while
+// each chunk costs one barrier.  Only loads wait on the vector memory
+// counter in the loop (no stores), so the compiler's own waits are exact.
+#ifndef TDP_GEMM_RS
+#define TDP_GEMM_RS 1
+#endif
+constexpr int kRK = 64;                                 // k per chunk
+constexpr int kRLoads = 256 * kRK * 2 / 1024 / 4;       // 1 KB per wave-load, per operand: 8
+// LDS rows of 64 k (128 bytes, 8 pieces of 16 B); piece p of row r sits at
+// p ^ ((r / 2) % 8).  Two rows share a 256-byte bank window, so a fragment
+// read's 16 consecutive rows of one piece land in 16 distinct 16-byte bank
+// groups, and a load's 8 whole rows fill each group four times.
+__device__ __forceinline__ int rs_slot(int r, int p) { return p ^ ((r >> 1) & 7); }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16 sA[2][256 * kRK];
+  __shared__ __attribute__((aligned(16))) bf16 sB[2][256 * kRK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t M = g.M;
+  const int64_t nm = cdiv(M, kWRows), nn = g.N / kWCols;
+  int64_t tm, tn;
+  {
+    const int64_t G = gridDim.x;   // a multiple of 8, >= nm * nn
+    const int64_t bid = blockIdx.x;
+    const int64_t lid = (bid % 8) * (G / 8) + bid / 8;
+    if (lid >= nm * nn) return;
+    constexpr int64_t kGroup = TDP_GEMM_GROUP_M > 0 ? TDP_GEMM_GROUP_M : 1;
+    const int64_t per_group = kGroup * nn;
+    const int64_t grp = lid / per_group;
+    const int64_t first_m = grp * kGroup;
+    const int64_t gm = min(kGroup, nm - first_m);
+    const int64_t in = lid - grp * per_group;
+    tm = first_m + in % gm;
+    tn = in / gm;
+  }
+  const int64_t row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tm))) *
+                       kWRows;
+  const int64_t col0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tn))) *
+                       kWCols;
+  // Load i of an operand's chunk: 16-byte position (i * 4 + wave) * 64 + lane
+  // of the [256][64] chunk, row r = pos / 8, piece p = pos % 8.  Rows past M
+  // read row M - 1 (their results are not stored).
+  const bf16 *ga[kRLoads];
+  const bf16 *gb[kRLoads];
+  int32_t lo[kRLoads];       // LDS element offset, the same for A and B
+#pragma unroll
+  for (int i = 0; i < kRLoads; ++i) {
+    const int pos = (i * 4 + uwave) * 64 + lane;
+    const int r = pos / 8, p = pos % 8;
+    ga[i] = g.a + min(row0 + r, M - 1) * g.lda + 8 * p;
+    gb[i] = g.bt + (col0 + r) * g.ldb + 8 * p;
+    lo[i] = r * kRK + 8 * rs_slot(r, p);
+  }
+  // Fragment offsets: A row 128 wm + 32 t + l32, B^T row 128 wn + 32 t + l32,
+  // piece 2 s + hh of k step s; the swizzle key of the row depends on l32
+  // only, so tile t adds 32 t rows.
+  int32_t fao[4], fbo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int x = 8 * rs_slot(l32, 2 * s + hh);
+    fao[s] = (128 * wm + l32) * kRK + x;
+    fbo[s] = (128 * wn + l32) * kRK + x;
+  }
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x16{};
+  bf16x8 fa[2][4], fb[2][4];            // fragments of k steps s (set s % 2)
+  bf16x8 stA[2][kRLoads], stB[2][kRLoads];   // staged chunks (set c % 2)
+  const int nc = g.K / kRK;
+#define TDP_FENCE() __builtin_amdgcn_sched_barrier(0)
+  auto gload = [&](int set, int c, int i) __attribute__((always_inline)) {
+    const int64_t k = static_cast<int64_t>(min(c, nc - 1)) * kRK;
+    if (i < kRLoads) stA[set][i] = *reinterpret_cast<const bf16x8 *>(ga[i] + k);
+    else stB[set][i - kRLoads] = *reinterpret_cast<const bf16x8 *>(gb[i - kRLoads] + k);
+  };
+  auto lwrite = [&](int set, int buf, int i) __attribute__((always_inline)) {
+    if (i < kRLoads) *reinterpret_cast<bf16x8 *>(&sA[buf][lo[i]]) = stA[set][i];
+    else *reinterpret_cast<bf16x8 *>(&sB[buf][lo[i - kRLoads]]) = stB[set][i - kRLoads];
+  };
+  auto fread = [&](int buf, int s, int q) __attribute__((always_inline)) {
+    // q 0..7: A tile 0, B tiles 0..3, A tiles 1..3 (the order step s's MFMAs use them)
+    if (q == 0) fa[s & 1][0] = *reinterpret_cast<const bf16x8 *>(&sA[buf][fao[s]]);
+    else if (q < 5) fb[s & 1][q - 1] = *reinterpret_cast<const bf16x8 *>(&sB[buf][fbo[s] + 32 * (q - 1) * kRK]);
+    else fa[s & 1][q - 4] = *reinterpret_cast<const bf16x8 *>(&sA[buf][fao[s] + 32 * (q - 4) * kRK]);
+  };
+  // Prologue: chunks 0 and 1 to registers, chunk 0 into buffer 0, step 0's
+  // fragments.
+#pragma unroll
+  for (int i = 0; i < 2 * kRLoads; ++i) gload(0, 0, i);
+#pragma unroll
+  for (int i = 0; i < 2 * kRLoads; ++i) gload(1, 1, i);
+#pragma unroll
+  for (int i = 0; i < 2 * kRLoads; ++i) lwrite(0, 0, i);
+  lds_barrier();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) fread(0, 0, q);
+  // Chunk c (buffer c % 2; register set c % 2 free, set (c + 1) % 2 holds
+  // chunk c + 1).  One memory instruction after each MFMA:
+  //   step 0: step 1's fragment reads, chunk c + 2's loads 0..7 (set c % 2);
+  //   step 1: step 2's reads, loads 8..15;
+  //   step 2: step 3's reads, chunk c + 1's LDS writes 0..7 (buffer
+  //           (c + 1) % 2, which chunk c - 1 used before the last barrier);
+  //   step 3: writes 8..15, then after 8 MFMAs the barrier and the next
+  //           chunk's step-0 reads.
+  auto chunk = [&](int c, auto par) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;   // c % 2
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int am = q / 4, bn = q % 4;
+        if (s == 3 && q == 8) {
+          lds_barrier();
+          TDP_FENCE();
+        }
+        acc[am][bn] = mfma32(fa[s & 1][am], fb[s & 1][bn], acc[am][bn]);
+        if (s < 3 && q % 2 == 0) {
+          fread(P, s + 1, q / 2);
+        } else if (s == 0) {
+          gload(P, c + 2, q / 2);
+        } else if (s == 1) {
+          gload(P, c + 2, 8 + q / 2);
+        } else if (s == 2) {
+          lwrite(1 - P, 1 - P, q / 2);
+        } else if (q < 8) {
+          lwrite(1 - P, 1 - P, 8 + q);
+        } else {
+          fread(1 - P, 0, q - 8);
+        }
+        TDP_FENCE();
+      }
+    }
+  };
+  // K is a multiple of 128: chunks in pairs, every buffer and set index a
+  // constant
+  for (int c = 0; c < nc; c += 2) {
+    chunk(c, std::integral_constant<int, 0>{});
+    chunk(c + 1, std::integral_constant<int, 1>{});
+  }
+#undef TDP_FENCE
+
+  // acc[mt][ct][v]: row 128 wm + 32 mt + 8 (v/4) + 4 hh + v%4, column
+  // 128 wn + 32 ct + l32 (stored as the large form stores them)
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int64_t base = row0 + 128 * wm + 32 * mt;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
+      if (r >= M) continue;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int64_t idx = r * g.ldc + col0 + 128 * wn + 32 * ct + l32;
+        const float x = acc[mt][ct][v];
+        if constexpr (EPI == kEpiBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(x);
+        if constexpr (EPI == kEpiF32) static_cast<float *>(g.c)[idx] = x;
+        if constexpr (EPI == kEpiGeluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(gelu_tanh(x));
+        if constexpr (EPI == kEpiSiluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(silu(x));
+      }
+    }
+  }
+}
+
 // Which form serves the large products: 2 = the large form above, 1 = the
 // wide form.
 #ifndef TDP_GEMM_BIG
@@ -763,7 +935,9 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
     if (TDP_GEMM_BIG == 2 && EPI != kEpiResid && EPI != kEpiResidGate &&
         a.K % (kBK * kBStages) == 0 && fits) {
       const dim3 bgrid(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8));
-      if (hd == 0)
+      if (TDP_GEMM_RS && hd == 0 && a.K % (2 * kRK) == 0)
+        hipLaunchKernelGGL((gemm_rs_kernel<EPI>), bgrid, dim3(256), 0, stream, a);
+      else if (hd == 0)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, 0>), bgrid, dim3(kBThreads), 0, stream, a);
       else if (hd == 64)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, 64>), bgrid, dim3(kBThreads), 0, stream, a);
