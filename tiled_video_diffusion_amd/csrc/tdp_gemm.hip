@@ -733,14 +733,20 @@ __global__ __launch_bounds__(kBThreads, 1) void gemm_big_kernel(GemmArgs g) {
   }
 }
 
-// Register-staged form: 256 x 256 per workgroup, 4 waves of 128 x 128 (one
-// wave per SIMD), k in chunks of 64 through two LDS buffers.  A chunk's
-// global loads land in registers two chunks ahead of its use and go into
-// LDS one chunk ahead, so a load has about a chunk and a half to arrive while
-// each chunk costs one barrier.  Only loads wait on the vector memory
-// counter in the loop (no stores), so the compiler's own waits are exact.
-#ifndef TDP_GEMM_RS
-#define TDP_GEMM_RS 1
+// Large form with 64-wide k chunks: 256 x 256 per workgroup, 4 waves of
+// 128 x 128 (one wave per SIMD), two LDS buffers.  Chunk c + 1 goes global
+// -> LDS by direct loads into the buffer chunk c - 1 used while chunk c is
+// computed (its loads spread over the first half of the chunk's MFMAs), so
+// each chunk costs one barrier and its loads have half to all of a chunk to
+// land.  One memory instruction after each MFMA, in a fixed order; the next
+// chunk's first fragments are read after the barrier, under the last 8
+// MFMAs.  Measured against the 4-stage ring of 32-wide chunks on the block's
+// shapes: FFN up 14.30 -> 13.37 ms, FFN down 15.47 -> 13.83, QKV 9.87 ->
+// 9.08; staging the loads through registers instead (two chunks ahead)
+// gave 13.76 / 13.67 / 9.8, its LDS writes and their waits costing more
+// than the extra lead saved.
+#ifndef TDP_GEMM_K64
+#define TDP_GEMM_K64 1
 #endif
 constexpr int kRK = 64;                                 // k per chunk
 constexpr int kRLoads = 256 * kRK * 2 / 1024 / 4;       // 1 KB per wave-load, per operand: 8
@@ -750,8 +756,10 @@ constexpr int kRLoads = 256 * kRK * 2 / 1024 / 4;       // 1 KB per wave-load, p
 // groups, and a load's 8 whole rows fill each group four times.
 __device__ __forceinline__ int rs_slot(int r, int p) { return p ^ ((r >> 1) & 7); }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmArgs g) {
+// HD = 0: row-major A; HD = 64 / 128: head-major A with that head size.
+template <int EPI, int HD>
+__global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
+  static_assert(HD % kRK == 0, "whole k chunks per head");
   __shared__ __attribute__((aligned(16))) bf16 sA[2][256 * kRK];
   __shared__ __attribute__((aligned(16))) bf16 sB[2][256 * kRK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -762,7 +770,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmArgs g) {
   const int64_t nm = cdiv(M, kWRows), nn = g.N / kWCols;
   int64_t tm, tn;
   {
-    const int64_t G = gridDim.x;   // a multiple of 8, >= nm * nn
+    const int64_t G = gridDim.x;
     const int64_t bid = blockIdx.x;
     const int64_t lid = (bid % 8) * (G / 8) + bid / 8;
     if (lid >= nm * nn) return;
@@ -779,19 +787,43 @@ __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmArgs g) {
                        kWRows;
   const int64_t col0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tn))) *
                        kWCols;
-  // Load i of an operand's chunk: 16-byte position (i * 4 + wave) * 64 + lane
-  // of the [256][64] chunk, row r = pos / 8, piece p = pos % 8.  Rows past M
-  // read row M - 1 (their results are not stored).
-  const bf16 *ga[kRLoads];
-  const bf16 *gb[kRLoads];
-  int32_t lo[kRLoads];       // LDS element offset, the same for A and B
+  const int64_t rows_here = min(static_cast<int64_t>(kWRows), M - row0);
+  const char *abase;
+  uint32_t a_extent;
+  if constexpr (HD > 0) {
+    abase = reinterpret_cast<const char *>(g.a);
+    a_extent = static_cast<uint32_t>(M * g.K * 2);   // host: < 2^32 bytes
+  } else {
+    abase = reinterpret_cast<const char *>(g.a + row0 * g.lda);
+    a_extent = static_cast<uint32_t>(((rows_here - 1) * g.lda + g.K) * 2);
+  }
+  const char *bbase = reinterpret_cast<const char *>(g.bt + col0 * g.ldb);
+  const uint32_t b_extent = static_cast<uint32_t>(((kWCols - 1) * g.ldb + g.K) * 2);
+  const i32x4 arsrc = buffer_rsrc(abase, a_extent);
+  const i32x4 brsrc = buffer_rsrc(bbase, b_extent);
+  // Direct load i of an operand's chunk: LDS 16-byte position (i * 4 +
+  // wave) * 64 + lane = row * 8 + slot takes the row's piece slot ^ key(row)
+  // (the swizzle is its own inverse).  Each descriptor covers exactly the
+  // bytes this workgroup may read; rows past M re-read row M - 1 (their
+  // results are not stored).
+  uint32_t aoff[kRLoads], boff[kRLoads];
 #pragma unroll
   for (int i = 0; i < kRLoads; ++i) {
     const int pos = (i * 4 + uwave) * 64 + lane;
-    const int r = pos / 8, p = pos % 8;
-    ga[i] = g.a + min(row0 + r, M - 1) * g.lda + 8 * p;
-    gb[i] = g.bt + (col0 + r) * g.ldb + 8 * p;
-    lo[i] = r * kRK + 8 * rs_slot(r, p);
+    const int r = pos / 8, slot = pos % 8;
+    const int p = rs_slot(r, slot);
+    const int64_t ra = min(static_cast<int64_t>(r), rows_here - 1);
+    if constexpr (HD > 0) {
+      // head-major A: row gr of segment seg (a_seg_rows rows each) is row
+      // gr - seg L of every head's slab; a chunk's head offset is scalar
+      const int64_t L = g.a_seg_rows;
+      const int64_t gr = row0 + ra;
+      const int64_t seg = gr / L;
+      aoff[i] = static_cast<uint32_t>(((seg * g.a_heads * L + (gr - seg * L)) * HD + 8 * p) * 2);
+    } else {
+      aoff[i] = static_cast<uint32_t>((ra * g.lda + 8 * p) * 2);
+    }
+    boff[i] = static_cast<uint32_t>((static_cast<int64_t>(r) * g.ldb + 8 * p) * 2);
   }
   // Fragment offsets: A row 128 wm + 32 t + l32, B^T row 128 wn + 32 t + l32,
   // piece 2 s + hh of k step s; the swizzle key of the row depends on l32
@@ -808,44 +840,40 @@ __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmArgs g) {
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x16{};
-  bf16x8 fa[2][4], fb[2][4];            // fragments of k steps s (set s % 2)
-  bf16x8 stA[2][kRLoads], stB[2][kRLoads];   // staged chunks (set c % 2)
+  bf16x8 fa[2][4], fb[2][4];            // fragments of k step s (set s % 2)
   const int nc = g.K / kRK;
 #define TDP_FENCE() __builtin_amdgcn_sched_barrier(0)
-  auto gload = [&](int set, int c, int i) __attribute__((always_inline)) {
-    const int64_t k = static_cast<int64_t>(min(c, nc - 1)) * kRK;
-    if (i < kRLoads) stA[set][i] = *reinterpret_cast<const bf16x8 *>(ga[i] + k);
-    else stB[set][i - kRLoads] = *reinterpret_cast<const bf16x8 *>(gb[i - kRLoads] + k);
+  // chunk c's load i into buffer buf (past the last chunk: the last again)
+  auto dload = [&](int buf, int c, int i) __attribute__((always_inline)) {
+    c = min(c, nc - 1);
+    const uint32_t so = static_cast<uint32_t>(c) * kRK * 2;
+    uint32_t sa = so;
+    if constexpr (HD > 0) {
+      constexpr int kPerHead = HD / kRK;
+      const int h = c / kPerHead;
+      sa = static_cast<uint32_t>((static_cast<int64_t>(h) * g.a_seg_rows * HD +
+                                  (c - h * kPerHead) * kRK) * 2);
+    }
+    if (i < kRLoads) load_lds16(arsrc, aoff[i], sa, &sA[buf][(i * 4 + uwave) * 512]);
+    else load_lds16(brsrc, boff[i - kRLoads], so, &sB[buf][((i - kRLoads) * 4 + uwave) * 512]);
   };
-  auto lwrite = [&](int set, int buf, int i) __attribute__((always_inline)) {
-    if (i < kRLoads) *reinterpret_cast<bf16x8 *>(&sA[buf][lo[i]]) = stA[set][i];
-    else *reinterpret_cast<bf16x8 *>(&sB[buf][lo[i - kRLoads]]) = stB[set][i - kRLoads];
-  };
+  // fragment read q of k step s: A tile 0, B tiles 0..3, A tiles 1..3 (the
+  // order step s's MFMAs use them)
   auto fread = [&](int buf, int s, int q) __attribute__((always_inline)) {
-    // q 0..7: A tile 0, B tiles 0..3, A tiles 1..3 (the order step s's MFMAs use them)
     if (q == 0) fa[s & 1][0] = *reinterpret_cast<const bf16x8 *>(&sA[buf][fao[s]]);
     else if (q < 5) fb[s & 1][q - 1] = *reinterpret_cast<const bf16x8 *>(&sB[buf][fbo[s] + 32 * (q - 1) * kRK]);
     else fa[s & 1][q - 4] = *reinterpret_cast<const bf16x8 *>(&sA[buf][fao[s] + 32 * (q - 4) * kRK]);
   };
-  // Prologue: chunks 0 and 1 to registers, chunk 0 into buffer 0, step 0's
-  // fragments.
 #pragma unroll
-  for (int i = 0; i < 2 * kRLoads; ++i) gload(0, 0, i);
-#pragma unroll
-  for (int i = 0; i < 2 * kRLoads; ++i) gload(1, 1, i);
-#pragma unroll
-  for (int i = 0; i < 2 * kRLoads; ++i) lwrite(0, 0, i);
+  for (int i = 0; i < 2 * kRLoads; ++i) dload(0, 0, i);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
 #pragma unroll
   for (int q = 0; q < 8; ++q) fread(0, 0, q);
-  // Chunk c (buffer c % 2; register set c % 2 free, set (c + 1) % 2 holds
-  // chunk c + 1).  One memory instruction after each MFMA:
-  //   step 0: step 1's fragment reads, chunk c + 2's loads 0..7 (set c % 2);
-  //   step 1: step 2's reads, loads 8..15;
-  //   step 2: step 3's reads, chunk c + 1's LDS writes 0..7 (buffer
-  //           (c + 1) % 2, which chunk c - 1 used before the last barrier);
-  //   step 3: writes 8..15, then after 8 MFMAs the barrier and the next
-  //           chunk's step-0 reads.
+  // Chunk c in buffer c % 2: step s's MFMAs carry step s + 1's reads (even
+  // slots) and, in steps 0 and 1, chunk c + 1's 16 direct loads (odd slots);
+  // after 8 of step 3's MFMAs the wait for those loads and the barrier, then
+  // chunk c + 1's step-0 reads.
   auto chunk = [&](int c, auto par) __attribute__((always_inline)) {
     constexpr int P = decltype(par)::value;   // c % 2
 #pragma unroll
@@ -854,37 +882,27 @@ __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmArgs g) {
       for (int q = 0; q < 16; ++q) {
         const int am = q / 4, bn = q % 4;
         if (s == 3 && q == 8) {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           lds_barrier();
           TDP_FENCE();
         }
         acc[am][bn] = mfma32(fa[s & 1][am], fb[s & 1][bn], acc[am][bn]);
-        if (s < 3 && q % 2 == 0) {
-          fread(P, s + 1, q / 2);
-        } else if (s == 0) {
-          gload(P, c + 2, q / 2);
-        } else if (s == 1) {
-          gload(P, c + 2, 8 + q / 2);
-        } else if (s == 2) {
-          lwrite(1 - P, 1 - P, q / 2);
-        } else if (q < 8) {
-          lwrite(1 - P, 1 - P, 8 + q);
-        } else {
-          fread(1 - P, 0, q - 8);
-        }
+        if (s < 3 && q % 2 == 0) fread(P, s + 1, q / 2);
+        else if (s < 2) dload(1 - P, c + 1, 8 * s + q / 2);
+        else if (s == 3 && q >= 8) fread(1 - P, 0, q - 8);
         TDP_FENCE();
       }
     }
   };
-  // K is a multiple of 128: chunks in pairs, every buffer and set index a
-  // constant
+  // K is a multiple of 128: chunks in pairs, every buffer index a constant
   for (int c = 0; c < nc; c += 2) {
     chunk(c, std::integral_constant<int, 0>{});
     chunk(c + 1, std::integral_constant<int, 1>{});
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #undef TDP_FENCE
-
   // acc[mt][ct][v]: row 128 wm + 32 mt + 8 (v/4) + 4 hh + v%4, column
-  // 128 wn + 32 ct + l32 (stored as the large form stores them)
+  // 128 wn + 32 ct + l32
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int64_t base = row0 + 128 * wm + 32 * mt;
@@ -904,6 +922,7 @@ __global__ __launch_bounds__(256, 1) void gemm_rs_kernel(GemmArgs g) {
     }
   }
 }
+
 
 // Which form serves the large products: 2 = the large form above, 1 = the
 // wide form.
@@ -935,9 +954,14 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
     if (TDP_GEMM_BIG == 2 && EPI != kEpiResid && EPI != kEpiResidGate &&
         a.K % (kBK * kBStages) == 0 && fits) {
       const dim3 bgrid(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8));
-      if (TDP_GEMM_RS && hd == 0 && a.K % (2 * kRK) == 0)
-        hipLaunchKernelGGL((gemm_rs_kernel<EPI>), bgrid, dim3(256), 0, stream, a);
-      else if (hd == 0)
+      if (TDP_GEMM_K64 && a.K % (2 * kRK) == 0) {
+        if (hd == 0)
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0>), bgrid, dim3(256), 0, stream, a);
+        else if (hd == 64)
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 64>), bgrid, dim3(256), 0, stream, a);
+        else
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 128>), bgrid, dim3(256), 0, stream, a);
+      } else if (hd == 0)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, 0>), bgrid, dim3(kBThreads), 0, stream, a);
       else if (hd == 64)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, 64>), bgrid, dim3(kBThreads), 0, stream, a);
