@@ -60,6 +60,7 @@ struct GemmArgs {
   int64_t g0_stride;
   const float *g1;
   int64_t rows_per_batch;
+  int32_t group_m;        // 64-wide large form: row blocks per tile-order group
 };
 
 // HD = 0: row-major A; HD = 64 / 128: head-major A with that head size.
@@ -774,11 +775,11 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
     const int64_t bid = blockIdx.x;
     const int64_t lid = (bid % 8) * (G / 8) + bid / 8;
     if (lid >= nm * nn) return;
-    constexpr int64_t kGroup = TDP_GEMM_GROUP_M > 0 ? TDP_GEMM_GROUP_M : 1;
-    const int64_t per_group = kGroup * nn;
+    const int64_t group = g.group_m;
+    const int64_t per_group = group * nn;
     const int64_t grp = lid / per_group;
-    const int64_t first_m = grp * kGroup;
-    const int64_t gm = min(kGroup, nm - first_m);
+    const int64_t first_m = grp * group;
+    const int64_t gm = min(group, nm - first_m);
     const int64_t in = lid - grp * per_group;
     tm = first_m + in % gm;
     tn = in / gm;
@@ -955,12 +956,19 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
         a.K % (kBK * kBStages) == 0 && fits) {
       const dim3 bgrid(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8));
       if (TDP_GEMM_K64 && a.K % (2 * kRK) == 0) {
+        // Tile order: groups of 4 row blocks walk down a column of tiles,
+        // groups of 2 for outputs of 16384 or more columns (measured on the
+        // block's shapes: FFN up, 16384 columns, 13.33 -> 12.95 ms with 2;
+        // FFN down and QKV, 4096 and 12288 columns, 13.79 -> 15.03 and 9.07
+        // -> 9.33 ms with 2; 8 slower for all three)
+        GemmArgs b = a;
+        b.group_m = a.N >= 16384 ? 2 : 4;
         if (hd == 0)
-          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0>), bgrid, dim3(256), 0, stream, a);
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0>), bgrid, dim3(256), 0, stream, b);
         else if (hd == 64)
-          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 64>), bgrid, dim3(256), 0, stream, a);
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 64>), bgrid, dim3(256), 0, stream, b);
         else
-          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 128>), bgrid, dim3(256), 0, stream, a);
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 128>), bgrid, dim3(256), 0, stream, b);
       } else if (hd == 0)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, 0>), bgrid, dim3(kBThreads), 0, stream, a);
       else if (hd == 64)
@@ -1003,7 +1011,7 @@ tdp_status gemm(int epi, const GemmDesc &d, hipStream_t stream) {
   if (epi == kEpiResidGate && d.rows_per_batch < 1) return TDP_ERR_ARG;
   if (cdiv(d.M, kGRows) > INT32_MAX) return TDP_ERR_UNSUPPORTED;
   GemmArgs a{d.a, d.lda, d.a_seg_rows, d.a_heads, d.bt, d.ldb, d.M, d.N, d.K, d.c, d.ldc,
-             d.g0, d.g0_stride, d.g1, d.rows_per_batch};
+             d.g0, d.g0_stride, d.g1, d.rows_per_batch, 4};
   const dim3 grid(static_cast<uint32_t>(cdiv(d.M, kGRows)), static_cast<uint32_t>(d.N / kGCols));
   switch (epi) {
     case kEpiBf16: return launch_epi<kEpiBf16>(a, d.a_head_dim, grid, stream);
