@@ -866,11 +866,10 @@ def time_step(step, steps: int, warmup: int, stream) -> tuple:
 def core_roofline(wl, plan, core_ms: float) -> dict:
     flops = attn_flops(plan, wl)
     achieved = flops / (core_ms * 1e-3) / 1e12
-    # The library runs the two-query-group kernel at head dim 128 and the
-    # one-group kernel otherwise; none of the timed workloads splits its keys
-    # (the rocprofv3 traces of each workload show the kernel launched).
-    kern = ("attn_core2_kernel<128>" if wl.head_dim == 128
-            else f"attn_core_kernel<{wl.head_dim}, false>")
+    # Unsplit launches run the two-query-group kernel at either head dim;
+    # none of the timed workloads splits its keys (the rocprofv3 traces of
+    # each workload show the kernel launched).
+    kern = f"attn_core2_kernel<{wl.head_dim}>"
     tr = recorded_traffic(wl.name, kern)
     return {"kernel": kern, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
