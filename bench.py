@@ -691,6 +691,38 @@ def loop_bench(name: str, reps: int, warmup: int) -> dict:
             "blend_euler": kern}
 
 
+def drift_sweep(name: str, sigma0s=(0.1, 0.3, 0.5, 0.7, 0.9)) -> dict:
+    """The upscale loop of workload `name` from several first sigmas, the same
+    number of linearly spaced steps each: every step's seam spread
+    sqrt(S2/S0) (the tiles' disagreement where they overlap) and how far the
+    loop moved the generated tokens from the stage-1 latent."""
+    import torch
+
+    import tdp_inputs as ti
+    from tiled_video_diffusion_amd import tdp
+    from tiled_video_diffusion_amd.step import UpscaleLoop
+
+    up = ti.make_upscale_inputs(name)
+    uw = up.workload
+    out = {"workload": name, "block": uw.block, "n_steps": uw.n_steps, "by_sigma0": {},
+           "note": ("synthetic weights: the spread shows the metric across first sigmas, "
+                    "not a quality; the page ties drift to the first sigma")}
+    for s0 in sigma0s:
+        lp = UpscaleLoop(up, sigmas=tdp.tdp_linear_sigmas(float(s0), uw.n_steps))
+        lp.renoise()
+        lp.loop()
+        torch.cuda.synchronize()
+        n = lp.n_gen
+        x1 = lp.x_stage1[:, :n].double()
+        moved = float((lp.x[:, :n].double() - x1).norm() / x1.norm())
+        seam = lp.seam.cpu().numpy()
+        out["by_sigma0"][f"{s0:g}"] = {"seam_relative_spread": [float(v) for v in seam[:lp.n_steps, 2]],
+                                       "displacement_from_stage1": moved}
+        lp = None
+        torch.cuda.empty_cache()
+    return out
+
+
 def _time_blend_euler(s, B, C, N, n_dst, n_launch=50) -> dict:
     """Mean launch time of tdp_blend_euler on TdpStep ``s``'s plan with random
     float32 tile rows, with and without the seam sums (HIP events on the
@@ -1032,6 +1064,9 @@ def run(args) -> dict:
     if args.loop:
         torch.cuda.empty_cache()
         out["loop"] = loop_bench(args.loop, max(2, args.steps // 8), 1)
+    if args.drift:
+        torch.cuda.empty_cache()
+        out["drift"] = drift_sweep(args.drift)
     if args.sp:
         torch.cuda.empty_cache()
         out["sp"] = sp_bench(args.sp)
@@ -1072,6 +1107,9 @@ def main():
     ap.add_argument("--loop", default="",
                     help="also time the upscale loop (an upscale workload name, e.g. "
                          "upscale_t16)")
+    ap.add_argument("--drift", default="",
+                    help="also run the upscale loop of this upscale workload from several first "
+                         "sigmas and report its seam spread per step (e.g. upscale_d128)")
     ap.add_argument("--sp", type=int, default=0,
                     help="also time one rank's share of sequence parallelism on the "
                          "first-stage latent for this many ranks")

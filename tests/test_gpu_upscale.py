@@ -195,6 +195,37 @@ def test_upscale_loop_matches_oracle(name):
         assert e2 <= SEAM_TOL and e0 <= SEAM_TOL
 
 
+@pytest.mark.parametrize("sigma0", [0.1, 0.9])
+def test_upscale_loop_first_sigma_sweep(sigma0):
+    """Drift is tied to the first sigma: from other first sigmas than the
+    workload's, the same number of linear steps still matches the oracle in
+    the latent and in every step's seam sums."""
+    say("loop upscale_tiny sigma0", sigma0)
+    up = ti.make_upscale_inputs("upscale_tiny")
+    n = up.workload.n_steps
+    from tiled_video_diffusion_amd import tdp
+    sig = tdp.tdp_linear_sigmas(sigma0, n)
+    assert np.array_equal(sig, ou.linear_sigmas(sigma0, n))
+    L, x0 = _loop(up, sigmas=sig)
+    binp = up.block
+    wl = binp.base.workload
+    N = wl.n_gen
+    po = oracle.plan(wl.grid, wl.tiling, binp.base.cond_pos)
+    ref = ou.upscale_loop(binp.base.x_global, up.noise, L.sigmas, N, ou.tdp_velocity(binp, po))
+    got = L.x.double().cpu().numpy()
+    e_x = rel_err(got[:, :N], ref.x[:, :N])
+    e_d = rel_err(got[:, :N] - x0.double().cpu().numpy()[:, :N], ref.x[:, :N] - ref.states[0][:, :N])
+    say(f"  x {e_x:.2e}  displacement {e_d:.2e}")
+    assert e_x <= TOL and e_d <= TOL
+    seam = L.seam.cpu().numpy()
+    assert len(ref.seam) == n
+    for i, (s2, s0) in enumerate(ref.seam):
+        e2, e0 = abs(seam[i, 0] - s2) / s2, abs(seam[i, 1] - s0) / s0
+        say(f"  step {i}: spread {seam[i, 2]:.4f} (oracle {ou.relative_spread(s2, s0):.4f})"
+            f"  S2 {e2:.2e}  S0 {e0:.2e}")
+        assert e2 <= SEAM_TOL and e0 <= SEAM_TOL
+
+
 def test_upscale_loop_edge_schedules():
     """No steps leaves the re-noised latent; sigma 0 throughout leaves the
     stage-1 latent; a non-uniform schedule matches the oracle."""
