@@ -1480,6 +1480,25 @@ __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t s
 #define TDP_ATTN_NG2 1
 #endif
 #define TDP_NG2_FENCE() __builtin_amdgcn_sched_barrier(0)
+// Within each MFMA step of the key loop the MFMA issues first and its
+// companions (accumulator reads, exponentials, packs, LDS reads, loads)
+// after it, in the matrix pipe's shadow.  Left to itself the scheduler
+// sometimes puts a step's accumulator reads ahead of its MFMA, and the
+// loop then takes about 2% more cycles.
+#ifndef TDP_ATTN_PIN
+#define TDP_ATTN_PIN 1
+#endif
+#if TDP_ATTN_PIN
+#define TDP_NG2_MFMA_FIRST()                                                       \
+  do {                                                                             \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   /* MFMA */                 \
+    __builtin_amdgcn_sched_group_barrier(0x496, 256, 0); /* VALU SALU VMEM DS trans */ \
+  } while (0)
+#else
+#define TDP_NG2_MFMA_FIRST() \
+  do {                       \
+  } while (0)
+#endif
 
 // Fragment offsets of the two-group core (128-key blocks at either head
 // dim): K row l32, head-dim chunk 2 st + hh, in CoreSmem's K swizzle; V^T
@@ -1631,6 +1650,12 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
     for (int i = 0; i < 2 * kLoads; ++i) load_one(i, kr, vr, kb, vb);
   };
 
+  // Blocks 0 and 1 go out before the Q-dependent check below, so their
+  // latency overlaps that of the Q loads.  (The exact path reloads block 0
+  // after waiting for every load: same data, same place.)
+  load_block(0, sk0, sv0);
+  load_block(1, sk1, sv1);
+
   // Cauchy-Schwarz bound of the shift-free softmax (see attn_core_kernel).
   constexpr float kNoShift = 64.f;
   bool need_exact = false;
@@ -1682,10 +1707,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
 #pragma unroll
     for (int i = 0; i < kDT; ++i) vf[i][0] = vf[i][1] = bf16x8{};
 
-    // blocks 0 and 1 into LDS; wait for block 0 (block 1's 16 loads stay in
-    // flight); S(0) from tile 0's K fragments
-    load_block(0, sk0, sv0);
-    load_block(1, sk1, sv1);
+    // wait for block 0 (block 1's loads may stay in flight); S(0) from tile
+    // 0's K fragments
     if constexpr (2 * kLoads == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     lds_barrier();
@@ -1742,6 +1765,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
             kf[(q - (kP1 - 2 * kLead)) / 2] =
                 *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[(q - (kP1 - 2 * kLead)) / 2]);
         }
+        TDP_NG2_MFMA_FIRST();
         TDP_NG2_FENCE();
       }
       i32x4 kr, vr;
@@ -1769,6 +1793,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
           load_one(q, kr, vr, kbuf(std::integral_constant<int, BP>{}),
                    vbuf(std::integral_constant<int, BP>{}));
         }
+        TDP_NG2_MFMA_FIRST();
         TDP_NG2_FENCE();
       }
     };
