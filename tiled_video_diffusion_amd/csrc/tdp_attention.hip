@@ -1480,11 +1480,11 @@ __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t s
 #define TDP_ATTN_NG2 1
 #endif
 #define TDP_NG2_FENCE() __builtin_amdgcn_sched_barrier(0)
-// Within each MFMA step of the key loop the MFMA issues first and its
-// companions (accumulator reads, exponentials, packs, LDS reads, loads)
-// after it, in the matrix pipe's shadow.  Left to itself the scheduler
-// sometimes puts a step's accumulator reads ahead of its MFMA, and the
-// loop then takes about 2% more cycles.
+// Within each MFMA step of the key loop the MFMA issues first, then the
+// step's LDS reads, then its other companions (accumulator reads,
+// exponentials, packs, loads), in the matrix pipe's shadow.  Left to itself
+// the scheduler sometimes puts a step's accumulator reads ahead of its
+// MFMA, and the loop then takes about 2% more cycles.
 #ifndef TDP_ATTN_PIN
 #define TDP_ATTN_PIN 1
 #endif
@@ -1492,7 +1492,8 @@ __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t s
 #define TDP_NG2_MFMA_FIRST()                                                       \
   do {                                                                             \
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   /* MFMA */                 \
-    __builtin_amdgcn_sched_group_barrier(0x496, 256, 0); /* VALU SALU VMEM DS trans */ \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   /* LDS reads */            \
+    __builtin_amdgcn_sched_group_barrier(0x616, 256, 0); /* VALU SALU VMEM LDS-write trans */ \
   } while (0)
 #else
 #define TDP_NG2_MFMA_FIRST() \
