@@ -1555,6 +1555,28 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
   const int64_t u = lid - bh * a.units_per_bh;
   const int64_t b = bh / a.heads;
   const int h = static_cast<int>(bh - b * a.heads);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+
+  // Q fragments first, before the unit's table lookups: group g holds query
+  // row 64 wave + 32 g + l32.  A tile unit's rows start at row 256 u of the
+  // (batch, head)'s padded slab (each tile takes whole 256-row units there);
+  // an audio unit's at row 256 (u - units) % (audio units per tile).  Rows
+  // of an empty unit (past the last tile) are in the slab and never used.
+  bf16x8 qf[2][kSteps];
+  {
+    const bool tile_unit = u < a.n_units;
+    const int64_t ua = u - a.n_units;
+    const bf16 *qsrc = tile_unit ? a.q + (bh * a.n_pad + u * kUnit) * D
+                                 : a.qa + (bh * a.a_pad + (ua % max(a.n_aqb, 1)) * kUnit) * D;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st)
+        qf[g][st] = *reinterpret_cast<const bf16x8 *>(qsrc + (64 * wave + 32 * g + l32) * D +
+                                                      16 * st + 8 * hh);
+  }
   int32_t t, q0;
   bool audio_q;
   if (u < a.n_units) {
@@ -1577,20 +1599,6 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
   const int32_t nq = audio_q ? (a.A - q0) : (len0 - q0);
   if (nq <= 0) return;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int l32 = lane & 31, hh = lane >> 5;
-  const int uwave = __builtin_amdgcn_readfirstlane(wave);
-
-  // Q fragments: group g holds query row 64 wave + 32 g + l32.
-  const bf16 *qsrc = audio_q ? a.qa + ((bh * a.a_pad) + q0) * D
-                             : a.q + ((bh * a.n_pad) + pad0 + q0) * D;
-  bf16x8 qf[2][kSteps];
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st)
-      qf[g][st] = *reinterpret_cast<const bf16x8 *>(qsrc + (64 * wave + 32 * g + l32) * D +
-                                                    16 * st + 8 * hh);
 
   // key blocks: the tile's rows (segment 0), then the audio rows (segment 1)
   const int nkb0 = a.tile_keys ? static_cast<int>(ceil_div(len0, kBN)) : 0;
@@ -1625,16 +1633,18 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
   const bf16 *vslab = a.vt + bh * D * a.vt_cols;
   const uint32_t kbytes = kBN * D * 2;
   const uint32_t vbytes = static_cast<uint32_t>(((D - 1) * a.vt_cols + kBN) * 2);
-  // Block j (clamped to the last; past it, in-range data is re-read and
-  // never used) straight into LDS: kLoads of K, then kLoads of V^T; load
-  // i < 8 is of K, 8..15 of V^T.
+  // Block j straight into LDS: kLoads of K, then kLoads of V^T; load i < 8
+  // is of K, 8..15 of V^T.  Past the last block the descriptors hold no
+  // bytes: those loads touch no memory and write zeros that are never read
+  // (the unit's last wait then does not wait on memory).
   auto block_rsrc = [&](int j, i32x4 &kr, i32x4 &vr) __attribute__((always_inline)) {
+    const bool live = j < nkb;
     j = min(j, nkb - 1);
     const bool s0 = j < nkb0;
     kr = buf_rsrc(s0 ? kslab0 + static_cast<int64_t>(j) * kBN * D
-                     : kslab1 + static_cast<int64_t>(j - nkb0) * kBN * D, kbytes);
+                     : kslab1 + static_cast<int64_t>(j - nkb0) * kBN * D, live ? kbytes : 0u);
     vr = buf_rsrc(vslab + (s0 ? pad0 + static_cast<int64_t>(j) * kBN
-                              : a.n_pad + static_cast<int64_t>(j - nkb0) * kBN), vbytes);
+                              : a.n_pad + static_cast<int64_t>(j - nkb0) * kBN), live ? vbytes : 0u);
   };
   auto load_one = [&](int i, const i32x4 &kr, const i32x4 &vr, bf16 *kb, bf16 *vb)
       __attribute__((always_inline)) {
