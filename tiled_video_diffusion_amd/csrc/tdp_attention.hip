@@ -1708,7 +1708,10 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
     bf16x8 pf[2][2][2];     // [parity][group][16-key half] bf16 P
     bf16x8 kf[kSteps];      // K fragments of the next tile (a few live at a time)
     bf16x8 vf[kDT][2];      // V^T fragments [32-row group of d][16-key half]
-    float lsum[2] = {0.f, 0.f};
+    // Row sums: at head dim 128 two fp32 partial sums of the exponentials per
+    // group (the bf16 dot instruction co-issues worse with the MFMAs); at 64,
+    // where registers are short, one dot2 over the packed pair.
+    float lsum[2] = {0.f, 0.f}, lsum2[2] = {0.f, 0.f};
     float e0 = 0.f, e1 = 0.f;
     // P and V^T of "tile -1" are zero: the first PV step adds nothing.
 #pragma unroll
@@ -1742,7 +1745,12 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
         const bf16x2 pp = {static_cast<bf16>(e0), static_cast<bf16>(e1)};
         pf[PC][g][v / 8][v % 8] = pp[0];
         pf[PC][g][v / 8][v % 8 + 1] = pp[1];
-        lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[g], false);
+        if constexpr (D == 128) {
+          lsum[g] += e0;
+          lsum2[g] += e1;
+        } else {
+          lsum[g] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum[g], false);
+        }
       }
     };
     constexpr int kLead = kSteps == 8 ? 3 : 2;   // K fragment reads run this many k steps ahead
@@ -1830,7 +1838,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
     bool bad = false;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const float lr = lsum[g] - static_cast<float>(nz);
+      const float lr = (lsum[g] + lsum2[g]) - static_cast<float>(nz);
       bad = bad || !(lr >= 0x1p-6f * static_cast<float>(nz));
       l_tot[g] = lr + __shfl_xor(lr, 32);
       bad = bad || !(l_tot[g] >= 0x1p-90f);
