@@ -1463,13 +1463,16 @@ __device__ __forceinline__ i32x4 buf_rsrc(const void *base, uint32_t bytes) {
   return r;
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const bf16 *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16 *)p));
+}
+
 // 16 bytes per lane at descriptor offset voff + soff (soff wave-uniform)
-// into LDS: the wave's 64 lanes fill the 1 KB at `lds` (wave-uniform) in
-// lane order.
+// into LDS: the wave's 64 lanes fill the 1 KB at LDS byte address m0
+// (wave-uniform) in lane order.
 __device__ __forceinline__ void lds_load16(i32x4 rsrc, uint32_t voff, uint32_t soff,
-                                           const bf16 *lds) {
-  const uint32_t m0 = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16 *)lds));
+                                           uint32_t m0) {
   asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
@@ -1527,7 +1530,6 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
   static_assert(D == 128 || D == 64, "the two-group core is built for head dim 64 or 128");
   constexpr int kBN = 128, kKT = kBN / 32, kW = 4;
   constexpr int kSteps = D / 16, kDT = D / 32;
-  constexpr int kRows = 256;                            // queries per workgroup
   constexpr int kLoads = kBN * D * 2 / 1024 / kW;       // 1 KB loads per wave, K or V^T block
   // MFMAs per phase of a 32-key tile: O += V P (phase 1), S = K Q^T (phase 2);
   // each phase also takes the 16 softmax steps of one group, kR1 / kR2 per MFMA
@@ -1646,19 +1648,30 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
     vr = buf_rsrc(vslab + (s0 ? pad0 + static_cast<int64_t>(j) * kBN
                               : a.n_pad + static_cast<int64_t>(j - nkb0) * kBN), live ? vbytes : 0u);
   };
-  auto load_one = [&](int i, const i32x4 &kr, const i32x4 &vr, bf16 *kb, bf16 *vb)
+  // The LDS destination of load i is the buffer's address + i * 4 KB + wb,
+  // wb = the wave's 1 KB slot, taken afresh (through an opaque copy) for
+  // every block: each destination is then one scalar add at its load
+  // instead of one of 32 registers held through the whole loop.
+  auto wave_slot = [&]() __attribute__((always_inline)) {
+    uint32_t wb = static_cast<uint32_t>(uwave) * 1024u;
+    asm volatile("" : "+s"(wb));
+    return wb;
+  };
+  auto load_one = [&](int i, const i32x4 &kr, const i32x4 &vr, bf16 *kb, bf16 *vb, uint32_t wb)
       __attribute__((always_inline)) {
     if (i < kLoads)
-      lds_load16(kr, koff0, static_cast<uint32_t>(i) * 4096u, kb + (i * kW + uwave) * 512);
+      lds_load16(kr, koff0, static_cast<uint32_t>(i) * 4096u,
+                 lds_addr(kb) + static_cast<uint32_t>(i * kW) * 1024u + wb);
     else
       lds_load16(vr, voff0, static_cast<uint32_t>(i - kLoads) * vstep,
-                 vb + ((i - kLoads) * kW + uwave) * 512);
+                 lds_addr(vb) + static_cast<uint32_t>((i - kLoads) * kW) * 1024u + wb);
   };
   auto load_block = [&](int j, bf16 *kb, bf16 *vb) __attribute__((always_inline)) {
     i32x4 kr, vr;
     block_rsrc(j, kr, vr);
+    const uint32_t wb = wave_slot();
 #pragma unroll
-    for (int i = 0; i < 2 * kLoads; ++i) load_one(i, kr, vr, kb, vb);
+    for (int i = 0; i < 2 * kLoads; ++i) load_one(i, kr, vr, kb, vb, wb);
   };
 
   // Blocks 0 and 1 go out before the Q-dependent check below, so their
@@ -1694,7 +1707,17 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
   // (at head dim 128 FragOffsets<128> holds the same offsets; it stays there,
   // as the register allocation of this kernel is sensitive to its form)
   using Frags = std::conditional_t<D == 128, FragOffsets<D>, Frag2<D>>;
-  const Frags fo(l32, hh);
+  // The V^T offsets carry the V^T buffers' base (64 KB into the LDS array),
+  // so that what a fragment read adds to them, at most 56 KB, fits the LDS
+  // read's 16-bit immediate offset.
+  Frags fo(l32, hh);
+#pragma unroll
+  for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      fo.v[kt][x] += 2 * kBufEl;
+      asm volatile("" : "+v"(fo.v[kt][x]));   // (kept out of the constant folding)
+    }
   f32x16 o[2][kDT];
   float l_tot[2];
   const bf16x2 ones = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
@@ -1768,15 +1791,14 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
       constexpr int TN = (T + 1) % kKT;               // tile index of tau + 1 in its block
       constexpr int NBP = T == kKT - 1 ? 1 - BP : BP; // its buffers
       const std::integral_constant<int, PC> pc{};
-      const bf16 *kc = kbuf(std::integral_constant<int, BP>{});
-      const bf16 *vc = vbuf(std::integral_constant<int, BP>{});
       const bf16 *kn = kbuf(std::integral_constant<int, NBP>{});
 #pragma unroll
       for (int q = 0; q < kP1; ++q) {
         const int dt = q / 4, x = (q / 2) % 2, g = q % 2;
         o[g][dt] = mfma32(vf[dt][x], pf[PN][g][x], o[g][dt]);
         if (g == 1)   // both groups have read vf[dt][x]: tile tau's goes in
-          vf[dt][x] = *reinterpret_cast<const bf16x8 *>(vc + 32 * dt * kBN + fo.v[T][x]);
+          vf[dt][x] = *reinterpret_cast<const bf16x8 *>(smem + (BP * kBufEl + 32 * dt * kBN) +
+                                                        fo.v[T][x]);
 #pragma unroll
         for (int r = 0; r < kR1; ++r) soft_step(pc, 0, kR1 * q + r);
         if constexpr (T != kKT - 1) {
@@ -1788,12 +1810,14 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
         TDP_NG2_FENCE();
       }
       i32x4 kr, vr;
+      uint32_t wb = 0;
       if constexpr (T == kKT - 1) {
         // block j + 1 landed (this wave's loads, then everyone's); every wave
         // is past its reads of block j, whose buffers now take block j + 2
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         lds_barrier();
         block_rsrc(j + 2, kr, vr);
+        wb = wave_slot();
 #pragma unroll
         for (int st = 0; st < kLead; ++st)
           kf[st] = *reinterpret_cast<const bf16x8 *>(kn + 32 * TN * D + fo.k[st]);
@@ -1810,7 +1834,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
         for (int r = 0; r < kR2; ++r) soft_step(pc, 1, kR2 * q + r);
         if constexpr (T == kKT - 1) {
           load_one(q, kr, vr, kbuf(std::integral_constant<int, BP>{}),
-                   vbuf(std::integral_constant<int, BP>{}));
+                   vbuf(std::integral_constant<int, BP>{}), wb);
         }
         TDP_NG2_MFMA_FIRST();
         TDP_NG2_FENCE();
@@ -1857,7 +1881,7 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
     // (the buffers are free: every wave passed the check above after its
     // loads completed)
     auto xblock = [&](auto par, int j) __attribute__((always_inline)) {
-      const bf16 *kb = kbuf(par), *vb = vbuf(par);
+      const bf16 *kb = kbuf(par);
       load_block(j + 1, kbuf(std::integral_constant<int, 1 - decltype(par)::value>{}),
                  vbuf(std::integral_constant<int, 1 - decltype(par)::value>{}));
       const int kvalid = (j == nkb0 - 1) ? kvalid0 : ((j == nkb - 1 && nkb1 > 0) ? kvalid1 : kBN);
@@ -1894,7 +1918,8 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
         for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
           for (int x = 0; x < 2; ++x) {
-            const bf16x8 v8 = *reinterpret_cast<const bf16x8 *>(vb + 32 * dt * kBN + fo.v[i][x]);
+            const bf16x8 v8 = *reinterpret_cast<const bf16x8 *>(
+                smem + (decltype(par)::value * kBufEl + 32 * dt * kBN) + fo.v[i][x]);
             o[0][dt] = mfma32(v8, px[0][0][x], o[0][dt]);
             o[1][dt] = mfma32(v8, px[1][0][x], o[1][dt]);
           }
