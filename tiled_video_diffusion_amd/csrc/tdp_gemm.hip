@@ -758,7 +758,13 @@ constexpr int kRLoads = 256 * kRK * 2 / 1024 / 4;       // 1 KB per wave-load, p
 __device__ __forceinline__ int rs_slot(int r, int p) { return p ^ ((r >> 1) & 7); }
 
 // HD = 0: row-major A; HD = 64 / 128: head-major A with that head size.
-template <int EPI, int HD>
+// LEAD: chunk c + 2's A loads go out right after chunk c's barrier (its
+// buffer is free from there) and chunk c + 1's B loads in chunk c's first
+// step, instead of both in chunk c's first two steps: more time for each
+// load to land.  Measured on the block's shapes: FFN down (K = 16384)
+// 13.75 -> 13.00 ms; FFN up and QKV (K = 4096) 12.56 -> 12.76 and 8.82 ->
+// 8.98 ms, so the launch takes it for K >= 8192 only.
+template <int EPI, int HD, bool LEAD = false>
 __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   static_assert(HD % kRK == 0, "whole k chunks per head");
   __shared__ __attribute__((aligned(16))) bf16 sA[2][256 * kRK];
@@ -869,6 +875,10 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   for (int i = 0; i < 2 * kRLoads; ++i) dload(0, 0, i);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
+  if constexpr (LEAD) {
+#pragma unroll
+    for (int i = 0; i < kRLoads; ++i) dload(1, 1, i);
+  }
 #pragma unroll
   for (int q = 0; q < 8; ++q) fread(0, 0, q);
   // Chunk c in buffer c % 2: step s's MFMAs carry step s + 1's reads (even
@@ -888,9 +898,18 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
           TDP_FENCE();
         }
         acc[am][bn] = mfma32(fa[s & 1][am], fb[s & 1][bn], acc[am][bn]);
-        if (s < 3 && q % 2 == 0) fread(P, s + 1, q / 2);
-        else if (s < 2) dload(1 - P, c + 1, 8 * s + q / 2);
-        else if (s == 3 && q >= 8) fread(1 - P, 0, q - 8);
+        if constexpr (LEAD) {
+          if (s < 3 && q % 2 == 0) fread(P, s + 1, q / 2);
+          else if (s == 0) dload(1 - P, c + 1, kRLoads + q / 2);
+          else if (s == 3 && q >= 8) {
+            fread(1 - P, 0, q - 8);
+            dload(P, c + 2, q - 8);
+          }
+        } else {
+          if (s < 3 && q % 2 == 0) fread(P, s + 1, q / 2);
+          else if (s < 2) dload(1 - P, c + 1, 8 * s + q / 2);
+          else if (s == 3 && q >= 8) fread(1 - P, 0, q - 8);
+        }
         TDP_FENCE();
       }
     }
@@ -963,7 +982,9 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
         // -> 9.33 ms with 2; 8 slower for all three)
         GemmArgs b = a;
         b.group_m = a.N >= 16384 ? 2 : 4;
-        if (hd == 0)
+        if (hd == 0 && a.K >= 8192)
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0, true>), bgrid, dim3(256), 0, stream, b);
+        else if (hd == 0)
           hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0>), bgrid, dim3(256), 0, stream, b);
         else if (hd == 64)
           hipLaunchKernelGGL((gemm_k64_kernel<EPI, 64>), bgrid, dim3(256), 0, stream, b);
