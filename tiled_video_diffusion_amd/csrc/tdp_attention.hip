@@ -1422,19 +1422,20 @@ void attn_core_kernel(CoreArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// core, two query groups per wave (head dim 128, unsplit launches)
+// core, two query groups per wave (head dim 64 and 128, unsplit launches)
 // ---------------------------------------------------------------------------
 //
 // 4 waves x 64 queries (two groups of 32 per wave) = 256 queries of one
-// (batch, head, tile) per workgroup, 128-key blocks, one workgroup per CU and
-// so one wave per SIMD.  Each K or V^T fragment a wave reads from LDS feeds
+// (batch, head, tile) per workgroup, 128-key blocks; at head dim 128 one
+// workgroup per CU and so one wave per SIMD (two at head dim 64).  Each K or V^T fragment a wave reads from LDS feeds
 // the MFMAs of both its query groups: half the LDS reads per MFMA of the
 // 8-wave form, whose 1 KB per MFMA (plus the K/V staging) would exceed the
 // CU's LDS bandwidth before the MFMA rate is reached.
 //
 // With one wave per SIMD nothing else covers latency, so the block loop is a
 // software pipeline over 32-key tiles tau in a fixed instruction order (a
-// scheduling fence after each MFMA and its companions).  Iteration tau:
+// scheduling fence after each MFMA and its companions; within a step the
+// MFMA issues first, then its LDS reads, then the rest).  Iteration tau:
 //   phase 1: 16 MFMAs of O += V(tau-1) P(tau-1), with the reads of the K
 //            fragments of tile tau+1 and the exponentials of group 0 of S(tau)
 //   phase 2: 16 MFMAs of S(tau+1) = K(tau+1) Q^T, with the reads of the V
