@@ -15,6 +15,9 @@
 // slots of a 256-byte bank window.
 #include "tdp_internal.h"
 
+#include <algorithm>
+#include <atomic>
+
 namespace tdp {
 namespace {
 
@@ -35,12 +38,16 @@ __device__ __forceinline__ int g_slot(int r, int piece) { return piece ^ ((r >> 
 
 constexpr float kLog2e = 1.4426950408889634f;
 // tanh-form GELU via 0.5 (1 + tanh z) = 1 / (1 + exp(-2 z)), z = sqrt(2/pi) (u + 0.044715 u^3).
-// The quotient uses the hardware reciprocal (about 1 ulp, far below the bf16
-// rounding of the result); for very negative u, exp2 -> inf and the
-// reciprocal -> 0.
+// The exponent -2 z log2(e) is u (c0 + c1 u^2): a multiply, an fma and a
+// multiply (written out literally it took five multiplies and an fma; FFN up
+// 13.47 -> 13.28 ms).  The quotient uses the hardware reciprocal (about 1
+// ulp, far below the bf16 rounding of the result); for very negative u,
+// exp2 -> inf and the reciprocal -> 0.
 __device__ __forceinline__ float gelu_tanh(float u) {
-  const float z = 0.7978845608028654f * (u + 0.044715f * u * u * u);
-  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.0f * kLog2e * z));
+  constexpr float c0 = -2.0f * kLog2e * 0.7978845608028654f;
+  constexpr float c1 = c0 * 0.044715f;
+  const float y = u * fmaf(u * u, c1, c0);
+  return u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(y));
 }
 // u sigmoid(u)
 __device__ __forceinline__ float silu(float u) {
@@ -734,18 +741,27 @@ __global__ __launch_bounds__(kBThreads, 1) void gemm_big_kernel(GemmArgs g) {
   }
 }
 
-// Large form with 64-wide k chunks: 256 x 256 per workgroup, 4 waves of
-// 128 x 128 (one wave per SIMD), two LDS buffers.  Chunk c + 1 goes global
-// -> LDS by direct loads into the buffer chunk c - 1 used while chunk c is
-// computed (its loads spread over the first half of the chunk's MFMAs), so
-// each chunk costs one barrier and its loads have half to all of a chunk to
-// land.  One memory instruction after each MFMA, in a fixed order; the next
-// chunk's first fragments are read after the barrier, under the last 8
-// MFMAs.  Measured against the 4-stage ring of 32-wide chunks on the block's
-// shapes: FFN up 14.30 -> 13.37 ms, FFN down 15.47 -> 13.83, QKV 9.87 ->
-// 9.08; staging the loads through registers instead (two chunks ahead)
-// gave 13.76 / 13.67 / 9.8, its LDS writes and their waits costing more
-// than the extra lead saved.
+// Large form with 64-wide k chunks: 256 x 256 per tile, 4 waves of 128 x 128
+// (one wave per SIMD), two LDS buffers.  Chunk c + 1 goes global -> LDS by
+// direct loads into the buffer chunk c - 1 used while chunk c is computed
+// (its loads spread over the first half of the chunk's MFMAs), so each chunk
+// costs one barrier and its loads have half to all of a chunk to land.  One
+// memory instruction after each MFMA, in a fixed order; the next chunk's
+// first fragments are read after the barrier, under the last 8 MFMAs.
+// Measured against the 4-stage ring of 32-wide chunks on the block's shapes:
+// FFN up 14.30 -> 13.37 ms, FFN down 15.47 -> 13.83, QKV 9.87 -> 9.08;
+// staging the loads through registers instead (two chunks ahead) gave 13.76
+// / 13.67 / 9.8, its LDS writes and their waits costing more than the extra
+// lead saved.
+//
+// Persistent: one workgroup per CU walks the tiles of its XCD (blockIdx % 8)
+// in order.  The last chunk of a tile loads the next tile's first chunk into
+// the free buffer and reads its first fragments after the barrier, so the
+// next tile's prologue runs under the previous tile's last MFMAs and its
+// epilogue; the first k step of a tile starts its accumulators from zero in
+// the MFMA itself.  Measured on the block's shapes against one workgroup per
+// tile (same box): FFN up 13.2 -> 12.96 ms, QKV 9.27 -> 9.08, FFN down
+// unchanged, results bitwise the same.
 #ifndef TDP_GEMM_K64
 #define TDP_GEMM_K64 1
 #endif
@@ -763,7 +779,7 @@ __device__ __forceinline__ int rs_slot(int r, int p) { return p ^ ((r >> 1) & 7)
 // step, instead of both in chunk c's first two steps: more time for each
 // load to land.  Measured on the block's shapes: FFN down (K = 16384)
 // 13.75 -> 13.00 ms; FFN up and QKV (K = 4096) 12.56 -> 12.76 and 8.82 ->
-// 8.98 ms, so the launch takes it for K >= 8192 only.
+// 8.98 ms, so the launch takes it for K >= 8192 only (there K / 64 >= 128).
 template <int EPI, int HD, bool LEAD = false>
 __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   static_assert(HD % kRK == 0, "whole k chunks per head");
@@ -775,63 +791,74 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t M = g.M;
   const int64_t nm = cdiv(M, kWRows), nn = g.N / kWCols;
-  int64_t tm, tn;
-  {
-    const int64_t G = gridDim.x;
-    const int64_t bid = blockIdx.x;
-    const int64_t lid = (bid % 8) * (G / 8) + bid / 8;
-    if (lid >= nm * nn) return;
+  const int64_t T = nm * nn;
+  // XCD x takes tiles [x T8, (x + 1) T8); its G / 8 workgroups one tile each
+  // at a time, in order (gridDim.x is a multiple of 8)
+  const int64_t G = gridDim.x, bid = blockIdx.x;
+  const int64_t T8 = cdiv(T, 8);
+  const int64_t lid_end = min((bid % 8) * T8 + T8, T);
+  const int64_t lstep = G / 8;
+  int64_t lid = (bid % 8) * T8 + bid / 8;
+  if (lid >= lid_end) return;
+  // Tile order within the XCD's range: groups of group_m row blocks walk
+  // down a column of tiles.
+  auto tile_of = [&](int64_t l, int64_t &row0, int64_t &col0) __attribute__((always_inline)) {
     const int64_t group = g.group_m;
     const int64_t per_group = group * nn;
-    const int64_t grp = lid / per_group;
+    const int64_t grp = l / per_group;
     const int64_t first_m = grp * group;
     const int64_t gm = min(group, nm - first_m);
-    const int64_t in = lid - grp * per_group;
-    tm = first_m + in % gm;
-    tn = in / gm;
-  }
-  const int64_t row0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tm))) *
-                       kWRows;
-  const int64_t col0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tn))) *
-                       kWCols;
-  const int64_t rows_here = min(static_cast<int64_t>(kWRows), M - row0);
-  const char *abase;
-  uint32_t a_extent;
-  if constexpr (HD > 0) {
-    abase = reinterpret_cast<const char *>(g.a);
-    a_extent = static_cast<uint32_t>(M * g.K * 2);   // host: < 2^32 bytes
-  } else {
-    abase = reinterpret_cast<const char *>(g.a + row0 * g.lda);
-    a_extent = static_cast<uint32_t>(((rows_here - 1) * g.lda + g.K) * 2);
-  }
-  const char *bbase = reinterpret_cast<const char *>(g.bt + col0 * g.ldb);
-  const uint32_t b_extent = static_cast<uint32_t>(((kWCols - 1) * g.ldb + g.K) * 2);
-  const i32x4 arsrc = buffer_rsrc(abase, a_extent);
-  const i32x4 brsrc = buffer_rsrc(bbase, b_extent);
+    const int64_t in = l - grp * per_group;
+    row0 = (first_m + in % gm) * kWRows;
+    col0 = (in / gm) * kWCols;
+  };
+  int64_t row0, col0;
+  tile_of(lid, row0, col0);
   // Direct load i of an operand's chunk: LDS 16-byte position (i * 4 +
   // wave) * 64 + lane = row * 8 + slot takes the row's piece slot ^ key(row)
   // (the swizzle is its own inverse).  Each descriptor covers exactly the
-  // bytes this workgroup may read; rows past M re-read row M - 1 (their
-  // results are not stored).
+  // bytes this tile may read (none once there is no next tile: those loads
+  // touch no memory); rows past M re-read row M - 1 (their results are not
+  // stored).
+  i32x4 arsrc, brsrc;
   uint32_t aoff[kRLoads], boff[kRLoads];
+  auto set_a = [&](int64_t r0, bool live) __attribute__((always_inline)) {
+    const int rows_here = static_cast<int>(min(static_cast<int64_t>(kWRows), M - r0));
+    if constexpr (HD > 0) {
+      arsrc = buffer_rsrc(g.a, live ? static_cast<uint32_t>(M * g.K * 2) : 0u);   // host: < 2^32 bytes
+    } else {
+      arsrc = buffer_rsrc(g.a + r0 * g.lda,
+                          live ? static_cast<uint32_t>(((rows_here - 1) * g.lda + g.K) * 2) : 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < kRLoads; ++i) {
+      const int pos = (i * 4 + uwave) * 64 + lane;
+      const int r = pos / 8, p = rs_slot(r, pos % 8);
+      const int ra = min(r, rows_here - 1);
+      if constexpr (HD > 0) {
+        // head-major A: row gr of segment seg (a_seg_rows rows each) is row
+        // gr - seg L of every head's slab; a chunk's head offset is scalar
+        const uint32_t L = static_cast<uint32_t>(g.a_seg_rows);
+        const uint32_t gr = static_cast<uint32_t>(r0 + ra);
+        const uint32_t seg = gr / L;
+        aoff[i] = ((seg * static_cast<uint32_t>(g.a_heads) * L + (gr - seg * L)) * HD + 8 * p) * 2;
+      } else {
+        aoff[i] = static_cast<uint32_t>((static_cast<int64_t>(ra) * g.lda + 8 * p) * 2);
+      }
+    }
+  };
+  auto set_b = [&](int64_t c0, bool live) __attribute__((always_inline)) {
+    brsrc = buffer_rsrc(g.bt + c0 * g.ldb,
+                        live ? static_cast<uint32_t>(((kWCols - 1) * g.ldb + g.K) * 2) : 0u);
+  };
 #pragma unroll
   for (int i = 0; i < kRLoads; ++i) {
     const int pos = (i * 4 + uwave) * 64 + lane;
-    const int r = pos / 8, slot = pos % 8;
-    const int p = rs_slot(r, slot);
-    const int64_t ra = min(static_cast<int64_t>(r), rows_here - 1);
-    if constexpr (HD > 0) {
-      // head-major A: row gr of segment seg (a_seg_rows rows each) is row
-      // gr - seg L of every head's slab; a chunk's head offset is scalar
-      const int64_t L = g.a_seg_rows;
-      const int64_t gr = row0 + ra;
-      const int64_t seg = gr / L;
-      aoff[i] = static_cast<uint32_t>(((seg * g.a_heads * L + (gr - seg * L)) * HD + 8 * p) * 2);
-    } else {
-      aoff[i] = static_cast<uint32_t>((ra * g.lda + 8 * p) * 2);
-    }
+    const int r = pos / 8, p = rs_slot(r, pos % 8);
     boff[i] = static_cast<uint32_t>((static_cast<int64_t>(r) * g.ldb + 8 * p) * 2);
   }
+  set_a(row0, true);
+  set_b(col0, true);
   // Fragment offsets: A row 128 wm + 32 t + l32, B^T row 128 wn + 32 t + l32,
   // piece 2 s + hh of k step s; the swizzle key of the row depends on l32
   // only, so tile t adds 32 t rows.
@@ -843,16 +870,11 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
     fbo[s] = (128 * wn + l32) * kRK + x;
   }
   f32x16 acc[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[mt][ct] = f32x16{};
   bf16x8 fa[2][4], fb[2][4];            // fragments of k step s (set s % 2)
   const int nc = g.K / kRK;
 #define TDP_FENCE() __builtin_amdgcn_sched_barrier(0)
-  // chunk c's load i into buffer buf (past the last chunk: the last again)
+  // chunk c's load i into buffer buf, with the current descriptors
   auto dload = [&](int buf, int c, int i) __attribute__((always_inline)) {
-    c = min(c, nc - 1);
     const uint32_t so = static_cast<uint32_t>(c) * kRK * 2;
     uint32_t sa = so;
     if constexpr (HD > 0) {
@@ -871,6 +893,7 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
     else if (q < 5) fb[s & 1][q - 1] = *reinterpret_cast<const bf16x8 *>(&sB[buf][fbo[s] + 32 * (q - 1) * kRK]);
     else fa[s & 1][q - 4] = *reinterpret_cast<const bf16x8 *>(&sA[buf][fao[s] + 32 * (q - 4) * kRK]);
   };
+  // the first tile's chunk 0 (and, LEAD, chunk 1's A)
 #pragma unroll
   for (int i = 0; i < 2 * kRLoads; ++i) dload(0, 0, i);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -881,12 +904,24 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   }
 #pragma unroll
   for (int q = 0; q < 8; ++q) fread(0, 0, q);
+  int64_t nrow0 = row0, ncol0 = col0;
+  bool has_next = false;
   // Chunk c in buffer c % 2: step s's MFMAs carry step s + 1's reads (even
-  // slots) and, in steps 0 and 1, chunk c + 1's 16 direct loads (odd slots);
+  // slots) and chunk c + 1's 16 direct loads (odd slots of steps 0 and 1;
+  // LEAD: the B loads in step 0, chunk c + 2's A loads after the barrier);
   // after 8 of step 3's MFMAs the wait for those loads and the barrier, then
-  // chunk c + 1's step-0 reads.
-  auto chunk = [&](int c, auto par) __attribute__((always_inline)) {
-    constexpr int P = decltype(par)::value;   // c % 2
+  // chunk c + 1's step-0 reads.  MODE 0: the loads are of this tile; 1 (LEAD,
+  // chunk nc - 2): the A loads after the barrier are of the next tile's
+  // chunk 0; 2 (chunk nc - 1): the loads are of the next tile's chunk 0
+  // (LEAD: its B, then chunk 1's A).  Z: step 0 starts the accumulators.
+  auto chunk = [&](int c, auto par, auto zero, auto mode) __attribute__((always_inline)) {
+    constexpr int P = decltype(par)::value;
+    constexpr bool Z = decltype(zero)::value;
+    constexpr int MODE = decltype(mode)::value;
+    if constexpr (MODE == 2) {
+      if constexpr (!LEAD) set_a(nrow0, has_next);
+      set_b(ncol0, has_next);
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -896,51 +931,77 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
           lds_barrier();
           TDP_FENCE();
+          if constexpr (LEAD && MODE == 1) set_a(nrow0, has_next);
         }
-        acc[am][bn] = mfma32(fa[s & 1][am], fb[s & 1][bn], acc[am][bn]);
+        if (Z && s == 0) acc[am][bn] = mfma32(fa[0][am], fb[0][bn], f32x16{});
+        else acc[am][bn] = mfma32(fa[s & 1][am], fb[s & 1][bn], acc[am][bn]);
+        const int cb = MODE == 2 ? 0 : c + 1;   // chunk of the B loads (and of A without LEAD)
         if constexpr (LEAD) {
+          const int ca = MODE == 0 ? c + 2 : (MODE == 1 ? 0 : 1);
           if (s < 3 && q % 2 == 0) fread(P, s + 1, q / 2);
-          else if (s == 0) dload(1 - P, c + 1, kRLoads + q / 2);
+          else if (s == 0) dload(1 - P, cb, kRLoads + q / 2);
           else if (s == 3 && q >= 8) {
             fread(1 - P, 0, q - 8);
-            dload(P, c + 2, q - 8);
+            dload(P, ca, q - 8);
           }
         } else {
           if (s < 3 && q % 2 == 0) fread(P, s + 1, q / 2);
-          else if (s < 2) dload(1 - P, c + 1, 8 * s + q / 2);
+          else if (s < 2) dload(1 - P, cb, 8 * s + q / 2);
           else if (s == 3 && q >= 8) fread(1 - P, 0, q - 8);
         }
         TDP_FENCE();
       }
     }
   };
-  // K is a multiple of 128: chunks in pairs, every buffer index a constant
-  for (int c = 0; c < nc; c += 2) {
-    chunk(c, std::integral_constant<int, 0>{});
-    chunk(c + 1, std::integral_constant<int, 1>{});
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-#undef TDP_FENCE
-  // acc[mt][ct][v]: row 128 wm + 32 mt + 8 (v/4) + 4 hh + v%4, column
-  // 128 wn + 32 ct + l32
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  for (;;) {
+    const int64_t nlid = lid + lstep;
+    has_next = nlid < lid_end;
+    if (has_next) tile_of(nlid, nrow0, ncol0);
+    // K is a multiple of 128 and at least 256: the first pair, the middle
+    // pairs, the last pair
+    chunk(0, P0{}, std::true_type{}, M0{});
+    chunk(1, P1{}, std::false_type{}, M0{});
+    for (int c = 2; c < nc - 2; c += 2) {
+      chunk(c, P0{}, std::false_type{}, M0{});
+      chunk(c + 1, P1{}, std::false_type{}, M0{});
+    }
+    if constexpr (LEAD) chunk(nc - 2, P0{}, std::false_type{}, M1{});
+    else chunk(nc - 2, P0{}, std::false_type{}, M0{});
+    chunk(nc - 1, P1{}, std::false_type{}, M2{});
+    // acc[mt][ct][v]: row 128 wm + 32 mt + 8 (v/4) + 4 hh + v%4, column
+    // 128 wn + 32 ct + l32
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int64_t base = row0 + 128 * wm + 32 * mt;
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t base = row0 + 128 * wm + 32 * mt;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
-      if (r >= M) continue;
+      for (int v = 0; v < 16; ++v) {
+        const int64_t r = base + 8 * (v / 4) + 4 * hh + (v % 4);
+        if (r >= M) continue;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int64_t idx = r * g.ldc + col0 + 128 * wn + 32 * ct + l32;
-        const float x = acc[mt][ct][v];
-        if constexpr (EPI == kEpiBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(x);
-        if constexpr (EPI == kEpiF32) static_cast<float *>(g.c)[idx] = x;
-        if constexpr (EPI == kEpiGeluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(gelu_tanh(x));
-        if constexpr (EPI == kEpiSiluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(silu(x));
+        for (int ct = 0; ct < 4; ++ct) {
+          const int64_t idx = r * g.ldc + col0 + 128 * wn + 32 * ct + l32;
+          const float x = acc[mt][ct][v];
+          if constexpr (EPI == kEpiBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(x);
+          if constexpr (EPI == kEpiF32) static_cast<float *>(g.c)[idx] = x;
+          if constexpr (EPI == kEpiGeluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(gelu_tanh(x));
+          if constexpr (EPI == kEpiSiluBf16) static_cast<bf16 *>(g.c)[idx] = static_cast<bf16>(silu(x));
+        }
       }
     }
+    if (!has_next) break;
+    lid = nlid;
+    row0 = nrow0;
+    col0 = ncol0;
   }
+  // the last tile's loads of "the next tile" touched no memory but still
+  // write LDS: wait for them before the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#undef TDP_FENCE
 }
 
 
@@ -953,6 +1014,23 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
 #ifndef TDP_GEMM_WIDE
 #define TDP_GEMM_WIDE 1
 #endif
+
+// Workgroups of the persistent large form: one per CU, rounded down to a
+// multiple of 8 (the XCD count), per device; 0 if HIP cannot say.
+int persistent_slots() {
+  static std::atomic<int> slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = slots[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    n = cus >= 8 ? cus / 8 * 8 : 8;
+    slots[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 template <int EPI>
 tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) {
@@ -974,22 +1052,26 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
     if (TDP_GEMM_BIG == 2 && EPI != kEpiResid && EPI != kEpiResidGate &&
         a.K % (kBK * kBStages) == 0 && fits) {
       const dim3 bgrid(static_cast<uint32_t>(cdiv(nm * nn, 8) * 8));
-      if (TDP_GEMM_K64 && a.K % (2 * kRK) == 0) {
+      if (TDP_GEMM_K64 && a.K % (2 * kRK) == 0 && a.K >= 4 * kRK) {
         // Tile order: groups of 4 row blocks walk down a column of tiles,
         // groups of 2 for outputs of 16384 or more columns (measured on the
         // block's shapes: FFN up, 16384 columns, 13.33 -> 12.95 ms with 2;
         // FFN down and QKV, 4096 and 12288 columns, 13.79 -> 15.03 and 9.07
-        // -> 9.33 ms with 2; 8 slower for all three)
+        // -> 9.33 ms with 2; 8 slower for all three; 1 for FFN up 15.1
+        // against 13.3 ms)
         GemmArgs b = a;
         b.group_m = a.N >= 16384 ? 2 : 4;
+        const int slots = persistent_slots();
+        if (slots == 0) return TDP_ERR_HIP;
+        const dim3 pgrid(static_cast<uint32_t>(std::min<int64_t>(cdiv(nm * nn, 8) * 8, slots)));
         if (hd == 0 && a.K >= 8192)
-          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0, true>), bgrid, dim3(256), 0, stream, b);
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0, true>), pgrid, dim3(256), 0, stream, b);
         else if (hd == 0)
-          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0>), bgrid, dim3(256), 0, stream, b);
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0>), pgrid, dim3(256), 0, stream, b);
         else if (hd == 64)
-          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 64>), bgrid, dim3(256), 0, stream, b);
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 64>), pgrid, dim3(256), 0, stream, b);
         else
-          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 128>), bgrid, dim3(256), 0, stream, b);
+          hipLaunchKernelGGL((gemm_k64_kernel<EPI, 128>), pgrid, dim3(256), 0, stream, b);
       } else if (hd == 0)
         hipLaunchKernelGGL((gemm_big_kernel<EPI, 0>), bgrid, dim3(kBThreads), 0, stream, a);
       else if (hd == 64)
