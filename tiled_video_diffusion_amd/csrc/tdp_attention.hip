@@ -96,6 +96,7 @@ struct Layout {
   int32_t hidden = 0;
   size_t off_wt = 0, off_wot = 0, off_pad_begin = 0, off_blk_tile = 0, off_blk_q0 = 0;
   size_t off_kmax = 0;  // [B][heads][T+1] largest squared K row norm per tile (slot T: audio)
+  size_t off_pool = 0;  // the core's tail-claim counter (one word right after the maxima)
   int64_t vt_cols = 0;  // columns per V^T row: the padded tile rows, then the padded audio rows
   size_t off_q = 0, off_k = 0, off_vt = 0, off_qa = 0, off_ka = 0;
   size_t off_o = 0, off_oa = 0, total = 0;
@@ -169,7 +170,8 @@ tdp_status make_layout(const tdp_attn_desc *d, int32_t n_tiles, int64_t n_rows, 
   L->off_pad_begin = take((T + 1) * 4);
   L->off_blk_tile = take(L->npb * 4);
   L->off_blk_q0 = take(L->npb * 4);
-  L->off_kmax = take(B * H * (T + 1) * 4);
+  L->off_kmax = take((B * H * (T + 1) + 1) * 4);
+  L->off_pool = L->off_kmax + B * H * (T + 1) * 4;
   L->off_q = take(B * H * L->n_pad * D * 2);
   L->off_k = take(B * H * L->n_pad * D * 2);
   L->off_vt = take(B * H * static_cast<size_t>(L->vt_cols) * D * 2);
@@ -235,7 +237,8 @@ __device__ inline void tile_rows(const int64_t *trb, int32_t t, int64_t n_rows, 
 // pad_begin[t] = first 128-row block of tile t in the padded row space, where
 // each tile takes a whole number of 256-row units (clamped to npb);
 // blk_tile/blk_q0 map each block to its tile and first tile row (-1 for blocks
-// past the last tile); also clears the per-tile K norm maxima.  One workgroup.
+// past the last tile); also clears the per-tile K norm maxima and, in the
+// word after them, the core's tail-claim counter.  One workgroup.
 __global__ __launch_bounds__(1024) void block_table_kernel(const int64_t *__restrict__ trb,
                                                            int32_t T, int64_t n_rows,
                                                            int32_t max_rows, int64_t npb,
@@ -774,6 +777,11 @@ struct CoreArgs {
   int32_t kv_splits;
   float *op;
   float2 *ml;
+  // Unsplit two-group launches: units assigned per XCD, then the claimed tail
+  // (see attn_core2_kernel).
+  int64_t per_xcd;
+  uint32_t pool_claims;
+  uint32_t *pool_ctr;
 };
 
 // What one query slot of the core covers: (batch, head), tile, first query
@@ -1550,10 +1558,31 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void attn_core2_kernel(CoreA
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
 
-  const int64_t G = gridDim.x;
+  // One 256-row unit per workgroup.  Workgroup i runs on XCD i % 8, and XCD
+  // x's first per_xcd workgroups take units x per_xcd, x per_xcd + 1, ... in
+  // order, so the units of one (tile, head) share that XCD's L2.  Units from
+  // 8 per_xcd on form a shared tail: every later workgroup claims the next
+  // one from a counter, so the XCDs that run faster (their shader clocks
+  // differ under load) take more of it, and claims past the last unit end
+  // at once.  Each of the pool_claims tail workgroups claims exactly once;
+  // the launch's last claim puts the counter back to zero for the next
+  // launch (the prepare stage zeroes it first).
   const int64_t bid = blockIdx.x;
-  const int64_t lid = (bid % 8) * (G / 8) + bid / 8;   // gridDim.x is a multiple of 8
-  if (lid >= a.total_units) return;                    // one workgroup per 256-row unit
+  const int64_t xcd = bid % 8, kx = bid / 8;
+  int64_t lid;
+  if (kx < a.per_xcd) {
+    lid = xcd * a.per_xcd + kx;
+  } else {
+    __shared__ uint32_t ticket;
+    if (threadIdx.x == 0) {
+      const uint32_t tk = atomicAdd(a.pool_ctr, 1u);
+      if (tk == a.pool_claims - 1u) atomicExch(a.pool_ctr, 0u);
+      ticket = tk;
+    }
+    __syncthreads();
+    lid = 8 * a.per_xcd + static_cast<int64_t>(ticket);
+  }
+  if (lid >= a.total_units) return;
   const int64_t bh = lid / a.units_per_bh;
   const int64_t u = lid - bh * a.units_per_bh;
   const int64_t b = bh / a.heads;
@@ -2089,7 +2118,7 @@ extern "C" tdp_status tdp_attn_prepare(const tdp_attn_desc *desc, int32_t n_tile
                      ws_at<int32_t>(workspace, L.off_blk_tile),
                      ws_at<int32_t>(workspace, L.off_blk_q0),
                      ws_at<uint32_t>(workspace, L.off_kmax),
-                     static_cast<int64_t>(desc->batch) * desc->heads * (n_tiles + 1));
+                     static_cast<int64_t>(desc->batch) * desc->heads * (n_tiles + 1) + 1);
   return launch_status();
 }
 
@@ -2203,8 +2232,20 @@ void launch_core(const Call &c, hipStream_t stream, bool tile_keys = true,
   if (S == 1) {
     const int64_t grid = ceil_div(slots, 8) * 8;
     if constexpr (TDP_ATTN_NG2) {
-      // one 256-query workgroup per unit
-      const int64_t grid2 = ceil_div(a.total_units, 8) * 8;
+      // one 256-query workgroup per unit: per_xcd units per XCD, then (for
+      // launches of 16 rounds or more) a claimed tail of about 1/12 of the
+      // units, with 1.5 times its even share of claiming workgroups per XCD
+      const int64_t U = a.total_units;
+      const int64_t resident = kCUs * (D == 128 ? 1 : 2);
+      a.per_xcd = ceil_div(U, 8);
+      int64_t claims = 0;
+      if (U >= 16 * resident) {
+        a.per_xcd = (U - U / 12) / 8;
+        claims = ceil_div(3 * (U - 8 * a.per_xcd), 16);
+      }
+      a.pool_claims = static_cast<uint32_t>(8 * claims);
+      a.pool_ctr = ws_at<uint32_t>(c.ws, L.off_pool);
+      const int64_t grid2 = 8 * (a.per_xcd + claims);
       hipLaunchKernelGGL((attn_core2_kernel<D>), dim3(static_cast<uint32_t>(grid2)), dim3(256), 0,
                          stream, a);
       return;
@@ -2409,7 +2450,7 @@ tdp_status attn_tables(const tdp_attn_desc *desc, int32_t n_tiles, const int64_t
                      max_rows, L.npb, ws_at<int32_t>(ws, L.off_pad_begin),
                      ws_at<int32_t>(ws, L.off_blk_tile), ws_at<int32_t>(ws, L.off_blk_q0),
                      ws_at<uint32_t>(ws, L.off_kmax),
-                     static_cast<int64_t>(desc->batch) * desc->heads * (n_tiles + 1));
+                     static_cast<int64_t>(desc->batch) * desc->heads * (n_tiles + 1) + 1);
   return launch_status();
 }
 
