@@ -314,6 +314,45 @@ def test_repeat_runs_are_deterministic(case):
         assert torch.equal(a, s.y_global)
 
 
+def test_claimed_tail_recomputed_on_every_launch():
+    """A core launch of 16 rounds or more hands its last units to workgroups
+    that claim them from a counter, which the launch's last claim puts back
+    to zero.  A second launch without the prepare stage (which also zeroes
+    it) must still compute every unit: new Q/K/V, core and projection again
+    give bitwise what a launch after a fresh prepare gives."""
+    inp = _variant("t16_16x64x64", heads=10)     # 4840 units of 256 rows >= 16 x 256 CUs
+    say("claimed tail", inp.workload.name, "heads", inp.workload.heads)
+    s = _step(inp)
+    s.run()
+    torch.cuda.synchronize()
+    y1 = s.y_tiles.clone()
+    s.x_global.neg_()
+    s.gather()
+    s.attn_qkv()
+    s.attn_core()                                # no prepare: the counter reset by the last launch
+    s.attn_out()
+    torch.cuda.synchronize()
+    y2 = s.y_tiles.clone()
+    s.attn_prepare()
+    s.attn_core()
+    s.attn_out()
+    torch.cuda.synchronize()
+    assert not torch.equal(y1, y2)
+    assert torch.equal(y2, s.y_tiles)
+    # and a sample of rows against the oracle
+    wl = inp.workload
+    p = oracle.plan(wl.grid, wl.tiling, inp.cond_pos)
+    x_tiles = oracle.gather_tiles(-inp.x_global, p)
+    rng = np.random.default_rng(5)
+    t = p.tile_id.size - 1                       # the last tile: its units are in the claimed tail
+    rows, r0, r1 = _sample_rows(p, t, rng, 16)
+    y, _ = oracle.tile_forward(x_tiles[0, r0:r1], p.row_pos[r0:r1], None, inp.wq, inp.wk,
+                               inp.wv, inp.wo, wl.heads, wl.head_dim, query_rows=rows)
+    e = rel_err(_np(y2)[0, r0 + rows], y)
+    say(f"  last tile rows {rows.size}: {e:.2e}")
+    assert e <= ATTN_TOL
+
+
 def _fallback_inputs():
     """Inputs whose Cauchy-Schwarz bound |q| max|k| is far above every real
     score while the scores stay ordinary: each head's K is zero on the first
