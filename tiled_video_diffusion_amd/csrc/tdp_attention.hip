@@ -2525,4 +2525,10 @@ const bf16 *attn_output(const tdp_attn_desc *desc, int32_t n_tiles, int64_t n_ro
   return ws_at<bf16>(ws, L.off_o);
 }
 
+uint32_t *attn_tail_counter(const tdp_attn_desc *desc, int32_t n_tiles, int64_t n_rows, void *ws) {
+  Layout L;
+  if (make_layout(desc, n_tiles, n_rows, &L) != TDP_OK) return nullptr;
+  return ws_at<uint32_t>(ws, L.off_pool);
+}
+
 }  // namespace tdp

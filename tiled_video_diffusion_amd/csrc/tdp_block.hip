@@ -319,6 +319,10 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
   bf16 *e1 = at<bf16>(workspace, L.off_e1);
   float *E = at<float>(workspace, L.off_e);
   bf16 *ckv = at<bf16>(workspace, L.off_ckv);
+  // every launch below runs in stream order, so the large GEMMs share the
+  // self-attention workspace's tail counter with its core (zeroed by
+  // attn_tables before the first of them)
+  uint32_t *tail_ctr = attn_tail_counter(&L.self, n_tiles, n_rows, ws_self);
   // h = RMSNorm of x with the modulation rows (shift_row, shift_row + 1) of
   // `table` (and E), after x += gate * y when y is given (y = the branch
   // output a GEMM just stored in h; gate rows of E and of the table by
@@ -372,6 +376,7 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
     g.g0_stride = 6 * D;
     g.g1 = g1;
     g.rows_per_batch = n_rows;
+    g.tail_ctr = tail_ctr;
     return gemm(epi, g, stream);
   };
   auto proj_o = [&](const tdp_attn_desc *ad, void *aws, const void *wo) {
@@ -387,6 +392,7 @@ extern "C" tdp_status tdp_block_forward(const tdp_block_desc *desc, int32_t n_ti
     g.K = static_cast<int32_t>(D);
     g.c = h;
     g.ldc = D;
+    g.tail_ctr = tail_ctr;
     return gemm(kEpiBf16, g, stream);
   };
 #define TDP_TRY(expr)               \

@@ -68,6 +68,11 @@ struct GemmArgs {
   const float *g1;
   int64_t rows_per_batch;
   int32_t group_m;        // 64-wide large form: row blocks per tile-order group
+  // 64-wide large form: tiles per XCD taken in order, then a tail of tiles
+  // claimed from *tail_ctr (tail_claims claims per launch; 0: no tail)
+  int64_t per_xcd;
+  uint32_t *tail_ctr;
+  uint32_t tail_claims;
 };
 
 // HD = 0: row-major A; HD = 64 / 128: head-major A with that head size.
@@ -755,7 +760,9 @@ __global__ __launch_bounds__(kBThreads, 1) void gemm_big_kernel(GemmArgs g) {
 // lead saved.
 //
 // Persistent: one workgroup per CU walks the tiles of its XCD (blockIdx % 8)
-// in order.  The last chunk of a tile loads the next tile's first chunk into
+// in order; with a counter given, the last ~1/12 of the tiles are instead
+// claimed one at a time by whichever workgroups get there first (the XCDs
+// hold different shader clocks under load).  The last chunk of a tile loads the next tile's first chunk into
 // the free buffer and reads its first fragments after the barrier, so the
 // next tile's prologue runs under the previous tile's last MFMAs and its
 // epilogue; the first k step of a tile starts its accumulators from zero in
@@ -792,14 +799,33 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   const int64_t M = g.M;
   const int64_t nm = cdiv(M, kWRows), nn = g.N / kWCols;
   const int64_t T = nm * nn;
-  // XCD x takes tiles [x T8, (x + 1) T8); its G / 8 workgroups one tile each
-  // at a time, in order (gridDim.x is a multiple of 8)
+  // XCD x takes tiles [x S8, (x + 1) S8); its G / 8 workgroups one tile each
+  // at a time, in order (gridDim.x is a multiple of 8).  Tiles from 8 S8 on
+  // (with a tail) are claimed: a claim returns the next of them; every
+  // workgroup claims until a claim returns no tile, so a launch makes
+  // exactly tail_claims = tail + G claims, and the last one puts the counter
+  // back to zero.  A tile's claim for its successor goes out as the tile
+  // starts; its result reaches the other waves through LDS at chunk 0's
+  // barrier.
   const int64_t G = gridDim.x, bid = blockIdx.x;
-  const int64_t T8 = cdiv(T, 8);
-  const int64_t lid_end = min((bid % 8) * T8 + T8, T);
+  const int64_t S8 = g.per_xcd;
+  const int64_t lid_end = min((bid % 8) * S8 + S8, T);
   const int64_t lstep = G / 8;
-  int64_t lid = (bid % 8) * T8 + bid / 8;
-  if (lid >= lid_end) return;
+  const bool tail = g.tail_claims != 0;
+  __shared__ int64_t s_claim;
+  auto claim = [&]() __attribute__((always_inline)) {
+    const uint32_t tk = atomicAdd(g.tail_ctr, 1u);
+    if (tk == g.tail_claims - 1u) atomicExch(g.tail_ctr, 0u);
+    return 8 * S8 + static_cast<int64_t>(tk);
+  };
+  int64_t lid = (bid % 8) * S8 + bid / 8;
+  if (lid >= lid_end) {
+    if (!tail) return;
+    if (threadIdx.x == 0) s_claim = claim();
+    __syncthreads();
+    lid = s_claim;
+    if (lid >= T) return;
+  }
   // Tile order within the XCD's range: groups of group_m row blocks walk
   // down a column of tiles.
   auto tile_of = [&](int64_t l, int64_t &row0, int64_t &col0) __attribute__((always_inline)) {
@@ -906,6 +932,8 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   for (int q = 0; q < 8; ++q) fread(0, 0, q);
   int64_t nrow0 = row0, ncol0 = col0;
   bool has_next = false;
+  int64_t claimed = 0;           // thread 0: this tile's claim for its successor
+  bool claiming = false;         // the successor comes from a claim
   // Chunk c in buffer c % 2: step s's MFMAs carry step s + 1's reads (even
   // slots) and chunk c + 1's 16 direct loads (odd slots of steps 0 and 1;
   // LEAD: the B loads in step 0, chunk c + 2's A loads after the barrier);
@@ -929,6 +957,9 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
         const int am = q / 4, bn = q % 4;
         if (s == 3 && q == 8) {
           asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          if constexpr (Z) {
+            if (claiming && threadIdx.x == 0) s_claim = claimed;
+          }
           lds_barrier();
           TDP_FENCE();
           if constexpr (LEAD && MODE == 1) set_a(nrow0, has_next);
@@ -959,12 +990,22 @@ __global__ __launch_bounds__(256, 1) void gemm_k64_kernel(GemmArgs g) {
   using M1 = std::integral_constant<int, 1>;
   using M2 = std::integral_constant<int, 2>;
   for (;;) {
-    const int64_t nlid = lid + lstep;
-    has_next = nlid < lid_end;
-    if (has_next) tile_of(nlid, nrow0, ncol0);
+    int64_t nlid = lid + lstep;
+    claiming = tail && !(nlid < lid_end);
+    if (claiming) {
+      if (threadIdx.x == 0) claimed = claim();
+    } else {
+      has_next = nlid < lid_end;
+      if (has_next) tile_of(nlid, nrow0, ncol0);
+    }
     // K is a multiple of 128 and at least 256: the first pair, the middle
     // pairs, the last pair
     chunk(0, P0{}, std::true_type{}, M0{});
+    if (claiming) {
+      nlid = s_claim;
+      has_next = nlid < T;
+      if (has_next) tile_of(nlid, nrow0, ncol0);
+    }
     chunk(1, P1{}, std::false_type{}, M0{});
     for (int c = 2; c < nc - 2; c += 2) {
       chunk(c, P0{}, std::false_type{}, M0{});
@@ -1063,7 +1104,16 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
         b.group_m = a.N >= 16384 ? 2 : 4;
         const int slots = persistent_slots();
         if (slots == 0) return TDP_ERR_HIP;
-        const dim3 pgrid(static_cast<uint32_t>(std::min<int64_t>(cdiv(nm * nn, 8) * 8, slots)));
+        const int64_t T = nm * nn;
+        const dim3 pgrid(static_cast<uint32_t>(std::min<int64_t>(cdiv(T, 8) * 8, slots)));
+        // tiles per XCD in order; with a counter and at least 16 tiles per
+        // workgroup, about 1/12 of the tiles are left to a claimed tail
+        b.per_xcd = cdiv(T, 8);
+        b.tail_claims = 0;
+        if (a.tail_ctr && T >= 16 * static_cast<int64_t>(pgrid.x)) {
+          b.per_xcd = (T - T / 12) / 8;
+          b.tail_claims = static_cast<uint32_t>(T - 8 * b.per_xcd + pgrid.x);
+        }
         if (hd == 0 && a.K >= 8192)
           hipLaunchKernelGGL((gemm_k64_kernel<EPI, 0, true>), pgrid, dim3(256), 0, stream, b);
         else if (hd == 0)
@@ -1114,7 +1164,7 @@ tdp_status gemm(int epi, const GemmDesc &d, hipStream_t stream) {
   if (epi == kEpiResidGate && d.rows_per_batch < 1) return TDP_ERR_ARG;
   if (cdiv(d.M, kGRows) > INT32_MAX) return TDP_ERR_UNSUPPORTED;
   GemmArgs a{d.a, d.lda, d.a_seg_rows, d.a_heads, d.bt, d.ldb, d.M, d.N, d.K, d.c, d.ldc,
-             d.g0, d.g0_stride, d.g1, d.rows_per_batch, 4};
+             d.g0, d.g0_stride, d.g1, d.rows_per_batch, 4, 0, d.tail_ctr, 0};
   const dim3 grid(static_cast<uint32_t>(cdiv(d.M, kGRows)), static_cast<uint32_t>(d.N / kGCols));
   switch (epi) {
     case kEpiBf16: return launch_epi<kEpiBf16>(a, d.a_head_dim, grid, stream);

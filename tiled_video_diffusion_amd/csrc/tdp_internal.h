@@ -39,6 +39,10 @@ struct GemmDesc {
   int64_t g0_stride = 0;
   const float *g1 = nullptr;
   int64_t rows_per_batch = 1;
+  // A zeroed counter the persistent large form may use for a claimed tail of
+  // tiles (each launch leaves it zero again); null: every tile assigned
+  // statically.  Launches that share a counter must not overlap.
+  uint32_t *tail_ctr = nullptr;
 };
 
 // Launches the GEMM on `stream`; TDP_ERR_UNSUPPORTED for shapes outside the
@@ -68,5 +72,8 @@ tdp_status attn_core_run(const tdp_attn_desc *desc, int32_t n_tiles, const int64
                          bool tile_keys, hipStream_t stream);
 // The core's output O, head-major [B][heads][n_rows][head_dim] (nullptr for a bad desc).
 const bf16 *attn_output(const tdp_attn_desc *desc, int32_t n_tiles, int64_t n_rows, void *ws);
+// The attention workspace's tail-claim counter: zeroed by attn_tables, left
+// zero by every launch that uses it (the core's, and GEMMs given it).
+uint32_t *attn_tail_counter(const tdp_attn_desc *desc, int32_t n_tiles, int64_t n_rows, void *ws);
 
 }  // namespace tdp
