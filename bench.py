@@ -909,8 +909,19 @@ def core_roofline(wl, plan, core_ms: float) -> dict:
             "flops_per_launch": flops, "ms_per_launch": core_ms}
 
 
+LEG_WARM_S = 0.5    # a leg's warm-up lasts at least this long (after its own setup)
+LEG_TIMED_S = 0.3   # and its timed region at least this long
+
+
 def leg(name: str, steps: int, warmup: int) -> dict:
-    """The whole step on another workload: throughput and the core's roofline."""
+    """The whole step on another workload: throughput and the core's roofline.
+
+    A leg follows seconds of host-side setup with the GPU idle, and its
+    shader clock takes a while to come back up: W warm-up steps of the
+    half-millisecond head-dim-64 step are 1.5 ms, and its core measured
+    8-9% slower that way than in steady state.  So a leg warms up for at
+    least LEG_WARM_S and times at least LEG_TIMED_S of steps (more than K
+    steps when the step is short); the counts used are reported."""
     import torch
 
     import tdp_inputs as ti
@@ -919,7 +930,19 @@ def leg(name: str, steps: int, warmup: int) -> dict:
     inp = ti.make_inputs(name)
     wl = inp.workload
     step = TdpStep(inp)
-    ms, stage_ms = time_step(step, steps, warmup, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or time.perf_counter() - t0 < LEG_WARM_S:
+        step.run()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    per_step = (time.perf_counter() - t0) / n
+    warmup = n
+    steps = max(steps, int(LEG_TIMED_S / max(per_step, 1e-6)) + 1)
+    ms, stage_ms = time_step(step, steps, 0, torch.cuda.current_stream())
     p = step.plan
     out = {"workload": name, "batch": wl.batch, "grid": list(wl.grid), "tiles": p.n_tiles_total,
            "rows": p.n_rows, "heads": wl.heads, "head_dim": wl.head_dim, "n_cond": wl.n_cond,

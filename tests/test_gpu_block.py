@@ -97,8 +97,11 @@ def test_block_runs_are_deterministic():
 
 
 def test_block_full_width_sampled():
-    """The 16-tile step at width 4096 (one block): sampled rows of a corner and
-    an interior tile against the oracle (every row gives keys and values)."""
+    """The 16-tile step at width 4096 (one block): sampled rows of two corner
+    tiles and an interior tile against the oracle (every row gives keys and
+    values).  The last tile's rows are in the large GEMMs' claimed tail of
+    tiles (the last ~1/12 of the tile order), which each of the block's GEMM
+    launches takes through one shared counter."""
     say("block t16 sampled")
     binp = ti.make_block_inputs("block_t16")
     s = _run(binp)
@@ -108,7 +111,7 @@ def test_block_full_width_sampled():
     yt = s.y_tiles.double().cpu().numpy()[0]
     model = ob.model_from_inputs(binp)
     rng = np.random.default_rng(11)
-    for t in (0, 5):
+    for t in (0, 5, p.tile_id.size - 1):
         r0, r1 = int(p.tile_row_begin[t]), int(p.tile_row_begin[t + 1])
         rows = np.array(sorted({0, r1 - r0 - 1, 127, 128} |
                                set(rng.integers(0, r1 - r0, size=12).tolist())))
