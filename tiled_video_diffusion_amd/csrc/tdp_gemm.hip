@@ -75,8 +75,51 @@ struct GemmArgs {
   uint32_t tail_claims;
 };
 
+// Workgroup barrier ordering LDS only (the direct loads are waited for with
+// an explicit vmcnt before it; a plain __syncthreads would also wait for every
+// load still in flight).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor of `bytes` bytes at `base` (wave-uniform): raw, stride 0,
+// the gfx9 data-format word.
+__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  r[3] = 0x00020000;
+  return r;
+}
+
+// 16 bytes per lane from descriptor offset voff + soff into LDS: the wave's
+// 64 lanes fill the 1 KB at `lds` (wave-uniform) in lane order.
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t soff,
+                                           const bf16 *lds) {
+  const uint32_t m0 = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16 *)lds));
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+               : "memory");
+}
+
+
 // HD = 0: row-major A; HD = 64 / 128: head-major A with that head size.
-template <int EPI, int HD>
+// ASM: the direct loads are buffer loads into LDS written in inline assembly,
+// which the compiler does not track; with the builtin (FLAT) form it waits
+// for every direct load in flight, the ring's later chunks included, before
+// the first fragment read of each step, so no load gets more than one step
+// to land.  The launcher takes the builtin form only when a workgroup's A
+// offsets do not fit the descriptors' 32 bits.
+template <int EPI, int HD, bool ASM = true>
 __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
   static_assert(HD % kGK == 0, "whole k chunks per head");
   __shared__ __attribute__((aligned(16))) bf16 sA0[kGRows * kGK], sA1[kGRows * kGK],
@@ -92,7 +135,20 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
 
   // Per-lane byte offsets of the direct loads (k chunk 0); LDS position
   // (r, slot) holds piece slot ^ ((r / 2) % 8) of row r.  Rows past M re-read
-  // row M - 1 (their results are not stored).
+  // row M - 1 (their results are not stored).  With ASM they are relative to
+  // the workgroup's first row (A) and first column (B^T), the bases of the
+  // two descriptors, and a chunk's k offset is the scalar offset.
+  auto a_elem = [&](int64_t gr) __attribute__((always_inline)) {
+    if constexpr (HD > 0) {
+      const int64_t L = g.a_seg_rows;
+      const int64_t seg = gr / L;
+      return (seg * g.a_heads * L + (gr - seg * L)) * HD;
+    } else {
+      return gr * g.lda;
+    }
+  };
+  const int64_t ael0 = ASM ? a_elem(min(row0, M - 1)) : 0;
+  const int64_t bel0 = ASM ? col0 * g.ldb : 0;
   uint64_t aoff[kGALoads];
   uint64_t boff[kGBLoads];
 #pragma unroll
@@ -100,24 +156,30 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
     const int pos = (i * kGWaves + uwave) * 64 + lane;   // 16-byte position in the tile
     const int r = pos / 8, slot = pos % 8;
     const int64_t gr = min(row0 + r, M - 1);
-    int64_t el;
-    if constexpr (HD > 0) {
-      const int64_t L = g.a_seg_rows;
-      const int64_t seg = gr / L;
-      el = (seg * g.a_heads * L + (gr - seg * L)) * HD;
-    } else {
-      el = gr * g.lda;
-    }
-    aoff[i] = static_cast<uint64_t>(el * 2 + 16 * g_slot(r, slot));
+    aoff[i] = static_cast<uint64_t>((a_elem(gr) - ael0) * 2 + 16 * g_slot(r, slot));
   }
 #pragma unroll
   for (int i = 0; i < kGBLoads; ++i) {
     const int pos = (i * kGWaves + uwave) * 64 + lane;
     const int r = pos / 8, slot = pos % 8;
-    boff[i] = static_cast<uint64_t>((col0 + r) * g.ldb * 2 + 16 * g_slot(r, slot));
+    boff[i] = static_cast<uint64_t>(((col0 + r) * g.ldb - bel0) * 2 + 16 * g_slot(r, slot));
   }
-  const char *abase = reinterpret_cast<const char *>(g.a);
-  const char *bbase = reinterpret_cast<const char *>(g.bt);
+  const char *abase = reinterpret_cast<const char *>(g.a) + ael0 * 2;
+  const char *bbase = reinterpret_cast<const char *>(g.bt) + bel0 * 2;
+  // descriptors (ASM): A from the first row to the end of A, B^T from the
+  // first column to the end of the workgroup's columns
+  i32x4 arsrc, brsrc;
+  if constexpr (ASM) {
+    int64_t a_end;
+    if constexpr (HD > 0) {
+      const int64_t segs = cdiv(M, g.a_seg_rows);
+      a_end = segs * g.a_heads * g.a_seg_rows * HD;
+    } else {
+      a_end = (M - 1) * g.lda + g.K;
+    }
+    arsrc = buffer_rsrc(abase, static_cast<uint32_t>(min<int64_t>((a_end - ael0) * 2, 0xffffffffLL)));
+    brsrc = buffer_rsrc(bbase, static_cast<uint32_t>((static_cast<int64_t>(kGCols - 1) * g.ldb + g.K) * 2));
+  }
   auto load_chunk = [&](int c, bf16 *sa, bf16 *sb) __attribute__((always_inline)) {
     const int64_t kb = static_cast<int64_t>(c) * kGK * 2;   // B^T (and row-major A): k = 64 c
     int64_t ab = kb;
@@ -126,14 +188,31 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
       const int h = c / kPerHead;
       ab = (static_cast<int64_t>(h) * g.a_seg_rows * HD + (c - h * kPerHead) * kGK) * 2;
     }
+    if constexpr (ASM) {
+      i32x4 ar, br;   // (wave-uniform: readfirstlane keeps them in scalar registers)
 #pragma unroll
-    for (int i = 0; i < kGALoads; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(abase + ab + aoff[i]),
-                                       (lvoid_t *)(sa + (i * kGWaves + uwave) * 512), 16, 0, 0);
+      for (int k = 0; k < 4; ++k) {
+        ar[k] = __builtin_amdgcn_readfirstlane(arsrc[k]);
+        br[k] = __builtin_amdgcn_readfirstlane(brsrc[k]);
+      }
+      const uint32_t sa_off = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(ab));
+      const uint32_t sb_off = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(kb));
 #pragma unroll
-    for (int i = 0; i < kGBLoads; ++i)
-      __builtin_amdgcn_global_load_lds((gvoid_t *)(bbase + kb + boff[i]),
-                                       (lvoid_t *)(sb + (i * kGWaves + uwave) * 512), 16, 0, 0);
+      for (int i = 0; i < kGALoads; ++i)
+        load_lds16(ar, static_cast<uint32_t>(aoff[i]), sa_off, sa + (i * kGWaves + uwave) * 512);
+#pragma unroll
+      for (int i = 0; i < kGBLoads; ++i)
+        load_lds16(br, static_cast<uint32_t>(boff[i]), sb_off, sb + (i * kGWaves + uwave) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kGALoads; ++i)
+        __builtin_amdgcn_global_load_lds((gvoid_t *)(abase + ab + aoff[i]),
+                                         (lvoid_t *)(sa + (i * kGWaves + uwave) * 512), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < kGBLoads; ++i)
+        __builtin_amdgcn_global_load_lds((gvoid_t *)(bbase + kb + boff[i]),
+                                         (lvoid_t *)(sb + (i * kGWaves + uwave) * 512), 16, 0, 0);
+    }
   };
   // fragment offsets (elements): A row wave*32 + l32, B^T row 32 ct + l32;
   // piece 2 ks + hh
@@ -169,7 +248,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
   if (nc > 1) load_chunk(1, sA1, sB1);
   if (nc > 1) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
+  if constexpr (ASM) lds_barrier();
+  else __syncthreads();
   // Step c: load chunk c+2 into the ring slot of chunk c-1, compute chunk c,
   // wait for chunk c+1, barrier.  Loads past the last chunk re-read chunk
   // nc-1 (in range; never used) so every step waits on the same count.
@@ -178,7 +258,8 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_kernel(GemmArgs g) {
     load_chunk(min(c + 2, nc - 1), ln_a, ln_b);
     compute(ca, cb);
     asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    __syncthreads();
+    if constexpr (ASM) lds_barrier();
+    else __syncthreads();
   };
   int c = 0;
   for (; c + 3 <= nc; c += 3) {
@@ -428,14 +509,6 @@ constexpr int kBLoadsB = kWCols * kBK * 2 / 1024 / kBWaves;   // 4
 constexpr int kBLoads = kBLoadsA + kBLoadsB;
 static_assert(kBStages >= 2 && kBStages <= 4, "2..4 stages of 32 KB");
 
-// Workgroup barrier ordering LDS only (the direct loads are waited for with
-// an explicit vmcnt before it; a plain __syncthreads would also wait for every
-// load still in flight).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // Wait until at most N chunks of direct loads (8 instructions each) are in
 // flight.
@@ -448,32 +521,6 @@ __device__ __forceinline__ void wait_chunks() {
 }
 
 __device__ __forceinline__ int b_slot(int r, int piece) { return piece ^ ((r >> 2) & 3); }
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor of `bytes` bytes at `base` (wave-uniform): raw, stride 0,
-// the gfx9 data-format word.
-__device__ __forceinline__ i32x4 buffer_rsrc(const void *base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<int>(a & 0xffffffffu));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<int>((a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-  r[3] = 0x00020000;
-  return r;
-}
-
-// 16 bytes per lane from descriptor offset voff + soff into LDS: the wave's
-// 64 lanes fill the 1 KB at `lds` (wave-uniform) in lane order.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t voff, uint32_t soff,
-                                           const bf16 *lds) {
-  const uint32_t m0 = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const bf16 *)lds));
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
-               : "memory");
-}
 
 template <int EPI, int HD>
 __global__ __launch_bounds__(kBThreads, 1) void gemm_big_kernel(GemmArgs g) {
@@ -1139,12 +1186,29 @@ tdp_status launch_epi(const GemmArgs &a, int hd, dim3 grid, hipStream_t stream) 
       hipLaunchKernelGGL((gemm_wide_kernel<EPI, 128>), wgrid, dim3(kGThreads), 0, stream, a);
     return launch_status();
   }
-  if (hd == 0)
-    hipLaunchKernelGGL((gemm_kernel<EPI, 0>), grid, dim3(kGThreads), 0, stream, a);
-  else if (hd == 64)
-    hipLaunchKernelGGL((gemm_kernel<EPI, 64>), grid, dim3(kGThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gemm_kernel<EPI, 128>), grid, dim3(kGThreads), 0, stream, a);
+  // buffer-descriptor offsets of the inline-assembly loads: a workgroup's A
+  // rows (one segment boundary at most in head-major A) plus a chunk's k
+  // offset, and B^T's 128 rows plus k, all below 2^32
+  constexpr int64_t k4G = int64_t{1} << 32;
+  const int64_t a_span = hd > 0 ? 2 * (a.a_seg_rows * a.K * 2) + int64_t{kGRows} * hd * 2
+                                : int64_t{kGRows} * a.lda * 2 + int64_t{a.K} * 2;
+  const int64_t b_span = int64_t{kGCols} * a.ldb * 2 + int64_t{a.K} * 2;
+  const bool asm_fits = a_span + 256 < k4G && b_span + 256 < k4G;
+  if (asm_fits) {
+    if (hd == 0)
+      hipLaunchKernelGGL((gemm_kernel<EPI, 0>), grid, dim3(kGThreads), 0, stream, a);
+    else if (hd == 64)
+      hipLaunchKernelGGL((gemm_kernel<EPI, 64>), grid, dim3(kGThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<EPI, 128>), grid, dim3(kGThreads), 0, stream, a);
+  } else {
+    if (hd == 0)
+      hipLaunchKernelGGL((gemm_kernel<EPI, 0, false>), grid, dim3(kGThreads), 0, stream, a);
+    else if (hd == 64)
+      hipLaunchKernelGGL((gemm_kernel<EPI, 64, false>), grid, dim3(kGThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<EPI, 128, false>), grid, dim3(kGThreads), 0, stream, a);
+  }
   return launch_status();
 }
 
