@@ -198,7 +198,13 @@ typedef struct {
                                * when there are few query blocks (the sequence-
                                * parallel share: all tokens, few heads).  0 splits
                                * only such launches; self-attention launches of
-                               * 256 or more query blocks (d = 128) never split. */
+                               * 256 or more query blocks (d = 128) never split.
+                               * With 0, an unsplit launch of two rounds or more
+                               * also leaves its last ~1/12 of the query blocks
+                               * to whichever workgroups reach them first (the
+                               * XCDs run at different clocks); with 1 every
+                               * block's workgroup is fixed.  The results are
+                               * bitwise the same either way. */
 } tdp_attn_desc;
 
 /* Workspace bytes tdp_tile_attention needs for these sizes.  Errors as

@@ -353,6 +353,26 @@ def test_claimed_tail_recomputed_on_every_launch():
     assert e <= ATTN_TOL
 
 
+@pytest.mark.parametrize("name,kw", [("d64_8x32x32", {}), ("t16_16x64x64", dict(heads=10))])
+def test_two_launch_geometries_bitwise(name, kw):
+    """The same step under two launch geometries of the core: every query
+    block on a fixed workgroup (kv_splits 1), and the last ~1/12 of them
+    claimed at run time by whichever workgroups reach them first (kv_splits
+    0; these launches are two rounds or more).  A query block's result must
+    not depend on where it runs, so the outputs are bitwise equal."""
+    inp = _variant(name, **kw) if kw else ti.make_inputs(name)
+    say("two launch geometries", name, kw)
+    outs = []
+    for k in (1, 0, 1):
+        s = _step(inp, kv_splits=k)
+        s.run()
+        torch.cuda.synchronize()
+        outs.append(s.y_tiles.clone())
+        del s
+    assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], outs[2])
+
+
 def _fallback_inputs():
     """Inputs whose Cauchy-Schwarz bound |q| max|k| is far above every real
     score while the scores stay ordinary: each head's K is zero on the first

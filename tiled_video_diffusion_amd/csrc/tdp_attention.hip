@@ -2233,13 +2233,14 @@ void launch_core(const Call &c, hipStream_t stream, bool tile_keys = true,
     const int64_t grid = ceil_div(slots, 8) * 8;
     if constexpr (TDP_ATTN_NG2) {
       // one 256-query workgroup per unit: per_xcd units per XCD, then (for
-      // launches of two rounds or more) a claimed tail of about 1/12 of the
-      // units, with 1.5 times its even share of claiming workgroups per XCD
+      // launches of two rounds or more, with the launch shape left to the
+      // library: kv_splits 0) a claimed tail of about 1/12 of the units, with
+      // 1.5 times its even share of claiming workgroups per XCD
       const int64_t U = a.total_units;
       const int64_t resident = kCUs * (D == 128 ? 1 : 2);
       a.per_xcd = ceil_div(U, 8);
       int64_t claims = 0;
-      if (U >= 2 * resident) {
+      if (c.d->kv_splits == 0 && U >= 2 * resident) {
         a.per_xcd = (U - U / 12) / 8;
         claims = ceil_div(3 * (U - 8 * a.per_xcd), 16);
       }
